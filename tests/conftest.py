@@ -1,0 +1,21 @@
+"""Shared pytest configuration: the `gpu` marker and common helpers."""
+
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+@pytest.fixture(scope="session")
+def page_facts():
+    with open(os.path.join(ROOT, "tests", "golden", "page_facts.json")) as f:
+        return json.load(f)
