@@ -1,0 +1,232 @@
+/*
+ * moe.h - C ABI of libmoe: the routed, block-scaled MoE expert-layer hot path
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations come from (cited by title and section):
+ *   [TRT]  TensorRT-LLM PR #15311 "Bound Triton MoE JIT specializations via
+ *          token-dim bucketing and warmup"
+ *   [TA]   torchada PR #115 "tune the Nemotron MTP decode row on S5000 with a
+ *          checked-in recipe"
+ *   [AIT]  ROCm/aiter PR #5310 "[Triton/Gluon] Add MoE GEMM variants and
+ *          weight-gradient kernel"
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are caller-owned device memory; (host) is host
+ *     memory. The library never allocates, frees or synchronizes: every device
+ *     call is asynchronous on `stream` (a hipStream_t; NULL = null stream).
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call returns an error code, touches no memory and launches
+ *     nothing. moe_last_error() then holds a message (thread-local).
+ *   - Device-resident data (routing ids, scale bytes) is not inspected: expert
+ *     ids outside [0, E) are not routed; an E8M0 byte of 0xFF yields NaN.
+ *   - Device faults are asynchronous and surface at the caller's next
+ *     synchronization; the library does not catch them.
+ *   - Slot s = t * top_k + j indexes the flattened routing [T, top_k].
+ *   - PAD = T * top_k marks an unused position of sorted_token_ids.
+ *   - All element offsets are formed in 64-bit arithmetic ([AIT] Notes: expert
+ *     255 of a 256-expert layer with N*K = 14.7M starts past INT32_MAX).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* a null pointer, a bad size, stride or combination */
+  MOE_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. not a gfx950 device) */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4               /* a HIP runtime call failed; see moe_last_error() */
+} moe_status;
+
+/* Element encodings. */
+typedef enum {
+  MOE_BF16 = 1,   /* bfloat16 */
+  MOE_FP32 = 2,   /* float */
+  MOE_E4M3 = 3,   /* OCP E4M3 "FN" byte (MXFP8 element) */
+  MOE_E2M1X2 = 4, /* two OCP E2M1 codes per byte (MXFP4): element 2i in the low nibble */
+  MOE_E8M0 = 5,   /* MX scale byte b: 2^(b - 127); 0xFF = NaN */
+  MOE_I32 = 6
+} moe_dtype;
+
+typedef enum {
+  MOE_EPILOGUE_NONE = 0,
+  /* h[:, j] = silu(pre[:, j]) * pre[:, N/2 + j], silu(z) = z / (1 + e^-z);
+     output width N/2. Gate = first half of the N weight rows, up = second. */
+  MOE_EPILOGUE_SWIGLU = 1
+} moe_epilogue;
+
+/* ------------------------------------------------------------------------
+ * Host helpers (pure, thread-safe, no GPU needed)
+ * ---------------------------------------------------------------------- */
+
+/* Token-dimension bucket of m ([TRT] Description and Test Coverage: eight
+ * buckets per power-of-two octave, at most 12.5% padding, fixed points,
+ * monotonic): m for m < 16, else m rounded up to a multiple of
+ * 2^(bitlen(m) - 4). Returns 0 for m = 0 and -1 for m < 0. */
+int64_t moe_bucket_round_up(int64_t m);
+
+/* The sorted closure {bucket(m) : 1 <= m <= max_tokens}. Writes up to `cap`
+ * values to out (host; may be NULL when cap = 0) and returns the closure's
+ * size (so a call with cap = 0 sizes the buffer); -1 if max_tokens < 0. */
+int64_t moe_bucket_enumerate(int64_t max_tokens, int64_t* out, int64_t cap);
+
+/* 1 when padding the token dimension cannot change real tokens' outputs:
+ * bf16 activations x MXFP4 weights with no dynamic activation scale ([TRT]
+ * Description: the padding is restricted to W4A16 MXFP4). 0 otherwise. */
+int32_t moe_padding_supported(int32_t a_dtype, int32_t w_dtype, int32_t dynamic_act_scale);
+
+/* Size of the block list for `num_slots` routed slots:
+ * floor((S + min(E, S) * (B - 1)) / B), an upper bound on the blocks any
+ * routing uses ([AIT] second review: the block list is sized above the real
+ * block count; the rest is sentinel blocks). -1 on bad arguments. */
+int64_t moe_align_max_blocks(int64_t num_slots, int32_t num_experts, int32_t block_m);
+
+/* BLOCK_M that moe_grouped_gemm expects the routing to be padded to. It
+ * depends only on the dtypes and on whether num_tokens <= 32 (the decode
+ * variant, [TA] "Follow-up on this table": the tiny-M default for M <= 32).
+ * 32 is itself a token bucket, so a padded and an unpadded run of the same
+ * tokens always take the same variant. -1 for an unsupported combination. */
+int32_t moe_gemm_block_m(int32_t a_dtype, int32_t w_dtype, int64_t num_tokens);
+
+/* BLOCK_M that moe_wgrad expects. */
+int32_t moe_wgrad_block_m(void);
+
+/* Largest number of tokens that takes the decode variant (32). */
+int64_t moe_decode_max_tokens(void);
+
+const char* moe_status_string(int32_t status);
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Routing ([AIT] Summary: moe_align_block_size's sorted_token_ids and
+ * expert_ids; [AIT] second review: sentinel blocks hold expert id -1;
+ * [TA] "Follow-up on this table": moe_align_block_size runs before the
+ * fused MoE GEMM).
+ *
+ * topk_ids            (device) int32 [num_tokens, top_k], row-major.
+ * sorted_token_ids    (device) int32 [max_blocks * block_m]: for expert e,
+ *                     positions [o_e, o_e + c_e) hold e's slots in ascending
+ *                     order, where c_e = #slots routed to e, p_e = c_e rounded
+ *                     up to a multiple of block_m, o_e = sum of p_e' (e' < e);
+ *                     every other position holds PAD.
+ * expert_ids          (device) int32 [max_blocks]: block b's expert; -1 for
+ *                     every block at or past num_tokens_post_pad / block_m.
+ * num_tokens_post_pad (device) int32 [1]: sum of p_e.
+ * max_blocks          the length of expert_ids; must be at least
+ *                     moe_align_max_blocks(num_tokens * top_k, E, block_m).
+ * The result is unique (a stable counting sort), and bit-identical run to run.
+ * num_tokens = 0 is legal: writes 0 and max_blocks sentinel blocks.
+ * Requirements: 1 <= top_k <= num_experts <= 1024, 1 <= block_m <= 256,
+ * num_tokens * top_k < 2^31. No workspace. */
+moe_status moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t top_k,
+                     int32_t num_experts, int32_t block_m,
+                     int32_t* sorted_token_ids, int32_t* expert_ids,
+                     int32_t* num_tokens_post_pad, int64_t max_blocks,
+                     moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Routed grouped GEMM ([AIT] Summary: moe_gemm_mxfp8, every expert's GEMM in
+ * one launch, E8M0 microscales per 32 K-elements applied per K-step, optional
+ * per-expert bias; [AIT] Notes: K-steps aligned to the 32-element scale
+ * blocks, int64 expert offsets; [AIT] second review: sentinel blocks exit at
+ * once, bias read through explicit strides; [TRT] Description: W4A16 MXFP4,
+ * rows independent; [TA] What it does: bf16 decode at M <= 32).
+ *
+ * For every block b with e = expert_ids[b] >= 0 and every position r of it
+ * with slot s = sorted_token_ids[b * block_m + r] < PAD:
+ *   pre[n] = sum_k A[s / a_row_div][k] * W_hat[e][n][k] + bias[e][n]
+ *   W_hat[e][n][k] = dec(W[e][n][k]) * 2^(w_scale[e][n][k / 32] - 127)
+ *   C[s][:] = bf16(pre) (MOE_EPILOGUE_NONE) or bf16(swiglu(pre)) (width N/2)
+ * accumulated in fp32, rounded once to bf16 (nearest-even) at the store.
+ * Rows of C for PAD positions and unrouted slots are not written.
+ * Weights are dequantized exactly into bf16 (the scale is a power of two)
+ * except that products below bf16's subnormal range round to zero.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t num_tokens;     /* T: routing rows; slots S = T * top_k; PAD = S */
+  int32_t top_k;
+  int32_t num_experts;    /* E */
+  int64_t n;              /* N: weight rows per expert (pre-epilogue width) */
+  int64_t k;              /* K: contraction length */
+
+  int32_t a_dtype;        /* MOE_BF16 */
+  int32_t a_row_div;      /* slot s reads A row s / a_row_div: top_k (A = token
+                             rows) or 1 (A = slot rows, e.g. the second GEMM) */
+  const void* a;          /* (device) A rows, row r at a + r * a_ld elements */
+  int64_t a_ld;           /* >= k */
+
+  int32_t w_dtype;        /* MOE_BF16, MOE_E4M3 or MOE_E2M1X2 */
+  const void* w;          /* (device) [E][N][K] codes; strides in storage units
+                             (elements; bytes of two codes for MOE_E2M1X2) */
+  int64_t w_stride_e;     /* >= n * w_ld */
+  int64_t w_ld;           /* >= k (or k/2 for MOE_E2M1X2) */
+  const uint8_t* w_scale; /* (device) E8M0 [E][N][K/32]; NULL for MOE_BF16 */
+  int64_t w_scale_stride_e;
+  int64_t w_scale_ld;     /* >= k / 32 */
+
+  const void* bias;       /* (device) bf16 [E][N] or NULL */
+  int64_t bias_stride_e;  /* in elements; any non-negative strides */
+  int64_t bias_stride_n;
+
+  int32_t epilogue;       /* moe_epilogue */
+  void* c;                /* (device) bf16 [S][N or N/2], row s at c + s * c_ld */
+  int64_t c_ld;           /* >= output width, in elements */
+
+  const int32_t* sorted_token_ids; /* (device) from moe_align */
+  const int32_t* expert_ids;       /* (device) */
+  const int32_t* num_tokens_post_pad; /* (device) */
+  int32_t block_m;        /* must equal moe_gemm_block_m(a_dtype, w_dtype, T) */
+  int64_t max_blocks;     /* length of expert_ids */
+} moe_gemm_args;
+
+/* Requirements: k % 32 == 0 and k >= 32; n >= 1 (even with SwiGLU);
+ * a_row_div in {1, top_k}; 16-byte aligned a and w rows (a_ld a multiple of
+ * 8; w_ld a multiple of 16 bytes); c_ld >= the output width. No workspace. */
+moe_status moe_grouped_gemm(const moe_gemm_args* args, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Top-k combine (the method's final step; [TRT] Description: the padded
+ * rows are sliced off after the grouped GEMMs).
+ *   y[t][n] = bf16( sum_{j < top_k, ascending} topk_w[t][j] * C[t*top_k + j][n] )
+ * in fp32. c (device) bf16 [T*top_k][n] with row stride c_ld; topk_w (device)
+ * fp32 [T][top_k]; y (device) bf16 [T][n] with row stride y_ld. Every row
+ * t < num_tokens is written. n % 8 == 0, c_ld and y_ld multiples of 8.
+ * ---------------------------------------------------------------------- */
+moe_status moe_combine(const void* c, int64_t c_ld, const float* topk_w,
+                       int64_t num_tokens, int32_t top_k, int64_t n,
+                       void* y, int64_t y_ld, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Expert weight gradient ([AIT] Summary: moe_wgrad, dW[e] = sum over the
+ * tokens routed to e of grad[t]^T x input[t], straight from
+ * sorted_token_ids / expert_ids; its trial-to-trial corruption came from
+ * atomics accumulating into an un-reset dW. Here each output tile is owned by
+ * one workgroup and written exactly once, so dW is overwritten, never
+ * accumulated into, and repeated calls give identical bits.)
+ *   dW[e][n][k] = sum_{slots s routed to e} grad[s][n] * x[s / top_k][k]
+ * in fp32; experts with no slots are written as zeros; PAD positions are
+ * skipped. x (device) bf16 [T][K], row stride x_ld; grad (device) bf16 [S][N],
+ * row stride grad_ld; dw (device) fp32 [E][N][K] contiguous.
+ * Requirements: block_m == moe_wgrad_block_m(); n % 32 == 0, k % 32 == 0;
+ * x_ld, grad_ld multiples of 8. No workspace.
+ * ---------------------------------------------------------------------- */
+moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad_ld,
+                     const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                     const int32_t* num_tokens_post_pad,
+                     int64_t num_tokens, int32_t top_k, int32_t num_experts,
+                     int64_t n, int64_t k, int32_t block_m, int64_t max_blocks,
+                     float* dw, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,325 @@
+"""Python binding of libmoe, the C-ABI library of gfx950 HIP kernels for the
+routed, block-scaled MoE expert layer.
+
+The functions here have the names of the C entry points (include/moe.h) and
+only marshal arguments: they check tensor shapes, dtypes and devices, take
+raw device pointers and the current HIP stream from torch, and call the
+library. Every step of the computation runs in the library's kernels; torch
+supplies device memory and streams. Importing this module loads libmoe.so and
+fails loudly when it has not been built (there is no fallback).
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MoeError", "lib", "MOE_BF16", "MOE_FP32", "MOE_E4M3", "MOE_E2M1X2", "MOE_E8M0",
+    "moe_bucket_round_up", "moe_bucket_enumerate", "moe_padding_supported",
+    "moe_align_max_blocks", "moe_gemm_block_m", "moe_wgrad_block_m", "moe_decode_max_tokens",
+    "moe_align", "moe_grouped_gemm", "moe_combine", "moe_wgrad", "moe_w4a16_layer",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_BF16, MOE_FP32, MOE_E4M3, MOE_E2M1X2, MOE_E8M0, MOE_I32 = 1, 2, 3, 4, 5, 6
+_W_DTYPES = {"bf16": MOE_BF16, "e4m3": MOE_E4M3, "e2m1x2": MOE_E2M1X2}
+_EPILOGUES = {"none": 0, "swiglu": 1}
+
+
+class MoeError(RuntimeError):
+    """A libmoe call returned an error status."""
+
+    def __init__(self, status, message):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class MoeGemmArgs(ctypes.Structure):
+    """ctypes mirror of moe_gemm_args (include/moe.h)."""
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64), ("top_k", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+        ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("a_dtype", ctypes.c_int32), ("a_row_div", ctypes.c_int32),
+        ("a", ctypes.c_void_p), ("a_ld", ctypes.c_int64),
+        ("w_dtype", ctypes.c_int32), ("w", ctypes.c_void_p),
+        ("w_stride_e", ctypes.c_int64), ("w_ld", ctypes.c_int64),
+        ("w_scale", ctypes.c_void_p), ("w_scale_stride_e", ctypes.c_int64), ("w_scale_ld", ctypes.c_int64),
+        ("bias", ctypes.c_void_p), ("bias_stride_e", ctypes.c_int64), ("bias_stride_n", ctypes.c_int64),
+        ("epilogue", ctypes.c_int32), ("c", ctypes.c_void_p), ("c_ld", ctypes.c_int64),
+        ("sorted_token_ids", ctypes.c_void_p), ("expert_ids", ctypes.c_void_p),
+        ("num_tokens_post_pad", ctypes.c_void_p),
+        ("block_m", ctypes.c_int32), ("max_blocks", ctypes.c_int64),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first with "
+            "`python -m mixture_experts_grouped_moe_amd._build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    sig = {
+        "moe_bucket_round_up": (i64, [i64]),
+        "moe_bucket_enumerate": (i64, [i64, ctypes.POINTER(i64), i64]),
+        "moe_padding_supported": (i32, [i32, i32, i32]),
+        "moe_align_max_blocks": (i64, [i64, i32, i32]),
+        "moe_gemm_block_m": (i32, [i32, i32, i64]),
+        "moe_wgrad_block_m": (i32, []),
+        "moe_decode_max_tokens": (i64, []),
+        "moe_status_string": (ctypes.c_char_p, [i32]),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_align": (i32, [vp, i64, i32, i32, i32, vp, vp, vp, i64, vp]),
+        "moe_grouped_gemm": (i32, [ctypes.POINTER(MoeGemmArgs), vp]),
+        "moe_combine": (i32, [vp, i64, vp, i64, i32, i64, vp, i64, vp]),
+        "moe_wgrad": (i32, [vp, i64, vp, i64, vp, vp, vp, i64, i32, i32, i64, i64, i32, i64, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _status_name(status):
+    return lib.moe_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != 0:
+        raise MoeError(status, lib.moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got {t.dim()}")
+    if t.numel() and t.dim() and t.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous in its last dimension")
+
+
+# ---------------------------------------------------------------- host helpers
+
+def moe_bucket_round_up(m):
+    """Token-dimension bucket of m (8 per power-of-two octave, <= 12.5% padding)."""
+    return int(lib.moe_bucket_round_up(int(m)))
+
+
+def moe_bucket_enumerate(max_tokens):
+    """Sorted closure of the buckets of 1..max_tokens."""
+    n = lib.moe_bucket_enumerate(int(max_tokens), None, 0)
+    if n < 0:
+        raise ValueError("max_tokens must be >= 0")
+    buf = (ctypes.c_int64 * max(n, 1))()
+    lib.moe_bucket_enumerate(int(max_tokens), buf, n)
+    return [int(buf[i]) for i in range(n)]
+
+
+def moe_padding_supported(a_dtype, w_dtype, dynamic_act_scale=False):
+    return bool(lib.moe_padding_supported(int(a_dtype), int(w_dtype), int(bool(dynamic_act_scale))))
+
+
+def moe_align_max_blocks(num_slots, num_experts, block_m):
+    return int(lib.moe_align_max_blocks(int(num_slots), int(num_experts), int(block_m)))
+
+
+def moe_gemm_block_m(w_dtype, num_tokens, a_dtype=MOE_BF16):
+    w = _W_DTYPES.get(w_dtype, w_dtype)
+    return int(lib.moe_gemm_block_m(int(a_dtype), int(w), int(num_tokens)))
+
+
+def moe_wgrad_block_m():
+    return int(lib.moe_wgrad_block_m())
+
+
+def moe_decode_max_tokens():
+    return int(lib.moe_decode_max_tokens())
+
+
+# ---------------------------------------------------------------- device calls
+
+def moe_align(topk_ids, num_experts, block_m, num_tokens=None, out=None, stream=None):
+    """Sort slots by expert and pad each expert to block_m.
+
+    topk_ids: int32 [T, top_k] on the device. Returns (sorted_token_ids,
+    expert_ids, num_tokens_post_pad) as int32 device tensors; `out` may give
+    preallocated ones. num_tokens (default T) routes only the first rows.
+    """
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    if not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be contiguous")
+    T = topk_ids.shape[0] if num_tokens is None else int(num_tokens)
+    if T > topk_ids.shape[0]:
+        raise ValueError("num_tokens exceeds topk_ids rows")
+    k = topk_ids.shape[1]
+    mb = moe_align_max_blocks(T * k, num_experts, block_m)
+    if out is None:
+        dev = topk_ids.device
+        out = (torch.empty(max(mb, 0) * block_m, dtype=torch.int32, device=dev),
+               torch.empty(max(mb, 0), dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev))
+    sorted_ids, expert_ids, post_pad = out
+    max_blocks = expert_ids.numel()
+    if sorted_ids.numel() < max_blocks * block_m:
+        raise ValueError("sorted_token_ids is shorter than max_blocks * block_m")
+    _check(lib.moe_align(_ptr(topk_ids), T, k, int(num_experts), int(block_m),
+                         _ptr(sorted_ids), _ptr(expert_ids), _ptr(post_pad), max_blocks,
+                         _stream(stream)))
+    return sorted_ids, expert_ids, post_pad
+
+
+def moe_grouped_gemm(a, w, w_dtype, routing, num_tokens, top_k, num_experts, a_row_div,
+                     w_scale=None, bias=None, epilogue="none", out=None, block_m=None,
+                     stream=None):
+    """Routed grouped GEMM: C[s] = epilogue(A[s // a_row_div] . W_hat[e]^T + bias[e]).
+
+    a: bf16 [rows, K]; w: [E, N, K] bf16 / uint8 E4M3 codes, or uint8 [E, N, K/2]
+    packed E2M1; w_scale: uint8 E8M0 [E, N, K/32]; bias: bf16 [E, N] (any
+    strides); routing: the (sorted_token_ids, expert_ids, num_tokens_post_pad)
+    of moe_align with block_m = moe_gemm_block_m(w_dtype, num_tokens).
+    Returns C, bf16 [num_tokens * top_k, N or N/2] (rows of unrouted slots are
+    left as they were).
+    """
+    wd = _W_DTYPES[w_dtype]
+    _need(a, "a", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 3)
+    E, N = w.shape[0], w.shape[1]
+    K = a.shape[1]
+    S = int(num_tokens) * int(top_k)
+    if w.shape[2] * (2 if w_dtype == "e2m1x2" else 1) != K:
+        raise ValueError("w's K does not match a's")
+    if a.shape[0] * int(a_row_div) < S:
+        raise ValueError("a has too few rows for num_tokens * top_k slots")
+    if w_dtype != "bf16":
+        _need(w_scale, "w_scale", torch.uint8, 3)
+        if tuple(w_scale.shape) != (E, N, K // 32):
+            raise ValueError(f"w_scale must be [E, N, K/32] = {(E, N, K // 32)}")
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or not bias.is_cuda or tuple(bias.shape) != (E, N):
+            raise TypeError("bias must be a bf16 [E, N] device tensor")
+    ep = _EPILOGUES[epilogue]
+    out_w = N // 2 if ep == 1 else N
+    if out is None:
+        out = torch.empty((S, out_w), dtype=torch.bfloat16, device=a.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if out.shape[0] < S or out.shape[1] < out_w:
+        raise ValueError(f"out must be at least [{S}, {out_w}]")
+    sorted_ids, expert_ids, post_pad = routing
+    if sorted_ids.numel() < expert_ids.numel() * (block_m or moe_gemm_block_m(w_dtype, num_tokens)):
+        raise ValueError("routing arrays do not match block_m")
+    bm = moe_gemm_block_m(w_dtype, num_tokens) if block_m is None else block_m
+    g = MoeGemmArgs()
+    g.num_tokens, g.top_k, g.num_experts = int(num_tokens), int(top_k), int(num_experts)
+    g.n, g.k = N, K
+    g.a_dtype, g.a_row_div, g.a, g.a_ld = MOE_BF16, int(a_row_div), a.data_ptr(), a.stride(0)
+    g.w_dtype, g.w, g.w_stride_e, g.w_ld = wd, w.data_ptr(), w.stride(0), w.stride(1)
+    if w_scale is not None:
+        g.w_scale, g.w_scale_stride_e, g.w_scale_ld = w_scale.data_ptr(), w_scale.stride(0), w_scale.stride(1)
+    if bias is not None:
+        g.bias, g.bias_stride_e, g.bias_stride_n = bias.data_ptr(), bias.stride(0), bias.stride(1)
+    g.epilogue, g.c, g.c_ld = ep, out.data_ptr(), out.stride(0)
+    g.sorted_token_ids, g.expert_ids = sorted_ids.data_ptr(), expert_ids.data_ptr()
+    g.num_tokens_post_pad = post_pad.data_ptr()
+    g.block_m, g.max_blocks = int(bm), expert_ids.numel()
+    _check(lib.moe_grouped_gemm(ctypes.byref(g), _stream(stream)))
+    return out
+
+
+def moe_combine(c, topk_w, top_k, num_tokens=None, out=None, stream=None):
+    """y[t] = sum_j topk_w[t, j] * c[t * top_k + j] (fp32, bf16 out), t < num_tokens."""
+    _need(c, "c", torch.bfloat16, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    if not topk_w.is_contiguous():
+        raise ValueError("topk_w must be contiguous")
+    T = topk_w.shape[0] if num_tokens is None else int(num_tokens)
+    N = c.shape[1]
+    if c.shape[0] < T * int(top_k) or topk_w.shape[0] < T or topk_w.shape[1] != int(top_k):
+        raise ValueError("c / topk_w too small for num_tokens * top_k")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=c.device)
+    _need(out, "out", torch.bfloat16, 2)
+    _check(lib.moe_combine(_ptr(c), c.stride(0), _ptr(topk_w), T, int(top_k), N,
+                           _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def moe_wgrad(x, grad, routing, num_tokens, top_k, num_experts, out=None, stream=None):
+    """dW[e] = sum over slots s routed to e of grad[s]^T x[s // top_k], fp32 [E, N, K]."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(grad, "grad", torch.bfloat16, 2)
+    N, K = grad.shape[1], x.shape[1]
+    if out is None:
+        out = torch.empty((num_experts, N, K), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, 3)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if x.shape[0] < int(num_tokens) or grad.shape[0] < int(num_tokens) * int(top_k):
+        raise ValueError("x / grad too small for num_tokens * top_k slots")
+    if tuple(out.shape) != (int(num_experts), N, K):
+        raise ValueError(f"out must be [E, N, K] = {(int(num_experts), N, K)}")
+    sorted_ids, expert_ids, post_pad = routing
+    _check(lib.moe_wgrad(_ptr(x), x.stride(0), _ptr(grad), grad.stride(0),
+                         _ptr(sorted_ids), _ptr(expert_ids), _ptr(post_pad),
+                         int(num_tokens), int(top_k), int(num_experts), N, K,
+                         moe_wgrad_block_m(), expert_ids.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+_warned_padding = False
+
+
+def moe_w4a16_layer(x, topk_ids, topk_w, w1, s1, w2, s2, b1=None, b2=None, num_tokens=None,
+                    pad_token_dim=False, stream=None):
+    """The W4A16 MXFP4 expert layer: align -> gate+up GEMM with SwiGLU ->
+    down GEMM -> top-k combine. Returns y bf16 [num_tokens, H].
+
+    With pad_token_dim, the token dimension is run at its bucket
+    (moe_bucket_round_up): the caller's x / topk_ids / topk_w must hold at
+    least that many rows (the rows past num_tokens are the padding; their
+    contents cannot change the real rows' results), and only the real rows of
+    y are formed. Padding is honoured only where moe_padding_supported() says
+    it is exact (bf16 activations x MXFP4 weights); elsewhere it is ignored
+    with a warning.
+    """
+    global _warned_padding
+    T = x.shape[0] if num_tokens is None else int(num_tokens)
+    Tr = T
+    if pad_token_dim:
+        if moe_padding_supported(MOE_BF16, MOE_E2M1X2):
+            Tr = moe_bucket_round_up(T)
+        elif not _warned_padding:
+            import warnings
+            warnings.warn("pad_token_dim ignored: padding is exact only for W4A16 MXFP4")
+            _warned_padding = True
+    if x.shape[0] < Tr or topk_ids.shape[0] < Tr:
+        raise ValueError(f"pad_token_dim needs {Tr} rows in x and topk_ids (bucket of {T})")
+    k = topk_ids.shape[1]
+    E = w1.shape[0]
+    bm = moe_gemm_block_m("e2m1x2", Tr)
+    routing = moe_align(topk_ids, E, bm, num_tokens=Tr, stream=stream)
+    h = moe_grouped_gemm(x, w1, "e2m1x2", routing, Tr, k, E, a_row_div=k, w_scale=s1, bias=b1,
+                         epilogue="swiglu", stream=stream)
+    c2 = moe_grouped_gemm(h, w2, "e2m1x2", routing, Tr, k, E, a_row_div=1, w_scale=s2, bias=b2,
+                          stream=stream)
+    return moe_combine(c2, topk_w, k, num_tokens=T, stream=stream)

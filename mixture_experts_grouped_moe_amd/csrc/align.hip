@@ -1,0 +1,154 @@
+// moe_align: per-expert histogram, scan of the BLOCK_M-padded counts, and a
+// stable scatter of slot ids into sorted_token_ids, with expert_ids per block
+// and -1 sentinel blocks past the used ones.
+//
+// Follows ROCm/aiter PR #5310 "Add MoE GEMM variants and weight-gradient
+// kernel" (Summary: sorted_token_ids / expert_ids of moe_align_block_size;
+// second review: sentinel blocks hold -1) and torchada PR #115 ("Follow-up on
+// this table": moe_align_block_size runs ahead of the fused MoE GEMM).
+//
+// One workgroup of 1024 threads does the whole job: the sizes on this path
+// (at most a few hundred thousand slots, at most 1024 experts) keep it in the
+// microsecond range, and one workgroup needs no cross-workgroup
+// synchronisation and no workspace. The scatter walks the slots in order,
+// 1024 at a time; inside a chunk each wave ranks equal expert ids with
+// ballots, so the order within an expert is ascending slot order and the
+// result is unique and deterministic.
+#include "common.h"
+#include "params.h"
+
+namespace moe {
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / kWave;
+constexpr int kAlignMaxExperts = 1024;
+constexpr int kAlignBatch = 4;  // slots per thread per batch (loads issued together)
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int32_t S, int32_t E, int32_t B,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ post_pad, int32_t max_blocks) {
+  __shared__ int32_t cnt[kAlignMaxExperts];
+  __shared__ int32_t off[kAlignMaxExperts];   // exclusive scan of padded counts
+  __shared__ int32_t run[kAlignMaxExperts];   // next free position per expert
+  __shared__ int32_t wave_cnt[kAlignWaves][kAlignMaxExperts];
+  __shared__ int32_t wave_sum[kAlignWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+
+  for (int e = tid; e < kAlignMaxExperts; e += kAlignThreads) cnt[e] = 0;
+  for (int i = tid; i < kAlignWaves * kAlignMaxExperts; i += kAlignThreads)
+    (&wave_cnt[0][0])[i] = 0;
+  __syncthreads();
+
+  // 1. histogram
+  for (int s = tid; s < S; s += kAlignThreads) {
+    int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // 2. exclusive scan of p_e = ceil(c_e / B) * B over experts (E <= 1024:
+  //    one value per thread; wave-level inclusive scan, then across waves).
+  int p = 0;
+  if (tid < E) p = ((cnt[tid] + B - 1) / B) * B;
+  int incl = p;
+  for (int d = 1; d < kWave; d <<= 1) {
+    int v = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += v;
+  }
+  if (lane == kWave - 1) wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_sum[w];
+  int total = 0;
+  for (int w = 0; w < kAlignWaves; ++w) total += wave_sum[w];
+  if (tid < E) {
+    off[tid] = before + incl - p;
+    run[tid] = before + incl - p;
+  }
+  if (tid == 0) *post_pad = total;
+  __syncthreads();
+
+  // 3. expert id per block: the largest e with off[e] <= b * B (that expert
+  //    is never empty when b * B < total); -1 past the used blocks.
+  for (int b = tid; b < max_blocks; b += kAlignThreads) {
+    int pos = b * B;
+    int e = -1;
+    if (pos < total) {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= pos) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+    }
+    expert_ids[b] = e;
+  }
+  // 4. PAD: the tail of each expert's segment and everything past `total`.
+  const int32_t pad = S;
+  if (tid < E) {
+    int start = off[tid] + cnt[tid];
+    int end = off[tid] + p;
+    for (int q = start; q < end; ++q) sorted_ids[q] = pad;
+  }
+  const int64_t len = (int64_t)max_blocks * B;
+  for (int64_t q = total + tid; q < len; q += kAlignThreads) sorted_ids[q] = pad;
+
+  // 5. stable scatter, 1024 slots per step, kAlignBatch steps per batch of loads.
+  for (int base = 0; base < S; base += kAlignThreads * kAlignBatch) {
+    int ev[kAlignBatch];
+#pragma unroll
+    for (int i = 0; i < kAlignBatch; ++i) {
+      int s = base + i * kAlignThreads + tid;
+      ev[i] = s < S ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kAlignBatch; ++i) {
+      const int s = base + i * kAlignThreads + tid;
+      if (base + i * kAlignThreads >= S) break;  // uniform across the workgroup
+      const int e = ev[i];
+      const bool valid = e >= 0 && e < E;
+      // lanes of this wave holding the same expert id
+      uint64_t m = __ballot(valid);
+#pragma unroll
+      for (int bit = 0; bit < 10; ++bit) {
+        bool one = (e >> bit) & 1;
+        uint64_t bal = __ballot(one);
+        m &= one ? bal : ~bal;
+      }
+      const uint64_t below = m & ((1ull << lane) - 1ull);
+      const int rank = __popcll(below);
+      if (valid && below == 0) wave_cnt[wave][e] = __popcll(m);
+      __syncthreads();
+      if (valid) {
+        int pos = run[e] + rank;
+        for (int w = 0; w < wave; ++w) pos += wave_cnt[w][e];
+        sorted_ids[pos] = s;
+      }
+      __syncthreads();
+      if (tid < E) {
+        int add = 0;
+#pragma unroll
+        for (int w = 0; w < kAlignWaves; ++w) {
+          add += wave_cnt[w][tid];
+          wave_cnt[w][tid] = 0;
+        }
+        run[tid] += add;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_align(const int32_t* ids, int32_t S, int32_t E, int32_t B,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* post_pad,
+                        int32_t max_blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, stream,
+                     ids, S, E, B, sorted_ids, expert_ids, post_pad, max_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,303 @@
+// Host side of libmoe: the C ABI declared in include/moe.h. Argument
+// validation (before anything touches the GPU), variant dispatch and the
+// pure host helpers.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "moe.h"
+
+#include "params.h"
+
+namespace {
+
+constexpr int64_t kDecodeMaxTokens = 32;
+constexpr int32_t kAlignMaxExperts = 1024;
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+// The kernels are written for gfx950 only: refuse any other device.
+moe_status check_device() {
+  static int cached[64] = {0};  // 0 unknown, 1 gfx950, -1 other
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+  if (dev >= 0 && dev < 64 && cached[dev] != 0)
+    return cached[dev] == 1 ? MOE_OK : fail(MOE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  hipDeviceProp_t prop;
+  err = hipGetDeviceProperties(&prop, dev);
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(err));
+  const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) cached[dev] = is950 ? 1 : -1;
+  if (!is950) return fail(MOE_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t err, const char* what) {
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+  return ok();
+}
+
+int64_t bucket(int64_t m) {
+  if (m < 0) return -1;
+  if (m < 16) return m;
+  int bits = 64 - __builtin_clzll((unsigned long long)m);
+  int64_t step = (int64_t)1 << (bits - 4);
+  return ((m + step - 1) / step) * step;
+}
+
+bool valid_w_dtype(int32_t d) { return d == MOE_BF16 || d == MOE_E4M3 || d == MOE_E2M1X2; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_bucket_round_up(int64_t m) { return bucket(m); }
+
+int64_t moe_bucket_enumerate(int64_t max_tokens, int64_t* out, int64_t cap) {
+  if (max_tokens < 0 || cap < 0 || (cap > 0 && out == nullptr)) return -1;
+  int64_t n = 0;
+  for (int64_t b = bucket(1); max_tokens >= 1 && b <= max_tokens; b = bucket(b + 1)) {
+    if (n < cap) out[n] = b;
+    ++n;
+  }
+  if (max_tokens >= 1) {
+    const int64_t top = bucket(max_tokens);
+    if (top > max_tokens) {
+      if (n < cap) out[n] = top;
+      ++n;
+    }
+  }
+  return n;
+}
+
+int32_t moe_padding_supported(int32_t a_dtype, int32_t w_dtype, int32_t dynamic_act_scale) {
+  return (a_dtype == MOE_BF16 && w_dtype == MOE_E2M1X2 && dynamic_act_scale == 0) ? 1 : 0;
+}
+
+int64_t moe_align_max_blocks(int64_t num_slots, int32_t num_experts, int32_t block_m) {
+  if (num_slots < 0 || num_experts < 1 || block_m < 1) return -1;
+  const int64_t used = num_slots < num_experts ? num_slots : num_experts;
+  return (num_slots + used * (block_m - 1)) / block_m;
+}
+
+int32_t moe_gemm_block_m(int32_t a_dtype, int32_t w_dtype, int64_t num_tokens) {
+  if (a_dtype != MOE_BF16 || !valid_w_dtype(w_dtype) || num_tokens < 0) return -1;
+  return num_tokens <= kDecodeMaxTokens ? moe::gemm_block_m_decode() : moe::gemm_block_m_large();
+}
+
+int32_t moe_wgrad_block_m(void) { return moe::wgrad_block_m(); }
+
+int64_t moe_decode_max_tokens(void) { return kDecodeMaxTokens; }
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t top_k, int32_t num_experts,
+                     int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
+                     int32_t* num_tokens_post_pad, int64_t max_blocks, moe_stream_t stream) {
+  if (num_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (top_k < 1 || num_experts < top_k)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "need 1 <= top_k (%d) <= num_experts (%d)", top_k, num_experts);
+  if (num_experts > kAlignMaxExperts)
+    return fail(MOE_ERR_UNSUPPORTED, "num_experts %d > %d", num_experts, kAlignMaxExperts);
+  if (block_m < 1 || block_m > 256) return fail(MOE_ERR_INVALID_ARGUMENT, "block_m %d not in [1, 256]", block_m);
+  const int64_t S = num_tokens * top_k;
+  if (S >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens * top_k must be < 2^31");
+  const int64_t need = moe_align_max_blocks(S, num_experts, block_m);
+  if (max_blocks < need)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks %lld < required %lld", (long long)max_blocks,
+                (long long)need);
+  if (max_blocks * block_m >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks * block_m too large");
+  if ((S > 0 && topk_ids == nullptr) || num_tokens_post_pad == nullptr ||
+      (max_blocks > 0 && (sorted_token_ids == nullptr || expert_ids == nullptr)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_align(topk_ids, (int32_t)S, num_experts, block_m, sorted_token_ids,
+                                      expert_ids, num_tokens_post_pad, (int32_t)max_blocks,
+                                      (hipStream_t)stream),
+                    "moe_align launch");
+}
+
+moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
+  if (g == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "args is null");
+  const moe_gemm_args& a = *g;
+  if (a.num_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (a.top_k < 1 || a.num_experts < a.top_k)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "need 1 <= top_k (%d) <= num_experts (%d)", a.top_k, a.num_experts);
+  if (a.a_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "a_dtype must be MOE_BF16");
+  if (!valid_w_dtype(a.w_dtype)) return fail(MOE_ERR_UNSUPPORTED, "w_dtype %d not supported", a.w_dtype);
+  if (a.n < 1 || a.n >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "n out of range");
+  if (a.k < 32 || a.k % 32 != 0 || a.k >= INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "k (%lld) must be a positive multiple of 32", (long long)a.k);
+  if (a.epilogue != MOE_EPILOGUE_NONE && a.epilogue != MOE_EPILOGUE_SWIGLU)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown epilogue %d", a.epilogue);
+  const bool swiglu = a.epilogue == MOE_EPILOGUE_SWIGLU;
+  if (swiglu && a.n % 2 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "SwiGLU needs an even n");
+  const int64_t out_w = swiglu ? a.n / 2 : a.n;
+  const int64_t S = a.num_tokens * a.top_k;
+  if (S >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens * top_k must be < 2^31");
+  if (a.a_row_div != 1 && a.a_row_div != a.top_k)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "a_row_div must be 1 or top_k");
+  if (a.a_ld < a.k || a.a_ld % 8 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "a_ld must be >= k and a multiple of 8");
+  const int64_t w_row_units = a.w_dtype == MOE_E2M1X2 ? a.k / 2 : a.k;
+  const int64_t w_elem_bytes = a.w_dtype == MOE_BF16 ? 2 : 1;
+  if (a.w_ld < w_row_units || (a.w_ld * w_elem_bytes) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a row and be a multiple of 16 bytes");
+  if (a.w_stride_e < a.n * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < n * w_ld");
+  if (a.w_dtype != MOE_BF16) {
+    if (a.w_scale == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale is null");
+    if (a.w_scale_ld < a.k / 32 || a.w_scale_stride_e < a.n * a.w_scale_ld)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale strides too small");
+  }
+  if (a.bias != nullptr && (a.bias_stride_e < 0 || a.bias_stride_n < 0))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "negative bias stride");
+  if (a.c_ld < out_w) return fail(MOE_ERR_INVALID_ARGUMENT, "c_ld must be >= the output width");
+  const int32_t bm = moe_gemm_block_m(a.a_dtype, a.w_dtype, a.num_tokens);
+  if (a.block_m != bm)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "block_m %d, expected %d for this call", a.block_m, bm);
+  const int64_t need = moe_align_max_blocks(S, a.num_experts, a.block_m);
+  if (a.max_blocks < need)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks %lld < required %lld", (long long)a.max_blocks,
+                (long long)need);
+  if (a.max_blocks * a.block_m >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks too large");
+  if (S > 0 && (a.a == nullptr || a.w == nullptr || a.c == nullptr || a.sorted_token_ids == nullptr ||
+                a.expert_ids == nullptr || a.num_tokens_post_pad == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (((uintptr_t)a.a | (uintptr_t)a.w) % 16 != 0 || (uintptr_t)a.c % 2 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "a and w must be 16-byte aligned, c 2-byte aligned");
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  if (S == 0 || a.max_blocks == 0) return ok();
+  const int64_t grid_guess = a.max_blocks * ((out_w + 7) / 8);
+  if (grid_guess >= (int64_t)UINT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
+
+  moe::GemmParams p;
+  p.a = static_cast<const uint16_t*>(a.a);
+  p.a_ld = a.a_ld;
+  p.a_row_div = a.a_row_div;
+  p.w = static_cast<const uint8_t*>(a.w);
+  p.w_stride_e = a.w_stride_e * w_elem_bytes;
+  p.w_ld = a.w_ld * w_elem_bytes;
+  p.ws = a.w_scale;
+  p.ws_stride_e = a.w_scale_stride_e;
+  p.ws_ld = a.w_scale_ld;
+  p.bias = static_cast<const uint16_t*>(a.bias);
+  p.bias_se = a.bias_stride_e;
+  p.bias_sn = a.bias_stride_n;
+  p.c = static_cast<uint16_t*>(a.c);
+  p.c_ld = a.c_ld;
+  p.sorted = a.sorted_token_ids;
+  p.expert_ids = a.expert_ids;
+  p.S = (int32_t)S;
+  p.N = (int32_t)a.n;
+  p.K = (int32_t)a.k;
+  p.max_blocks = (int32_t)a.max_blocks;
+  const bool decode = a.num_tokens <= kDecodeMaxTokens;
+  return hip_status(moe::launch_grouped_gemm(p, a.w_dtype, swiglu, a.bias != nullptr, decode,
+                                             (hipStream_t)stream),
+                    "moe_grouped_gemm launch");
+}
+
+moe_status moe_combine(const void* c, int64_t c_ld, const float* topk_w, int64_t num_tokens, int32_t top_k,
+                       int64_t n, void* y, int64_t y_ld, moe_stream_t stream) {
+  if (num_tokens < 0 || top_k < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens < 0 or top_k < 1");
+  if (n < 8 || n % 8 != 0 || n >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "n must be a positive multiple of 8");
+  if (c_ld < n || c_ld % 8 != 0 || y_ld < n || y_ld % 8 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "c_ld and y_ld must be >= n and multiples of 8");
+  if (num_tokens > 0 && (c == nullptr || topk_w == nullptr || y == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (((uintptr_t)c | (uintptr_t)y) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "c and y must be 16-byte aligned");
+  if (num_tokens * (n / 8) >= (int64_t)INT32_MAX * 128)
+    return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_combine(static_cast<const uint16_t*>(c), c_ld, topk_w, num_tokens, top_k, n,
+                                        static_cast<uint16_t*>(y), y_ld, (hipStream_t)stream),
+                    "moe_combine launch");
+}
+
+moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad_ld,
+                     const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                     const int32_t* num_tokens_post_pad, int64_t num_tokens, int32_t top_k,
+                     int32_t num_experts, int64_t n, int64_t k, int32_t block_m, int64_t max_blocks,
+                     float* dw, moe_stream_t stream) {
+  if (num_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (top_k < 1 || num_experts < top_k)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "need 1 <= top_k (%d) <= num_experts (%d)", top_k, num_experts);
+  if (n < 32 || n % 32 != 0 || k < 32 || k % 32 != 0 || n >= INT32_MAX || k >= INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "n and k must be positive multiples of 32");
+  if (x_ld < k || x_ld % 8 != 0 || grad_ld < n || grad_ld % 8 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x_ld / grad_ld must cover a row and be multiples of 8");
+  if (block_m != moe::wgrad_block_m())
+    return fail(MOE_ERR_INVALID_ARGUMENT, "block_m %d, expected %d", block_m, moe::wgrad_block_m());
+  const int64_t S = num_tokens * top_k;
+  if (S >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens * top_k must be < 2^31");
+  const int64_t need = moe_align_max_blocks(S, num_experts, block_m);
+  if (max_blocks < need)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks %lld < required %lld", (long long)max_blocks,
+                (long long)need);
+  if (max_blocks * block_m >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks too large");
+  if (dw == nullptr || (S > 0 && (x == nullptr || grad == nullptr || sorted_token_ids == nullptr ||
+                                  expert_ids == nullptr)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (((uintptr_t)x | (uintptr_t)grad) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x and grad must be 16-byte aligned");
+  const int64_t grid = (int64_t)num_experts * ((n + 127) / 128) * ((k + 127) / 128);
+  if (grid >= (int64_t)UINT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
+  (void)num_tokens_post_pad;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  moe::WgradParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.x_ld = x_ld;
+  p.grad = static_cast<const uint16_t*>(grad);
+  p.grad_ld = grad_ld;
+  p.sorted = sorted_token_ids;
+  p.expert_ids = expert_ids;
+  p.S = (int32_t)S;
+  p.top_k = top_k;
+  p.E = num_experts;
+  p.N = (int32_t)n;
+  p.K = (int32_t)k;
+  p.max_blocks = (int32_t)max_blocks;
+  p.tiles_n = 0;
+  p.tiles_k = 0;
+  p.dw = dw;
+  return hip_status(moe::launch_wgrad(p, (hipStream_t)stream), "moe_wgrad launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+"""GPU parity of moe_wgrad against the float64 oracle: small shapes in full,
+the full-size weight-gradient workload on sampled experts (including the last
+expert, whose dW starts past 2^31 elements), empty experts, zero-padded
+tokens, and identical bits on repeated calls (no accumulation across calls)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import assert_parity, host, need_gpu
+from oracle import wgrad as owgrad
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def run_wgrad(d, out=None):
+    import mixture_experts_grouped_moe_amd as moe
+    routing = moe.moe_align(d["ids"], d["E"], moe.moe_wgrad_block_m())
+    dw = moe.moe_wgrad(d["x"], d["grad"], routing, d["T"], d["k"], d["E"], out=out)
+    torch.cuda.synchronize()
+    return dw
+
+
+@pytest.mark.parametrize("T,k,E,N,K", [(300, 4, 8, 256, 384), (97, 2, 5, 160, 96), (1000, 8, 32, 64, 128)])
+def test_small_full(T, k, E, N, K):
+    d = synth.config5(seed=T, T=T, E=E, N=N, K=K, k=k, device="cuda")
+    poison = torch.full((E, N, K), float("nan"), device="cuda")
+    dw = run_wgrad(d, out=poison).cpu().double().numpy()
+    h = host(d)
+    ref = owgrad.wgrad(h["x"], h["grad"], h["ids"], k, E)
+    for e in range(E):
+        assert_parity(dw[e], ref[e], what=f"expert {e}")
+
+
+def test_empty_experts_are_zero_and_repeat_is_identical():
+    T, k, E, N, K = 64, 2, 16, 128, 128
+    d = synth.config5(seed=3, T=T, E=E, N=N, K=K, k=k, device="cuda")
+    ids = d["ids"].clone()
+    ids[ids >= 12] = ids[ids >= 12] % 4  # experts 12..15 get no tokens
+    # keep the k ids of each token distinct
+    ids[:, 1] = torch.where(ids[:, 1] == ids[:, 0], (ids[:, 0] + 4) % 12, ids[:, 1])
+    d["ids"] = ids.contiguous()
+    out = torch.full((E, N, K), 7.0, device="cuda")
+    a = run_wgrad(d, out=out).clone()
+    assert torch.all(a[12:] == 0)
+    b = run_wgrad(d, out=out)
+    assert torch.equal(a, b)
+    h = host(d)
+    ref = owgrad.wgrad(h["x"], h["grad"], h["ids"], k, E)
+    for e in range(12):
+        assert_parity(a[e].cpu().double().numpy(), ref[e])
+
+
+def test_zero_padded_tokens_do_not_change_dw():
+    T, k, E, N, K = 200, 4, 8, 128, 256
+    d = synth.config5(seed=4, T=T + 37, E=E, N=N, K=K, k=k, device="cuda")
+    d["grad"][T * k:] = 0
+    full = run_wgrad(d).clone()
+    d2 = dict(d, T=T, x=d["x"][:T].contiguous(), grad=d["grad"][:T * k].contiguous(),
+              ids=d["ids"][:T].contiguous())
+    part = run_wgrad(d2)
+    h = host(d2)
+    ref = owgrad.wgrad(h["x"], h["grad"], h["ids"], k, E)
+    for e in range(E):
+        assert_parity(full[e].cpu().double().numpy(), ref[e])
+        assert_parity(part[e].cpu().double().numpy(), ref[e])
+
+
+def test_full_size_sampled_experts():
+    # E=256, top-8, T=16384, x [T, 7168], grad [8T, 2048], dW fp32 [256, 2048, 7168]
+    d = synth.config5(device="cuda")
+    dw = run_wgrad(d)
+    h = host(d)
+    counts = np.bincount(h["ids"].reshape(-1), minlength=256)
+    assert counts.sum() == 16384 * 8
+    for e in (0, 131, 255):
+        ref = owgrad.wgrad_expert(h["x"], h["grad"], h["ids"], 8, e)
+        got = dw[e].cpu().double().numpy()
+        assert_parity(got, ref, what=f"expert {e} ({counts[e]} slots)")
+    # the last expert's output lives past INT32_MAX elements
+    assert 255 * 2048 * 7168 > 2 ** 31 - 1

@@ -1,0 +1,209 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, its host helpers agree with the oracle, and every argument check
+rejects bad calls before anything reaches a GPU (all calls here are invalid
+on purpose, so none of them launches a kernel)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import align as oalign
+from oracle import bucket as obucket
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+moe = pytest.importorskip("mixture_experts_grouped_moe_amd")
+L = moe.lib
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below is rejected first
+
+
+@pytest.fixture
+def no_device():
+    """The rejection tests pass fake pointers; keep them off any machine with a
+    GPU, where a check that wrongly let a call through would launch a kernel."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("argument-rejection tests run on hosts without a GPU")
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    syms = _declared_symbols()
+    assert len(syms) == 13, syms
+    for name in syms:
+        assert hasattr(L, name), name
+
+
+def test_bucket_matches_oracle_exhaustively():
+    for m in range(0, 65537):
+        assert moe.moe_bucket_round_up(m) == obucket.bucket_round_up(m)
+    assert moe.moe_bucket_round_up(-5) == -1
+
+
+@pytest.mark.parametrize("mx", [1, 15, 16, 17, 1000, 20000, 65536])
+def test_enumerate_matches_oracle(mx):
+    assert moe.moe_bucket_enumerate(mx) == obucket.bucket_enumerate(mx)
+
+
+def test_enumerate_capacity_query():
+    assert L.moe_bucket_enumerate(20000, None, 0) == 98
+    assert L.moe_bucket_enumerate(-1, None, 0) == -1
+    assert moe.moe_bucket_enumerate(0) == []
+
+
+def test_max_blocks_matches_oracle():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        S, E, B = int(rng.integers(0, 10 ** 6)), int(rng.integers(1, 1025)), int(rng.integers(1, 257))
+        assert moe.moe_align_max_blocks(S, E, B) == oalign.max_blocks(S, E, B)
+    assert moe.moe_align_max_blocks(-1, 4, 4) == -1
+
+
+def test_block_m_rule():
+    for wd in ("bf16", "e4m3", "e2m1x2"):
+        small = {moe.moe_gemm_block_m(wd, t) for t in range(0, 33)}
+        large = {moe.moe_gemm_block_m(wd, t) for t in (33, 100, 6554, 8192, 32768)}
+        assert len(small) == 1 and len(large) == 1 and small != large
+    # the decode threshold is a bucket, so padding never switches variants
+    assert moe.moe_decode_max_tokens() == 32 == moe.moe_bucket_round_up(32)
+    for t in range(1, 2000):
+        assert (t <= 32) == (moe.moe_bucket_round_up(t) <= 32)
+    assert L.moe_gemm_block_m(moe.MOE_E4M3, moe.MOE_E4M3, 100) == -1  # fp8 activations: not here
+    assert L.moe_gemm_block_m(moe.MOE_BF16, 99, 100) == -1
+
+
+def test_padding_policy():
+    # padding is exact only for bf16 activations x MXFP4 weights without
+    # dynamic activation scales; the flag is ignored everywhere else
+    codes = [moe.MOE_BF16, moe.MOE_FP32, moe.MOE_E4M3, moe.MOE_E2M1X2, moe.MOE_E8M0]
+    for a in codes:
+        for w in codes:
+            for dyn in (0, 1):
+                want = a == moe.MOE_BF16 and w == moe.MOE_E2M1X2 and dyn == 0
+                assert moe.moe_padding_supported(a, w, dyn) == want
+
+
+def test_status_strings():
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(1) == b"MOE_ERR_INVALID_ARGUMENT"
+    assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+def _align(ids=FAKE, T=10, k=2, E=8, B=16, s=FAKE, e=FAKE, p=FAKE, mb=None):
+    if mb is None:
+        mb = moe.moe_align_max_blocks(T * k, E, B) if T >= 0 else 0
+    return L.moe_align(ids, T, k, E, B, s, e, p, mb, None)
+
+
+def test_align_rejects(no_device):
+    assert _align(T=-1) == INVALID
+    assert _align(k=0) == INVALID
+    assert _align(k=9, E=8) == INVALID
+    assert _align(E=2000, k=2) == UNSUPPORTED
+    assert _align(B=0) == INVALID
+    assert _align(B=300) == INVALID
+    assert _align(mb=1) == INVALID
+    assert _align(ids=None) == INVALID
+    assert _align(p=None) == INVALID
+    assert _align(s=None) == INVALID
+
+
+def _gemm_args(**kw):
+    g = moe.MoeGemmArgs()
+    T, k, E, N, K = kw.pop("T", 100), kw.pop("k", 2), kw.pop("E", 8), kw.pop("N", 256), kw.pop("K", 128)
+    wd = kw.pop("w_dtype", moe.MOE_E2M1X2)
+    g.num_tokens, g.top_k, g.num_experts, g.n, g.k = T, k, E, N, K
+    g.a_dtype, g.a_row_div, g.a, g.a_ld = moe.MOE_BF16, k, 0x100000, K
+    wld = K // 2 if wd == moe.MOE_E2M1X2 else K
+    g.w_dtype, g.w, g.w_stride_e, g.w_ld = wd, 0x100000, N * wld, wld
+    g.w_scale, g.w_scale_stride_e, g.w_scale_ld = 0x100000, N * (K // 32), K // 32
+    g.epilogue, g.c, g.c_ld = 0, 0x100000, N
+    g.sorted_token_ids = g.expert_ids = g.num_tokens_post_pad = 0x100000
+    g.block_m = L.moe_gemm_block_m(moe.MOE_BF16, wd, T)
+    g.max_blocks = moe.moe_align_max_blocks(T * k, E, g.block_m)
+    for key, v in kw.items():
+        setattr(g, key, v)
+    return g
+
+
+def _gemm(**kw):
+    return L.moe_grouped_gemm(ctypes.byref(_gemm_args(**kw)), None)
+
+
+def test_grouped_gemm_rejects(no_device):
+    assert L.moe_grouped_gemm(None, None) == INVALID
+    assert _gemm(K=100) == INVALID                 # K % 32
+    assert _gemm(K=0) == INVALID
+    assert _gemm(N=255, epilogue=1) == INVALID     # odd N with SwiGLU
+    assert _gemm(epilogue=7) == INVALID
+    assert _gemm(block_m=32) == INVALID            # not the variant's block_m
+    assert _gemm(max_blocks=1) == INVALID
+    assert _gemm(a_row_div=3) == INVALID
+    assert _gemm(a_ld=64) == INVALID               # < K
+    assert _gemm(a_ld=130) == INVALID              # not a multiple of 8
+    assert _gemm(w_ld=16) == INVALID
+    assert _gemm(w_stride_e=10) == INVALID
+    assert _gemm(w_scale=0) == INVALID
+    assert _gemm(w_scale_ld=1) == INVALID
+    assert _gemm(c_ld=100) == INVALID              # < N
+    assert _gemm(c=0x100001) == INVALID            # odd address
+    assert _gemm(c=0) == INVALID
+    assert _gemm(a=0x100004) == INVALID            # misaligned
+    assert _gemm(top_k=9, E=8) == INVALID
+    assert _gemm(a_dtype=moe.MOE_E4M3) == UNSUPPORTED
+    assert _gemm(w_dtype=moe.MOE_FP32) == UNSUPPORTED
+    assert _gemm(num_tokens=-1) == INVALID
+    assert _gemm(bias=0x100000, bias_stride_e=-1) == INVALID
+
+
+def test_combine_rejects(no_device):
+    c = L.moe_combine
+    assert c(FAKE, 256, FAKE, -1, 2, 256, FAKE, 256, None) == INVALID
+    assert c(FAKE, 256, FAKE, 10, 0, 256, FAKE, 256, None) == INVALID
+    assert c(FAKE, 256, FAKE, 10, 2, 100, FAKE, 256, None) == INVALID
+    assert c(FAKE, 100, FAKE, 10, 2, 256, FAKE, 256, None) == INVALID
+    assert c(None, 256, FAKE, 10, 2, 256, FAKE, 256, None) == INVALID
+    assert c(ctypes.c_void_p(0x100002), 256, FAKE, 10, 2, 256, FAKE, 256, None) == INVALID
+
+
+def test_wgrad_rejects(no_device):
+    w = L.moe_wgrad
+    mb = moe.moe_align_max_blocks(80, 8, 64)
+    args = dict(x=FAKE, xld=256, g=FAKE, gld=128, s=FAKE, e=FAKE, p=FAKE, T=10, k=8, E=8,
+                n=128, kk=256, bm=64, mb=mb, dw=FAKE)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return w(a["x"], a["xld"], a["g"], a["gld"], a["s"], a["e"], a["p"], a["T"], a["k"], a["E"],
+                 a["n"], a["kk"], a["bm"], a["mb"], a["dw"], None)
+
+    assert call(bm=32) == INVALID
+    assert call(n=100) == INVALID
+    assert call(kk=200) == INVALID
+    assert call(k=9) == INVALID
+    assert call(mb=0) == INVALID
+    assert call(dw=None) == INVALID
+    assert call(xld=100) == INVALID
+    assert call(T=-1) == INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "moe_copy", os.path.join(ROOT, "mixture_experts_grouped_moe_amd", "__init__.py"))
+    mod = importlib.util.module_from_spec(spec)
+    src = open(spec.origin).read().replace(
+        'LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")',
+        f'LIB_PATH = {str(tmp_path / "missing.so")!r}')
+    with pytest.raises(ImportError):
+        exec(compile(src, spec.origin, "exec"), mod.__dict__)
