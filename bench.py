@@ -1,0 +1,542 @@
+"""Benchmark of the MoE expert-layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|w4a16|mxfp8|wgrad]
+
+Prints one JSON line. The default workload is the bf16 decode MoE
+(E=128, N=1856, K=2048, top-6) at the MTP6 verify token counts
+M = 1, 7, 14, 21, 28: one step runs, for each M, moe_align -> decode grouped
+GEMM -> moe_combine on a fresh routing (a seeded set of routings is cycled).
+`value` is the step's algorithmic HBM bytes over its time (GB/s); the
+per-call microseconds are reported beside it. The other workloads (the
+gpt-oss-shaped W4A16 MXFP4 layer, the 256-expert MXFP8 grouped GEMM, the
+weight gradient) are selected with --workload and report TFLOP/s.
+
+Inputs are synthetic (seeded), generated on the device before the timed
+region. Steps are replayed from HIP graphs captured once per routing variant.
+The dominant kernel's launch duration is measured with HIP events on the
+launch stream in a second timed pass of eager launches; the roofline fraction
+uses algorithmic bytes (or flops) per launch. The CPU baseline is the float64
+oracle on a bounded sample of the same workload, timed on this host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+METRIC = "grouped-GEMM TFLOP/s & % MFMA peak (large M); decode µs/call & % HBM BW"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode", choices=["decode", "w4a16", "mxfp8", "wgrad"])
+    ap.add_argument("--variants", type=int, default=4, help="routing variants cycled across steps")
+    ap.add_argument("--launch-reps", type=int, default=10,
+                    help="back-to-back launches per event pair when timing the dominant kernel")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.join(ROOT, "mixture_experts_grouped_moe_amd", "csrc"))):
+        with open(os.path.join(ROOT, "mixture_experts_grouped_moe_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, launches_units):
+    """HBM traffic per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------- workloads
+
+class LazyRows:
+    """Host view of a device tensor that copies one leading-index slice (an
+    expert's weights) on first use and keeps it, so the CPU oracle's timed
+    passes read host memory only."""
+
+    def __init__(self, t):
+        self.t, self.shape, self.cache = t, tuple(t.shape), {}
+
+    def __getitem__(self, i):
+        import synth
+        i = int(i)
+        if i not in self.cache:
+            self.cache[i] = synth.bits(self.t[i])
+        return self.cache[i]
+
+
+class Workload:
+    """A set of pre-generated inputs and the launches of one step."""
+    name = ""
+    dominant = ""          # kernel name as rocprofv3 reports it (prefix)
+    bound = "hbm"
+
+    def step(self, v):            # eager launches of one step on the current stream
+        raise NotImplementedError
+
+    def dominant_launches(self, v):  # list of (callable, algorithmic units) for the dominant kernel
+        raise NotImplementedError
+
+
+def _routing_buffers(torch, T, k, E, bm, dev):
+    import mixture_experts_grouped_moe_amd as moe
+    mb = moe.moe_align_max_blocks(T * k, E, bm)
+    return (torch.empty(mb * bm, dtype=torch.int32, device=dev),
+            torch.empty(mb, dtype=torch.int32, device=dev),
+            torch.empty(1, dtype=torch.int32, device=dev))
+
+
+class Decode(Workload):
+    name = "decode"
+    dominant = "moe_decode_kernel"
+    bound = "hbm"
+    MS = (1, 7, 14, 21, 28)
+
+    def __init__(self, torch, dev, variants):
+        import numpy as np
+        import mixture_experts_grouped_moe_amd as moe
+        import synth
+        self.torch, self.moe = torch, moe
+        self.E, self.N, self.K, self.k = 128, 1856, 2048, 6
+        self.w = synth.bf16_normal((self.E, self.N, self.K), 0.02, 1002, "w", dev)
+        self.calls = []   # per variant: list of dicts per M
+        self.bytes_gemm = []  # per variant: list of algorithmic GEMM bytes per M
+        for v in range(variants):
+            per_m, per_b = [], []
+            for M in self.MS:
+                x = synth.bf16_normal((M, self.K), 1.0, 1002, f"x{M}v{v}", dev)
+                ids, tw = synth.softmax_topk_routing(M, self.E, self.k, 1002, f"route{M}v{v}", dev)
+                bm = moe.moe_gemm_block_m("bf16", M)
+                c = dict(M=M, x=x, ids=ids, tw=tw, bm=bm,
+                         routing=_routing_buffers(torch, M, self.k, self.E, bm, dev),
+                         C=torch.empty((M * self.k, self.N), dtype=torch.bfloat16, device=dev),
+                         y=torch.empty((M, self.N), dtype=torch.bfloat16, device=dev))
+                touched = len(np.unique(ids.cpu().numpy()))
+                c["touched"] = touched
+                per_b.append(touched * self.N * self.K * 2 + M * self.K * 2 + M * self.k * self.N * 2)
+                per_m.append(c)
+            self.calls.append(per_m)
+            self.bytes_gemm.append(per_b)
+
+    def _call_bytes(self, v, i):
+        c = self.calls[v][i]
+        S = c["M"] * self.k
+        mb = c["routing"][1].numel()
+        align = S * 4 + mb * c["bm"] * 4 + mb * 4 + 4
+        combine = S * self.N * 2 + c["M"] * self.N * 2 + S * 4
+        return self.bytes_gemm[v][i] + align + combine
+
+    def step_bytes(self, v):
+        return sum(self._call_bytes(v, i) for i in range(len(self.MS)))
+
+    def step_flops(self, v):
+        return sum(2 * c["M"] * self.k * self.N * self.K for c in self.calls[v])
+
+    def _gemm(self, c):
+        if "gemm_call" not in c:
+            c["gemm_call"], _ = self.moe.moe_grouped_gemm_prepare(
+                c["x"], self.w, "bf16", c["routing"], c["M"], self.k, self.E, self.k, out=c["C"])
+        return c["gemm_call"]()
+
+    def step(self, v):
+        moe = self.moe
+        for c in self.calls[v]:
+            moe.moe_align(c["ids"], self.E, c["bm"], out=c["routing"])
+            self._gemm(c)
+            moe.moe_combine(c["C"], c["tw"], self.k, out=c["y"])
+
+    def dominant_launches(self, v):
+        return [(lambda c=c: self._gemm(c), self.bytes_gemm[v][i]) for i, c in enumerate(self.calls[v])]
+
+    def extra(self, per_call_us):
+        return {"us_per_call": {str(M): round(t, 2) for M, t in zip(self.MS, per_call_us)},
+                "touched_experts": {str(M): self.calls[0][i]["touched"] for i, M in enumerate(self.MS)}}
+
+    cpu_sample_desc = "align + decode GEMM + combine for M = 1, 7, 14, 21, 28 of routing variant 0"
+
+    def cpu_sample(self):
+        """Oracle on variant 0, all five calls (align + GEMM + combine)."""
+        import synth
+        from oracle import align as oalign, gemm as ogemm
+        lw = LazyRows(self.w)
+        items = []
+        for i, c in enumerate(self.calls[0]):
+            items.append((synth.bits(c["x"]), synth.bits(c["ids"]), synth.bits(c["tw"]), c["bm"], i))
+
+        def run(item):
+            x, ids, tw, bm, i = item
+            oalign.moe_align(ids, self.E, bm)
+            C, _ = ogemm.grouped_gemm(x, self.k, lw, "bf16", None, ids, self.E)
+            ogemm.combine(C, tw, self.k)
+            return self._call_bytes(0, i)
+        return items, run, "GB/s"
+
+
+class W4A16(Workload):
+    name = "w4a16"
+    dominant = "moe_gemm_kernel<4, true"
+    bound = "mfma"
+
+    def __init__(self, torch, dev, variants):
+        import mixture_experts_grouped_moe_amd as moe
+        import synth
+        self.torch, self.moe = torch, moe
+        self.E, self.H, self.I, self.k = 128, 2880, 2880, 4
+        d = synth.config3(8192, device=dev)
+        self.d = d
+        self.Ts = synth.draw_token_counts(variants, 6554, 8192, seed=1003)
+        self.calls = []
+        for T in self.Ts:
+            Tb = moe.moe_bucket_round_up(T)
+            x = d["x"][:Tb].clone()
+            x[T:] = 0
+            bm = moe.moe_gemm_block_m("e2m1x2", Tb)
+            self.calls.append(dict(T=T, Tb=Tb, x=x, ids=d["ids"][:Tb].contiguous(), tw=d["topk_w"][:Tb].contiguous(),
+                                   bm=bm, routing=_routing_buffers(torch, Tb, self.k, self.E, bm, dev),
+                                   h=torch.empty((Tb * self.k, self.I), dtype=torch.bfloat16, device=dev),
+                                   c2=torch.empty((Tb * self.k, self.H), dtype=torch.bfloat16, device=dev),
+                                   y=torch.empty((T, self.H), dtype=torch.bfloat16, device=dev)))
+
+    def step_flops(self, v):
+        T = self.calls[v]["T"]
+        return 2 * T * self.k * (2 * self.I * self.H + self.H * self.I)
+
+    def step_bytes(self, v):
+        c = self.calls[v]
+        S = c["T"] * self.k
+        w = self.E * (2 * self.I * self.H + self.H * self.I) // 2 * (1 + 1 / 16)
+        return int(w + c["T"] * self.H * 2 + S * self.I * 2 * 2 + S * self.H * 2 * 2 + c["T"] * self.H * 2)
+
+    def _up(self, c):
+        d = self.d
+        return self.moe.moe_grouped_gemm(c["x"], d["w1"], "e2m1x2", c["routing"], c["Tb"], self.k, self.E, self.k,
+                                         w_scale=d["s1"], epilogue="swiglu", out=c["h"])
+
+    def step(self, v):
+        c, d, moe = self.calls[v], self.d, self.moe
+        moe.moe_align(c["ids"], self.E, c["bm"], out=c["routing"])
+        self._up(c)
+        moe.moe_grouped_gemm(c["h"], d["w2"], "e2m1x2", c["routing"], c["Tb"], self.k, self.E, 1,
+                             w_scale=d["s2"], out=c["c2"])
+        moe.moe_combine(c["c2"], c["tw"], self.k, num_tokens=c["T"], out=c["y"])
+
+    def dominant_launches(self, v):
+        c = self.calls[v]
+        return [(lambda c=c: self._up(c), 2 * c["T"] * self.k * 2 * self.I * self.H)]
+
+    def extra(self, per_call_us):
+        return {"tokens": [c["T"] for c in self.calls], "buckets": [c["Tb"] for c in self.calls]}
+
+    cpu_sample_desc = "gate+up GEMM with SwiGLU and down GEMM over all slots of experts 0-3"
+
+    def cpu_sample(self):
+        """Oracle layer on the slots of 4 experts of variant 0 (up and down GEMM rows)."""
+        import numpy as np
+        import synth
+        from oracle import layer as olayer
+        c = self.calls[0]
+        ids = synth.bits(c["ids"])[:c["T"]]
+        d = self.d
+        xs = synth.bits(c["x"])
+        w1, s1, w2, s2 = LazyRows(d["w1"]), LazyRows(d["s1"]), LazyRows(d["w2"]), LazyRows(d["s2"])
+        flat = ids.reshape(-1)
+        items = []
+        for e in range(4):
+            slots = np.nonzero(flat == e)[0]
+            items.append(slots)
+
+        def run(slots):
+            olayer.w4a16_layer(xs, ids, None, self.k, self.E, w1, s1, None, w2, s2, None, slots=slots)
+            return 2 * len(slots) * (2 * self.I * self.H + self.H * self.I)
+        return items, run, "TFLOP/s"
+
+
+class MXFP8(Workload):
+    name = "mxfp8"
+    cpu_sample_desc = "grouped GEMM over all slots of the median-load and the top-load expert"
+    dominant = "moe_gemm_kernel<3, false"
+    bound = "hbm"
+
+    def __init__(self, torch, dev, variants, bias=False):
+        import numpy as np
+        import mixture_experts_grouped_moe_amd as moe
+        import synth
+        self.torch, self.moe = torch, moe
+        d = synth.config4(device=dev, bias=bias)
+        self.d = d
+        self.E, self.N, self.K, self.k, self.T = 256, 4096, 7168, 8, 4096
+        bm = moe.moe_gemm_block_m("e4m3", self.T)
+        self.bm = bm
+        self.routing = _routing_buffers(torch, self.T, self.k, self.E, bm, dev)
+        self.C = torch.empty((self.T * self.k, self.N), dtype=torch.bfloat16, device=dev)
+        counts = np.bincount(synth.bits(d["ids"]).reshape(-1), minlength=self.E)
+        self.touched = int((counts > 0).sum())
+        self.empty = int((counts == 0).sum())
+
+    def step_flops(self, v):
+        return 2 * self.T * self.k * self.N * self.K
+
+    def gemm_bytes(self):
+        w = self.touched * self.N * self.K * (1 + 1 / 32)
+        return int(w + self.T * self.K * 2 + self.T * self.k * self.N * 2)
+
+    def step_bytes(self, v):
+        return self.gemm_bytes()
+
+    def _gemm(self):
+        d = self.d
+        return self.moe.moe_grouped_gemm(d["x"], d["w"], "e4m3", self.routing, self.T, self.k, self.E, self.k,
+                                         w_scale=d["w_scale"], bias=d["bias"], out=self.C)
+
+    def step(self, v):
+        self.moe.moe_align(self.d["ids"], self.E, self.bm, out=self.routing)
+        self._gemm()
+
+    def dominant_launches(self, v):
+        return [(self._gemm, self.gemm_bytes())]
+
+    def extra(self, per_call_us):
+        return {"touched_experts": self.touched, "empty_experts": self.empty}
+
+    def cpu_sample(self):
+        import numpy as np
+        import synth
+        from oracle import gemm as ogemm
+        d = self.d
+        ids = synth.bits(d["ids"])
+        flat = ids.reshape(-1)
+        x, w, ws = synth.bits(d["x"]), LazyRows(d["w"]), LazyRows(d["w_scale"])
+        counts = np.bincount(flat, minlength=self.E)
+        order = np.argsort(counts)
+        experts = [int(order[len(order) // 2]), int(order[-1])]
+        items = [np.nonzero(flat == e)[0] for e in experts]
+
+        def run(slots):
+            ogemm.grouped_gemm(x, self.k, w, "e4m3", ws, ids, self.E, slots=slots)
+            return 2 * len(slots) * self.N * self.K
+        return items, run, "TFLOP/s"
+
+
+class Wgrad(Workload):
+    name = "wgrad"
+    cpu_sample_desc = "dW of experts 0, 128 and 255"
+    dominant = "wgrad_kernel"
+    bound = "hbm"
+
+    def __init__(self, torch, dev, variants):
+        import mixture_experts_grouped_moe_amd as moe
+        import synth
+        self.torch, self.moe = torch, moe
+        d = synth.config5(device=dev)
+        self.d = d
+        self.E, self.N, self.K, self.k, self.T = 256, 2048, 7168, 8, 16384
+        self.routing = _routing_buffers(torch, self.T, self.k, self.E, moe.moe_wgrad_block_m(), dev)
+        self.dw = torch.empty((self.E, self.N, self.K), dtype=torch.float32, device=dev)
+
+    def step_flops(self, v):
+        return 2 * self.T * self.k * self.N * self.K
+
+    def wgrad_bytes(self):
+        return self.E * self.N * self.K * 4 + self.T * self.K * 2 + self.T * self.k * self.N * 2
+
+    def step_bytes(self, v):
+        return self.wgrad_bytes()
+
+    def _wgrad(self):
+        d = self.d
+        return self.moe.moe_wgrad(d["x"], d["grad"], self.routing, self.T, self.k, self.E, out=self.dw)
+
+    def step(self, v):
+        self.moe.moe_align(self.d["ids"], self.E, self.moe.moe_wgrad_block_m(), out=self.routing)
+        self._wgrad()
+
+    def dominant_launches(self, v):
+        return [(self._wgrad, self.wgrad_bytes())]
+
+    def extra(self, per_call_us):
+        return {}
+
+    def cpu_sample(self):
+        import numpy as np
+        import synth
+        from oracle import wgrad as owgrad
+        d = self.d
+        ids = synth.bits(d["ids"])
+        x, g = synth.bits(d["x"]), synth.bits(d["grad"])
+        items = [0, 128, 255]
+
+        def run(e):
+            owgrad.wgrad_expert(x, g, ids, self.k, e)
+            slots = int((ids.reshape(-1) == e).sum())
+            return 2 * slots * self.N * self.K
+        return items, run, "TFLOP/s"
+
+
+WORKLOADS = {"decode": Decode, "w4a16": W4A16, "mxfp8": MXFP8, "wgrad": Wgrad}
+CONFIG_NAMES = {
+    "decode": "decode bf16 MoE, E=128 N=1856 K=2048 top-6, M in {1,7,14,21,28}",
+    "w4a16": "W4A16 MXFP4 MoE layer (gpt-oss-shaped), E=128 top-4 H=2880, gate+up 5760 -> SwiGLU -> down 2880, T~U[6554,8192] bucketed",
+    "mxfp8": "MXFP8 grouped GEMM, E=256 top-8 K=7168 N=4096 T=4096, Zipf(1.1) routing with 16 empty experts",
+    "wgrad": "moe_wgrad, E=256 top-8 T=16384, x [T,7168], grad [8T,2048], fp32 dW [256,2048,7168]",
+}
+
+
+def cpu_baseline(wl, target_s):
+    """Time the float64 oracle on a bounded sample of the workload."""
+    import numpy as np
+    items, run, unit = wl.cpu_sample()
+    cores = len(os.sched_getaffinity(0))
+    for it in items:  # untimed pass: moves the sample's device data to host memory
+        run(it)
+    done_units, n, t0 = 0, 0, time.perf_counter()
+    while True:  # cycle over the sample until the time target (at least one pass)
+        done_units += run(items[n % len(items)])
+        n += 1
+        if n >= len(items) and time.perf_counter() - t0 > target_s:
+            break
+    dt = time.perf_counter() - t0
+    scale = 1e9 if unit == "GB/s" else 1e12
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+    except Exception:
+        threads = cores
+    _ = np
+    return {"value": done_units / dt / scale, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} runs over a {len(items)}-item sample of the {wl.name} workload "
+                      f"({wl.cpu_sample_desc}), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of this "
+                                   "build (--gpus must be 1)"}))
+        sys.exit(2)
+    import torch
+    import mixture_experts_grouped_moe_amd as moe  # noqa: F401  (fails loudly if libmoe.so is missing)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS[args.workload](torch, dev, args.variants)
+    nv = len(getattr(wl, "calls", [None])) if args.workload in ("decode", "w4a16") else 1
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    # capture one graph per routing variant (the step's launches only)
+    graphs = []
+    with torch.cuda.stream(stream):
+        for v in range(nv):
+            wl.step(v)  # eager run first (warms caches of the library and allocator)
+        torch.cuda.synchronize()
+        for v in range(nv):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                wl.step(v)
+            graphs.append(g)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % nv].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % nv].replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt / args.steps * 1e3
+    step_bytes = sum(wl.step_bytes(i % nv) for i in range(args.steps))
+    step_flops = sum(wl.step_flops(i % nv) for i in range(args.steps))
+
+    # dominant kernel: HIP events on the launch stream around a run of
+    # back-to-back launches of it (same inputs; each launch overwrites its
+    # output), so the average excludes host-side launch cost
+    n_dom = 0
+    dom_units, dom_time_ms = 0.0, 0.0
+    per_call = {}
+    reps = args.launch_reps
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            v = i % nv
+            for j, (fn, units) in enumerate(wl.dominant_launches(v)):
+                fn()  # queue ahead so the timed launches run back to back
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(reps):
+                    fn()
+                b.record(stream)
+                b.synchronize()
+                t = a.elapsed_time(b) / reps
+                dom_time_ms += t
+                dom_units += units
+                n_dom += 1
+                per_call.setdefault(j, []).append(t * 1e3)
+    torch.cuda.synchronize()
+    avg_launch_us = dom_time_ms / n_dom * 1e3
+    if wl.bound == "hbm":
+        achieved = dom_units / (dom_time_ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved = dom_units / (dom_time_ms * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    traffic = load_traffic(wl.name, None)
+    roofline = {"bound": wl.bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "kernel": wl.dominant, "avg_launch_us": round(avg_launch_us, 3)}
+
+    if args.workload == "decode":
+        value = step_bytes / dt / 1e9
+        unit_v = "GB/s"
+        extra = wl.extra([sum(v) / len(v) for _, v in sorted(per_call.items())])
+        extra["hbm_frac_step"] = round(value / PEAK_HBM_GBS, 4)
+        dtype = "bf16"
+    else:
+        value = step_flops / dt / 1e12
+        unit_v = "TFLOP/s"
+        extra = wl.extra(None)
+        extra["mfma_frac_step_bf16"] = round(value / PEAK_BF16_TFLOPS, 4)
+        extra["hbm_GBps_step"] = round(step_bytes / dt / 1e9, 1)
+        dtype = {"w4a16": "bf16 x e2m1 (bf16 MFMA)", "mxfp8": "bf16 x e4m3 (bf16 MFMA)",
+                 "wgrad": "bf16 (bf16 MFMA, fp32 out)"}[args.workload]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    line = {"metric": METRIC, "value": round(value, 3), "unit": unit_v, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+            "config": {"workload": CONFIG_NAMES[args.workload], "routing_variants": nv,
+                       "parallelism": "single GPU"},
+            "roofline": roofline, "cpu_baseline": cpu}
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,8 @@ __all__ = [
     "MoeError", "lib", "MOE_BF16", "MOE_FP32", "MOE_E4M3", "MOE_E2M1X2", "MOE_E8M0",
     "moe_bucket_round_up", "moe_bucket_enumerate", "moe_padding_supported",
     "moe_align_max_blocks", "moe_gemm_block_m", "moe_wgrad_block_m", "moe_decode_max_tokens",
-    "moe_align", "moe_grouped_gemm", "moe_combine", "moe_wgrad", "moe_w4a16_layer",
+    "moe_align", "moe_grouped_gemm", "moe_grouped_gemm_prepare", "moe_combine", "moe_wgrad",
+    "moe_w4a16_layer",
     "LIB_PATH",
 ]
 
@@ -192,14 +193,27 @@ def moe_align(topk_ids, num_experts, block_m, num_tokens=None, out=None, stream=
 def moe_grouped_gemm(a, w, w_dtype, routing, num_tokens, top_k, num_experts, a_row_div,
                      w_scale=None, bias=None, epilogue="none", out=None, block_m=None,
                      stream=None):
+    """See moe_grouped_gemm_prepare; this builds the call and runs it once."""
+    call, out = moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_experts, a_row_div,
+                                         w_scale=w_scale, bias=bias, epilogue=epilogue, out=out,
+                                         block_m=block_m, stream=stream)
+    call()
+    return out
+
+
+def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_experts, a_row_div,
+                             w_scale=None, bias=None, epilogue="none", out=None, block_m=None,
+                             stream=None):
     """Routed grouped GEMM: C[s] = epilogue(A[s // a_row_div] . W_hat[e]^T + bias[e]).
 
     a: bf16 [rows, K]; w: [E, N, K] bf16 / uint8 E4M3 codes, or uint8 [E, N, K/2]
     packed E2M1; w_scale: uint8 E8M0 [E, N, K/32]; bias: bf16 [E, N] (any
     strides); routing: the (sorted_token_ids, expert_ids, num_tokens_post_pad)
     of moe_align with block_m = moe_gemm_block_m(w_dtype, num_tokens).
-    Returns C, bf16 [num_tokens * top_k, N or N/2] (rows of unrouted slots are
-    left as they were).
+    C is bf16 [num_tokens * top_k, N or N/2]; rows of unrouted slots are left
+    as they were. Returns (call, C): call() launches the GEMM on the stream
+    captured here, with the arguments checked and marshalled once (for tight
+    loops and graph capture).
     """
     wd = _W_DTYPES[w_dtype]
     _need(a, "a", torch.bfloat16, 2)
@@ -242,8 +256,15 @@ def moe_grouped_gemm(a, w, w_dtype, routing, num_tokens, top_k, num_experts, a_r
     g.sorted_token_ids, g.expert_ids = sorted_ids.data_ptr(), expert_ids.data_ptr()
     g.num_tokens_post_pad = post_pad.data_ptr()
     g.block_m, g.max_blocks = int(bm), expert_ids.numel()
-    _check(lib.moe_grouped_gemm(ctypes.byref(g), _stream(stream)))
-    return out
+    st = _stream(stream)
+    ref = ctypes.byref(g)
+    keep = (a, w, w_scale, bias, out, routing)  # the call holds its tensors alive
+
+    def call():
+        _check(lib.moe_grouped_gemm(ref, st))
+        return keep[4]
+    call.args = g
+    return call, out
 
 
 def moe_combine(c, topk_w, top_k, num_tokens=None, out=None, stream=None):
