@@ -28,7 +28,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["api.cpp", "align.hip", "gemm.hip", "combine.hip", "wgrad.hip"]
+SOURCES = ["api.cpp", "align.hip", "gemm.hip", "decode.hip", "combine.hip", "wgrad.hip"]
 
 
 def _hipcc():

@@ -198,6 +198,13 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (((uintptr_t)a.a | (uintptr_t)a.w) % 16 != 0 || (uintptr_t)a.c % 2 != 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "a and w must be 16-byte aligned, c 2-byte aligned");
+  // the large-M kernel addresses A, one expert's weights and one expert's
+  // scales through 32-bit buffer offsets
+  const int64_t a_rows = S > 0 ? (S - 1) / a.a_row_div + 1 : 0;
+  constexpr int64_t kBufMax = (int64_t)0xFFFFFFF0;
+  if (a_rows * a.a_ld * 2 >= kBufMax || a.n * a.w_ld * w_elem_bytes >= kBufMax ||
+      (a.w_dtype != MOE_BF16 && a.n * a.w_scale_ld >= kBufMax))
+    return fail(MOE_ERR_UNSUPPORTED, "A, one expert's weights or its scales exceed 4 GB");
   moe_status st = check_device();
   if (st != MOE_OK) return st;
   if (S == 0 || a.max_blocks == 0) return ok();
@@ -207,6 +214,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   moe::GemmParams p;
   p.a = static_cast<const uint16_t*>(a.a);
   p.a_ld = a.a_ld;
+  p.a_rows = a_rows;
   p.a_row_div = a.a_row_div;
   p.w = static_cast<const uint8_t*>(a.w);
   p.w_stride_e = a.w_stride_e * w_elem_bytes;
@@ -226,8 +234,9 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   p.K = (int32_t)a.k;
   p.max_blocks = (int32_t)a.max_blocks;
   const bool decode = a.num_tokens <= kDecodeMaxTokens;
-  return hip_status(moe::launch_grouped_gemm(p, a.w_dtype, swiglu, a.bias != nullptr, decode,
-                                             (hipStream_t)stream),
+  const bool bias = a.bias != nullptr;
+  return hip_status(decode ? moe::launch_gemm_decode(p, a.w_dtype, swiglu, bias, (hipStream_t)stream)
+                           : moe::launch_gemm_large(p, a.w_dtype, swiglu, bias, (hipStream_t)stream),
                     "moe_grouped_gemm launch");
 }
 

@@ -1,0 +1,208 @@
+// Decode variant of the routed grouped GEMM (at most 32 tokens): weight
+// streaming at HBM speed.
+#include "common.h"
+#include "params.h"
+
+namespace moe {
+
+constexpr int kThreadsDec = 256;
+
+// ---------------------------------------------------------------------------
+// Decode variant (at most 32 tokens): each touched expert's weight rows are
+// streamed once from HBM. A workgroup owns (routing block of 8 slots, 16 weight
+// rows); each wave streams 4 full rows with 16-byte loads spread over its 64
+// lanes, so each lane holds a K-slice of every row, and keeps one fp32 partial
+// per (row, slot). The slots' activations are staged in LDS, 2048 K-elements
+// at a time. Partials are reduced across the wave at the end (a fixed order,
+// so results are reproducible). Splitting N this finely gives thousands of
+// workgroups even at one token, enough bytes in flight to fill HBM.
+// Follows torchada PR #115 "tune the Nemotron MTP decode row on S5000 with a
+// checked-in recipe": What it does (the tiny-M bucket, M <= 32, dominates the
+// decode step) and "Follow-up on this table" (the tiny-M path is chosen by
+// M <= 32, never by a tuned table).
+// ---------------------------------------------------------------------------
+constexpr int kDecBM = 8;         // routing block for decode
+constexpr int kDecRowsPerWave = 4;
+constexpr int kDecRows = 4 * kDecRowsPerWave;  // weight rows per workgroup
+constexpr int kDecKC = 2048;      // K elements staged per pass
+
+template <int WDT, bool SWIGLU, bool BIAS>
+__global__ __launch_bounds__(kThreadsDec) void moe_decode_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kDecBM][kDecKC];
+  __shared__ int32_t s_slot[kDecBM];
+
+  const int b = blockIdx.x % p.max_blocks;
+  const int chunk = blockIdx.x / p.max_blocks;
+  const int e = p.expert_ids[b];
+  if (e < 0) return;  // sentinel block
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  if (tid < kDecBM) s_slot[tid] = p.sorted[(int64_t)b * kDecBM + tid];
+  __syncthreads();
+  // which of the block's positions hold a real slot (PAD marks the rest)
+  uint32_t vmask = 0;
+#pragma unroll
+  for (int j = 0; j < kDecBM; ++j) vmask |= (s_slot[j] < p.S ? 1u : 0u) << j;
+
+  // this wave's weight rows (and output columns)
+  int32_t wrow[kDecRowsPerWave], ocol[kDecRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kDecRowsPerWave; ++r) {
+    if (!SWIGLU) {
+      const int n = chunk * kDecRows + wave * kDecRowsPerWave + r;
+      wrow[r] = n < p.N ? n : -1;
+      ocol[r] = wrow[r];
+    } else {
+      const int half = p.N / 2;
+      const int hcol = chunk * (kDecRows / 2) + wave * (kDecRowsPerWave / 2) + (r % 2);
+      const bool up = r >= 2;
+      wrow[r] = hcol < half ? (up ? half + hcol : hcol) : -1;
+      ocol[r] = hcol < half ? hcol : -1;
+    }
+  }
+  const uint8_t* w_base = p.w + (int64_t)e * p.w_stride_e;
+  const uint8_t* ws_base = (WDT != W_BF16) ? p.ws + (int64_t)e * p.ws_stride_e : nullptr;
+
+  float acc[kDecRowsPerWave][kDecBM];
+#pragma unroll
+  for (int r = 0; r < kDecRowsPerWave; ++r)
+#pragma unroll
+    for (int j = 0; j < kDecBM; ++j) acc[r][j] = 0.0f;
+
+  constexpr int kPer = kDecKC / 8 / kWave;  // 8-element pieces per lane per pass
+  for (int kc = 0; kc < p.K; kc += kDecKC) {
+    __syncthreads();
+    // stage the real slots' activations: kDecBM rows x kDecKC (zeros for PAD)
+    for (int q = tid; q < kDecBM * (kDecKC / 8); q += kThreadsDec) {
+      const int j = q / (kDecKC / 8), c = q % (kDecKC / 8);
+      u32x4_t v = {0, 0, 0, 0};
+      if (((vmask >> j) & 1u) && kc + c * 8 < p.K)
+        v = *reinterpret_cast<const u32x4_t*>(p.a + (int64_t)(s_slot[j] / p.a_row_div) * p.a_ld + kc + c * 8);
+      *reinterpret_cast<u32x4_t*>(&xs[j][c * 8]) = v;
+    }
+    __syncthreads();
+
+    // weight pieces: [row][i] holds elements kc + 8 * (lane + 64 i) .. +8
+    bf16x8_t wv[kDecRowsPerWave][kPer];
+#pragma unroll
+    for (int r = 0; r < kDecRowsPerWave; ++r) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int k = kc + 8 * (lane + kWave * i);
+        const bool ok = wrow[r] >= 0 && k < p.K;
+        const uint8_t* rowp = w_base + (int64_t)(ok ? wrow[r] : 0) * p.w_ld;
+        if constexpr (WDT == W_BF16) {
+          u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(rowp + (int64_t)k * 2) : u32x4_t{0, 0, 0, 0};
+          __builtin_memcpy(&wv[r][i], &v, 16);
+        } else {
+          const uint8_t sb = ok ? ws_base[(int64_t)wrow[r] * p.ws_ld + k / 32] : 127;
+          const float sc = e8m0_as_scale(sb);
+          if constexpr (WDT == W_E4M3) {
+            u32x2_t v = ok ? *reinterpret_cast<const u32x2_t*>(rowp + k) : u32x2_t{0, 0};
+            wv[r][i] = dequant_e4m3x8(v[0], v[1], sc);
+          } else {
+            uint32_t v = ok ? *reinterpret_cast<const uint32_t*>(rowp + k / 2) : 0u;
+            wv[r][i] = dequant_e2m1x8(v, sc);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = lane + kWave * i;
+#pragma unroll
+      for (int j = 0; j < kDecBM; ++j) {
+        if ((vmask >> j) & 1u) {
+          const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(&xs[j][c * 8]);
+#pragma unroll
+          for (int r = 0; r < kDecRowsPerWave; ++r) {
+            float a = acc[r][j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              bf16x2_t x2, w2;
+              __builtin_memcpy(&x2, reinterpret_cast<const char*>(&xv) + 4 * q, 4);
+              __builtin_memcpy(&w2, reinterpret_cast<const char*>(&wv[r][i]) + 4 * q, 4);
+              a = __builtin_amdgcn_fdot2_f32_bf16(x2, w2, a, false);
+            }
+            acc[r][j] = a;
+          }
+        }
+      }
+    }
+  }
+
+  // reduce each partial over the wave's 64 lanes (butterfly, fixed order)
+#pragma unroll
+  for (int r = 0; r < kDecRowsPerWave; ++r)
+#pragma unroll
+    for (int j = 0; j < kDecBM; ++j) {
+      if ((vmask >> j) & 1u) {
+        float v = acc[r][j];
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+        acc[r][j] = v;
+      }
+    }
+
+  if (lane < kDecBM && ((vmask >> lane) & 1u)) {
+    const int s = s_slot[lane];
+    uint16_t* crow = p.c + (int64_t)s * p.c_ld;
+    float bvals[kDecRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kDecRowsPerWave; ++r)
+      bvals[r] = (BIAS && wrow[r] >= 0)
+                     ? bf16_bits_to_f32(p.bias[(int64_t)e * p.bias_se + (int64_t)wrow[r] * p.bias_sn])
+                     : 0.0f;
+    // select this lane's slot column from the (uniform) partials
+    float v[kDecRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kDecRowsPerWave; ++r) {
+      v[r] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kDecBM; ++j) v[r] = (j == lane) ? acc[r][j] : v[r];
+      v[r] += bvals[r];
+    }
+    if (!SWIGLU) {
+#pragma unroll
+      for (int r = 0; r < kDecRowsPerWave; ++r)
+        if (ocol[r] >= 0) crow[ocol[r]] = (uint16_t)f32_to_bf16_bits(v[r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (ocol[r] >= 0) crow[ocol[r]] = (uint16_t)f32_to_bf16_bits(silu_f32(v[r]) * v[r + 2]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+#define MOE_LAUNCH_DEC(WDT, SW, BI) \
+  hipLaunchKernelGGL((moe_decode_kernel<WDT, SW, BI>), grid, dim3(kThreadsDec), 0, stream, p)
+
+template <int WDT>
+static void launch_decode_wdt(const GemmParams& p, bool swiglu, bool bias, dim3 grid, hipStream_t stream) {
+  if (swiglu) {
+    if (bias) MOE_LAUNCH_DEC(WDT, true, true);
+    else MOE_LAUNCH_DEC(WDT, true, false);
+  } else {
+    if (bias) MOE_LAUNCH_DEC(WDT, false, true);
+    else MOE_LAUNCH_DEC(WDT, false, false);
+  }
+}
+
+int gemm_block_m_decode() { return kDecBM; }
+
+hipError_t launch_gemm_decode(const GemmParams& p, int wdt, bool swiglu, bool bias, hipStream_t stream) {
+  if (p.max_blocks <= 0) return hipSuccess;
+  const int rows = swiglu ? kDecRows / 2 : kDecRows;
+  const int out_w = swiglu ? p.N / 2 : p.N;
+  const int64_t chunks = (out_w + rows - 1) / rows;
+  dim3 grid((uint32_t)(chunks * p.max_blocks));
+  if (wdt == W_E2M1) launch_decode_wdt<W_E2M1>(p, swiglu, bias, grid, stream);
+  else if (wdt == W_E4M3) launch_decode_wdt<W_E4M3>(p, swiglu, bias, grid, stream);
+  else launch_decode_wdt<W_BF16>(p, swiglu, bias, grid, stream);
+  return hipGetLastError();
+}
+
+}  // namespace moe

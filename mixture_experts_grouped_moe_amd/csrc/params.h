@@ -10,6 +10,7 @@ namespace moe {
 struct GemmParams {
   const uint16_t* a;   // bf16 activation rows
   int64_t a_ld;        // elements
+  int64_t a_rows;      // rows of A that slots can address: ceil(S / a_row_div)
   int32_t a_row_div;   // slot s reads row s / a_row_div
   const uint8_t* w;    // weight codes
   int64_t w_stride_e;  // bytes
@@ -44,8 +45,8 @@ struct WgradParams {
 
 hipError_t launch_align(const int32_t* ids, int32_t S, int32_t E, int32_t B, int32_t* sorted_ids,
                         int32_t* expert_ids, int32_t* post_pad, int32_t max_blocks, hipStream_t stream);
-hipError_t launch_grouped_gemm(const GemmParams& p, int wdt, bool swiglu, bool bias, bool decode,
-                               hipStream_t stream);
+hipError_t launch_gemm_large(const GemmParams& p, int wdt, bool swiglu, bool bias, hipStream_t stream);
+hipError_t launch_gemm_decode(const GemmParams& p, int wdt, bool swiglu, bool bias, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* c, int64_t c_ld, const float* w, int64_t T, int32_t top_k,
                           int64_t N, uint16_t* y, int64_t y_ld, hipStream_t stream);
 hipError_t launch_wgrad(const WgradParams& p, hipStream_t stream);
