@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode", choices=["decode", "w4a16", "mxfp8", "wgrad"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "w4a16", "mxfp8", "wgrad", "copy"])
     ap.add_argument("--variants", type=int, default=4, help="routing variants cycled across steps")
     ap.add_argument("--launch-reps", type=int, default=10,
                     help="back-to-back launches per event pair when timing the dominant kernel")
@@ -396,12 +396,56 @@ class Wgrad(Workload):
         return items, run, "TFLOP/s"
 
 
-WORKLOADS = {"decode": Decode, "w4a16": W4A16, "mxfp8": MXFP8, "wgrad": Wgrad}
+class Copy(Workload):
+    """A plain device-to-device copy of a known size (1 GiB): the reference
+    kernel against which the HBM byte counters are calibrated."""
+    name = "copy"
+    dominant = "__amd_rocclr_copyBuffer"
+    bound = "hbm"
+    cpu_sample_desc = "numpy copy of 64 MiB"
+
+    def __init__(self, torch, dev, variants):
+        self.torch = torch
+        self.n = 1 << 30
+        self.src = torch.ones(self.n, dtype=torch.uint8, device=dev)
+        self.dst = torch.empty(self.n, dtype=torch.uint8, device=dev)
+
+    def step_flops(self, v):
+        return 0
+
+    def step_bytes(self, v):
+        return 2 * self.n
+
+    def _copy(self):
+        self.dst.copy_(self.src)
+
+    def step(self, v):
+        self._copy()
+
+    def dominant_launches(self, v):
+        return [(self._copy, 2 * self.n)]
+
+    def extra(self, per_call_us):
+        return {"bytes_copied": self.n}
+
+    def cpu_sample(self):
+        import numpy as np
+        a = np.ones(1 << 26, dtype=np.uint8)
+        b = np.empty_like(a)
+
+        def run(_):
+            np.copyto(b, a)
+            return 2 * a.size
+        return [0], run, "GB/s"
+
+
+WORKLOADS = {"decode": Decode, "w4a16": W4A16, "mxfp8": MXFP8, "wgrad": Wgrad, "copy": Copy}
 CONFIG_NAMES = {
     "decode": "decode bf16 MoE, E=128 N=1856 K=2048 top-6, M in {1,7,14,21,28}",
     "w4a16": "W4A16 MXFP4 MoE layer (gpt-oss-shaped), E=128 top-4 H=2880, gate+up 5760 -> SwiGLU -> down 2880, T~U[6554,8192] bucketed",
     "mxfp8": "MXFP8 grouped GEMM, E=256 top-8 K=7168 N=4096 T=4096, Zipf(1.1) routing with 16 empty experts",
     "wgrad": "moe_wgrad, E=256 top-8 T=16384, x [T,7168], grad [8T,2048], fp32 dW [256,2048,7168]",
+    "copy": "device-to-device copy of 1 GiB (counter calibration)",
 }
 
 
@@ -509,12 +553,12 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": wl.dominant, "avg_launch_us": round(avg_launch_us, 3)}
 
-    if args.workload == "decode":
+    if args.workload in ("decode", "copy"):
         value = step_bytes / dt / 1e9
         unit_v = "GB/s"
         extra = wl.extra([sum(v) / len(v) for _, v in sorted(per_call.items())])
         extra["hbm_frac_step"] = round(value / PEAK_HBM_GBS, 4)
-        dtype = "bf16"
+        dtype = "bf16" if args.workload == "decode" else "u8"
     else:
         value = step_flops / dt / 1e12
         unit_v = "TFLOP/s"

@@ -38,12 +38,17 @@ __global__ __launch_bounds__(kThreadsDec) void moe_decode_kernel(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
-  if (tid < kDecBM) s_slot[tid] = p.sorted[(int64_t)b * kDecBM + tid];
+  // the block's real slots, compacted: s_slot[0 .. nv) (PAD positions dropped)
+  __shared__ int32_t s_nv;
+  if (tid < kWave) {
+    const int32_t s = tid < kDecBM ? p.sorted[(int64_t)b * kDecBM + tid] : p.S;
+    const bool real = tid < kDecBM && s < p.S;
+    const uint64_t m = __ballot(real);
+    if (real) s_slot[__popcll(m & ((1ull << tid) - 1ull))] = s;
+    if (tid == 0) s_nv = __popcll(m);
+  }
   __syncthreads();
-  // which of the block's positions hold a real slot (PAD marks the rest)
-  uint32_t vmask = 0;
-#pragma unroll
-  for (int j = 0; j < kDecBM; ++j) vmask |= (s_slot[j] < p.S ? 1u : 0u) << j;
+  const int nv = s_nv;
 
   // this wave's weight rows (and output columns)
   int32_t wrow[kDecRowsPerWave], ocol[kDecRowsPerWave];
@@ -70,21 +75,15 @@ __global__ __launch_bounds__(kThreadsDec) void moe_decode_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < kDecBM; ++j) acc[r][j] = 0.0f;
 
+  // raw weight codes of one 8-element piece: 16 B (bf16), 8 B (E4M3), 4 B (E2M1)
+  constexpr int kWords = (WDT == W_BF16) ? 4 : (WDT == W_E4M3 ? 2 : 1);
   constexpr int kPer = kDecKC / 8 / kWave;  // 8-element pieces per lane per pass
   for (int kc = 0; kc < p.K; kc += kDecKC) {
-    __syncthreads();
-    // stage the real slots' activations: kDecBM rows x kDecKC (zeros for PAD)
-    for (int q = tid; q < kDecBM * (kDecKC / 8); q += kThreadsDec) {
-      const int j = q / (kDecKC / 8), c = q % (kDecKC / 8);
-      u32x4_t v = {0, 0, 0, 0};
-      if (((vmask >> j) & 1u) && kc + c * 8 < p.K)
-        v = *reinterpret_cast<const u32x4_t*>(p.a + (int64_t)(s_slot[j] / p.a_row_div) * p.a_ld + kc + c * 8);
-      *reinterpret_cast<u32x4_t*>(&xs[j][c * 8]) = v;
-    }
-    __syncthreads();
-
-    // weight pieces: [row][i] holds elements kc + 8 * (lane + 64 i) .. +8
-    bf16x8_t wv[kDecRowsPerWave][kPer];
+    // 1. this wave's weight pieces for the pass ([row][i] holds elements
+    //    kc + 8 * (lane + 64 i) .. +8): issued first, so their latency
+    //    overlaps the activation staging below
+    uint32_t wraw[kDecRowsPerWave][kPer][kWords];
+    uint32_t sraw[kDecRowsPerWave][kPer];
 #pragma unroll
     for (int r = 0; r < kDecRowsPerWave; ++r) {
 #pragma unroll
@@ -93,27 +92,47 @@ __global__ __launch_bounds__(kThreadsDec) void moe_decode_kernel(GemmParams p) {
         const bool ok = wrow[r] >= 0 && k < p.K;
         const uint8_t* rowp = w_base + (int64_t)(ok ? wrow[r] : 0) * p.w_ld;
         if constexpr (WDT == W_BF16) {
-          u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(rowp + (int64_t)k * 2) : u32x4_t{0, 0, 0, 0};
-          __builtin_memcpy(&wv[r][i], &v, 16);
+          const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(rowp + (int64_t)k * 2) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) wraw[r][i][q] = v[q];
+        } else if constexpr (WDT == W_E4M3) {
+          const u32x2_t v = ok ? *reinterpret_cast<const u32x2_t*>(rowp + k) : u32x2_t{0, 0};
+          wraw[r][i][0] = v[0];
+          wraw[r][i][1] = v[1];
         } else {
-          const uint8_t sb = ok ? ws_base[(int64_t)wrow[r] * p.ws_ld + k / 32] : 127;
-          const float sc = e8m0_as_scale(sb);
-          if constexpr (WDT == W_E4M3) {
-            u32x2_t v = ok ? *reinterpret_cast<const u32x2_t*>(rowp + k) : u32x2_t{0, 0};
-            wv[r][i] = dequant_e4m3x8(v[0], v[1], sc);
-          } else {
-            uint32_t v = ok ? *reinterpret_cast<const uint32_t*>(rowp + k / 2) : 0u;
-            wv[r][i] = dequant_e2m1x8(v, sc);
-          }
+          wraw[r][i][0] = ok ? *reinterpret_cast<const uint32_t*>(rowp + k / 2) : 0u;
         }
+        if constexpr (WDT != W_BF16) sraw[r][i] = ok ? ws_base[(int64_t)wrow[r] * p.ws_ld + k / 32] : 127u;
       }
     }
+    // 2. stage the real slots' activations for this pass
+    __syncthreads();
+    for (int q = tid; q < nv * (kDecKC / 8); q += kThreadsDec) {
+      const int j = q / (kDecKC / 8), c = q % (kDecKC / 8);
+      u32x4_t v = {0, 0, 0, 0};
+      if (kc + c * 8 < p.K)
+        v = *reinterpret_cast<const u32x4_t*>(p.a + (int64_t)(s_slot[j] / p.a_row_div) * p.a_ld + kc + c * 8);
+      *reinterpret_cast<u32x4_t*>(&xs[j][c * 8]) = v;
+    }
+    __syncthreads();
+    // 3. dequantise and accumulate one fp32 partial per (row, slot)
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int c = lane + kWave * i;
+      bf16x8_t wv[kDecRowsPerWave];
+#pragma unroll
+      for (int r = 0; r < kDecRowsPerWave; ++r) {
+        if constexpr (WDT == W_BF16) {
+          __builtin_memcpy(&wv[r], wraw[r][i], 16);
+        } else if constexpr (WDT == W_E4M3) {
+          wv[r] = dequant_e4m3x8(wraw[r][i][0], wraw[r][i][1], e8m0_as_scale(sraw[r][i]));
+        } else {
+          wv[r] = dequant_e2m1x8(wraw[r][i][0], e8m0_as_scale(sraw[r][i]));
+        }
+      }
 #pragma unroll
       for (int j = 0; j < kDecBM; ++j) {
-        if ((vmask >> j) & 1u) {
+        if (j < nv) {
           const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(&xs[j][c * 8]);
 #pragma unroll
           for (int r = 0; r < kDecRowsPerWave; ++r) {
@@ -122,7 +141,7 @@ __global__ __launch_bounds__(kThreadsDec) void moe_decode_kernel(GemmParams p) {
             for (int q = 0; q < 4; ++q) {
               bf16x2_t x2, w2;
               __builtin_memcpy(&x2, reinterpret_cast<const char*>(&xv) + 4 * q, 4);
-              __builtin_memcpy(&w2, reinterpret_cast<const char*>(&wv[r][i]) + 4 * q, 4);
+              __builtin_memcpy(&w2, reinterpret_cast<const char*>(&wv[r]) + 4 * q, 4);
               a = __builtin_amdgcn_fdot2_f32_bf16(x2, w2, a, false);
             }
             acc[r][j] = a;
@@ -137,7 +156,7 @@ __global__ __launch_bounds__(kThreadsDec) void moe_decode_kernel(GemmParams p) {
   for (int r = 0; r < kDecRowsPerWave; ++r)
 #pragma unroll
     for (int j = 0; j < kDecBM; ++j) {
-      if ((vmask >> j) & 1u) {
+      if (j < nv) {
         float v = acc[r][j];
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
@@ -145,7 +164,7 @@ __global__ __launch_bounds__(kThreadsDec) void moe_decode_kernel(GemmParams p) {
       }
     }
 
-  if (lane < kDecBM && ((vmask >> lane) & 1u)) {
+  if (lane < nv) {
     const int s = s_slot[lane];
     uint16_t* crow = p.c + (int64_t)s * p.c_ld;
     float bvals[kDecRowsPerWave];
