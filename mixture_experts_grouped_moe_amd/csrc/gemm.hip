@@ -31,8 +31,8 @@
 //    which gives exactly 2^(b-127) including the 0x00 and 0xFF codes.
 //  * v_mfma_f32_32x32x16_bf16, fp32 accumulators, one bf16 rounding at the
 //    store. Each wave: 64 rows x (32 * NT) columns.
-//  * LDS rows are made of 16-byte units XOR-swizzled by row so that the 32
-//    rows read by one instruction spread over all banks.
+//  * LDS rows are made of 16-byte units XOR-swizzled by row so that each
+//    16-lane group of a read instruction spreads over all 64 banks.
 //  * Workgroup ids are remapped so each XCD walks all routing blocks of one
 //    N tile in order: consecutive blocks of one expert reuse the weight tile
 //    from that XCD's L2.
@@ -107,9 +107,13 @@ __device__ __forceinline__ void wait_loads_barrier(uint32_t (&regs)[R]) {
 }
 
 // Physical 16-byte unit of logical unit u in LDS row `row` (rows of U units).
+// gfx950's LDS serves a ds_read_b128 16 lanes at a time from 64 banks
+// (256 bytes); the 16 rows one such group reads get distinct 16-byte slots
+// of that window (measured: conflict-free, where a 32-bank layout conflicts
+// two-way).
 template <int U>
 __device__ __forceinline__ int swz(int row, int u) {
-  return u ^ ((row / (8 / U)) % U);
+  return u ^ ((row / (16 / U)) % U);
 }
 
 // Global weight row of local tile row r, or -1 beyond N.
