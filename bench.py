@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--variants", type=int, default=4, help="routing variants cycled across steps")
     ap.add_argument("--launch-reps", type=int, default=10,
                     help="back-to-back launches per event pair when timing the dominant kernel")
+    ap.add_argument("--layout", default="auto", choices=["auto", "rows", "kblock"],
+                    help="expert weight layout: rows ([E][N][K]) or kblock (packed once by moe_pack_weights "
+                         "before timing); auto = kblock for the large-M workloads, rows for decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     return ap.parse_args()
@@ -102,6 +105,17 @@ class Workload:
         raise NotImplementedError
 
 
+LAYOUT = {"decode": "rows", "w4a16": "kblock", "mxfp8": "kblock"}  # resolved --layout per workload
+
+
+def _gemm_weights(moe, name, w, w_dtype, w_scale):
+    """The weights the timed GEMMs read: as drawn (rows layout) or packed once
+    into the K-block layout (a weight-load-time step, outside the timing)."""
+    if LAYOUT.get(name) == "kblock":
+        return moe.moe_pack_weights(w, w_dtype, w_scale=w_scale), None
+    return w, w_scale
+
+
 def _routing_buffers(torch, T, k, E, bm, dev):
     import mixture_experts_grouped_moe_amd as moe
     mb = moe.moe_align_max_blocks(T * k, E, bm)
@@ -123,6 +137,7 @@ class Decode(Workload):
         self.torch, self.moe = torch, moe
         self.E, self.N, self.K, self.k = 128, 1856, 2048, 6
         self.w = synth.bf16_normal((self.E, self.N, self.K), 0.02, 1002, "w", dev)
+        self.wg, _ = _gemm_weights(moe, self.name, self.w, "bf16", None)
         self.calls = []   # per variant: list of dicts per M
         self.bytes_gemm = []  # per variant: list of algorithmic GEMM bytes per M
         for v in range(variants):
@@ -159,7 +174,7 @@ class Decode(Workload):
     def _gemm(self, c):
         if "gemm_call" not in c:
             c["gemm_call"], _ = self.moe.moe_grouped_gemm_prepare(
-                c["x"], self.w, "bf16", c["routing"], c["M"], self.k, self.E, self.k, out=c["C"])
+                c["x"], self.wg, "bf16", c["routing"], c["M"], self.k, self.E, self.k, out=c["C"])
         return c["gemm_call"]()
 
     def step(self, v):
@@ -208,6 +223,8 @@ class W4A16(Workload):
         self.E, self.H, self.I, self.k = 128, 2880, 2880, 4
         d = synth.config3(8192, device=dev)
         self.d = d
+        self.w1, self.s1 = _gemm_weights(moe, self.name, d["w1"], "e2m1x2", d["s1"])
+        self.w2, self.s2 = _gemm_weights(moe, self.name, d["w2"], "e2m1x2", d["s2"])
         self.Ts = synth.draw_token_counts(variants, 6554, 8192, seed=1003)
         self.calls = []
         for T in self.Ts:
@@ -233,15 +250,15 @@ class W4A16(Workload):
 
     def _up(self, c):
         d = self.d
-        return self.moe.moe_grouped_gemm(c["x"], d["w1"], "e2m1x2", c["routing"], c["Tb"], self.k, self.E, self.k,
-                                         w_scale=d["s1"], epilogue="swiglu", out=c["h"])
+        return self.moe.moe_grouped_gemm(c["x"], self.w1, "e2m1x2", c["routing"], c["Tb"], self.k, self.E, self.k,
+                                         w_scale=self.s1, epilogue="swiglu", out=c["h"])
 
     def step(self, v):
         c, d, moe = self.calls[v], self.d, self.moe
         moe.moe_align(c["ids"], self.E, c["bm"], out=c["routing"])
         self._up(c)
-        moe.moe_grouped_gemm(c["h"], d["w2"], "e2m1x2", c["routing"], c["Tb"], self.k, self.E, 1,
-                             w_scale=d["s2"], out=c["c2"])
+        moe.moe_grouped_gemm(c["h"], self.w2, "e2m1x2", c["routing"], c["Tb"], self.k, self.E, 1,
+                             w_scale=self.s2, out=c["c2"])
         moe.moe_combine(c["c2"], c["tw"], self.k, num_tokens=c["T"], out=c["y"])
 
     def dominant_launches(self, v):
@@ -288,6 +305,7 @@ class MXFP8(Workload):
         self.torch, self.moe = torch, moe
         d = synth.config4(device=dev, bias=bias)
         self.d = d
+        self.wg, self.sg = _gemm_weights(moe, self.name, d["w"], "e4m3", d["w_scale"])
         self.E, self.N, self.K, self.k, self.T = 256, 4096, 7168, 8, 4096
         bm = moe.moe_gemm_block_m("e4m3", self.T)
         self.bm = bm
@@ -309,8 +327,8 @@ class MXFP8(Workload):
 
     def _gemm(self):
         d = self.d
-        return self.moe.moe_grouped_gemm(d["x"], d["w"], "e4m3", self.routing, self.T, self.k, self.E, self.k,
-                                         w_scale=d["w_scale"], bias=d["bias"], out=self.C)
+        return self.moe.moe_grouped_gemm(d["x"], self.wg, "e4m3", self.routing, self.T, self.k, self.E, self.k,
+                                         w_scale=self.sg, bias=d["bias"], out=self.C)
 
     def step(self, v):
         self.moe.moe_align(self.d["ids"], self.E, self.bm, out=self.routing)
@@ -486,6 +504,9 @@ def main():
     import mixture_experts_grouped_moe_amd as moe  # noqa: F401  (fails loudly if libmoe.so is missing)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.layout != "auto":
+        for name in LAYOUT:
+            LAYOUT[name] = args.layout
     wl = WORKLOADS[args.workload](torch, dev, args.variants)
     nv = len(getattr(wl, "calls", [None])) if args.workload in ("decode", "w4a16") else 1
     stream = torch.cuda.Stream()
@@ -576,7 +597,7 @@ def main():
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
             "config": {"workload": CONFIG_NAMES[args.workload], "routing_variants": nv,
-                       "parallelism": "single GPU"},
+                       "weight_layout": LAYOUT.get(args.workload, "n/a"), "parallelism": "single GPU"},
             "roofline": roofline, "cpu_baseline": cpu}
     line.update(extra)
     print(json.dumps(line), flush=True)

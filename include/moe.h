@@ -56,6 +56,27 @@ typedef enum {
   MOE_I32 = 6
 } moe_dtype;
 
+/* Weight layouts (a storage unit is an element, or a byte of two codes for
+ * MOE_E2M1X2; R = 64 elements = 64 units, 32 for MOE_E2M1X2).
+ *   MOE_LAYOUT_ROWS:   code (e, n, k) at unit e*w_stride_e + n*w_ld + k (k/2
+ *                      for E2M1X2); scale byte (e, n, k/32) at
+ *                      e*w_scale_stride_e + n*w_scale_ld + k/32. The layout
+ *                      the pages' kernels read.
+ *   MOE_LAYOUT_KBLOCK: 64-element K blocks outermost: code (e, n, k) at unit
+ *                      e*w_stride_e + (k/64)*w_ld + n*R + (k%64) (halved for
+ *                      E2M1X2), i.e. for every K block all N rows' 64 codes
+ *                      back to back; scale byte (e, n, k/32) at
+ *                      e*w_scale_stride_e + (k/64)*w_scale_ld + 2n + (k/32)%2.
+ *                      Made by moe_pack_weights. A K block's codes for a run
+ *                      of consecutive rows are one contiguous piece, so the
+ *                      large-M kernel's weight loads are whole cache lines.
+ *                      A library layout, not one from the pages; the values
+ *                      are the same, so every result is identical. */
+typedef enum {
+  MOE_LAYOUT_ROWS = 0,
+  MOE_LAYOUT_KBLOCK = 1
+} moe_layout;
+
 typedef enum {
   MOE_EPILOGUE_NONE = 0,
   /* h[:, j] = silu(pre[:, j]) * pre[:, N/2 + j], silu(z) = z / (1 + e^-z);
@@ -164,13 +185,15 @@ typedef struct {
   int64_t a_ld;           /* >= k */
 
   int32_t w_dtype;        /* MOE_BF16, MOE_E4M3 or MOE_E2M1X2 */
-  const void* w;          /* (device) [E][N][K] codes; strides in storage units
-                             (elements; bytes of two codes for MOE_E2M1X2) */
-  int64_t w_stride_e;     /* >= n * w_ld */
-  int64_t w_ld;           /* >= k (or k/2 for MOE_E2M1X2) */
-  const uint8_t* w_scale; /* (device) E8M0 [E][N][K/32]; NULL for MOE_BF16 */
-  int64_t w_scale_stride_e;
-  int64_t w_scale_ld;     /* >= k / 32 */
+  int32_t w_layout;       /* moe_layout of w and w_scale */
+  const void* w;          /* (device) codes of [E][N][K]; strides in storage
+                             units (elements; bytes of two codes for E2M1X2) */
+  int64_t w_stride_e;     /* ROWS: >= n * w_ld; KBLOCK: >= ceil(k/64) * w_ld */
+  int64_t w_ld;           /* ROWS: row stride >= k (k/2 for E2M1X2);
+                             KBLOCK: K-block stride >= n * R */
+  const uint8_t* w_scale; /* (device) E8M0 of [E][N][K/32]; NULL for MOE_BF16 */
+  int64_t w_scale_stride_e; /* ROWS: >= n * w_scale_ld; KBLOCK: >= ceil(k/64) * w_scale_ld */
+  int64_t w_scale_ld;     /* ROWS: >= k / 32; KBLOCK: K-block stride >= 2n */
 
   const void* bias;       /* (device) bf16 [E][N] or NULL */
   int64_t bias_stride_e;  /* in elements; any non-negative strides */
@@ -189,8 +212,34 @@ typedef struct {
 
 /* Requirements: k % 32 == 0 and k >= 32; n >= 1 (even with SwiGLU);
  * a_row_div in {1, top_k}; 16-byte aligned a and w rows (a_ld a multiple of
- * 8; w_ld a multiple of 16 bytes); c_ld >= the output width. No workspace. */
+ * 8; w_ld a multiple of 16 bytes); c_ld >= the output width; one expert's
+ * weights and scales each span less than 4 GB. No workspace. */
 moe_status moe_grouped_gemm(const moe_gemm_args* args, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Weight repacking (a one-time step at weight-load time, outside the
+ * method: it moves codes and scale bytes, computes nothing).
+ * Copies E experts' codes and scales from MOE_LAYOUT_ROWS (w, w_scale with
+ * the strides of moe_gemm_args) into MOE_LAYOUT_KBLOCK with dense strides:
+ *   w_out:       K-block stride n*R units, expert stride ceil(k/64)*n*R units
+ *   w_scale_out: K-block stride 2n bytes, expert stride ceil(k/64)*2n bytes
+ * (moe_packed_sizes returns both expert strides). When k % 64 == 32 the
+ * unused upper half of the last K block is written as zero codes and zero
+ * scale bytes; no kernel reads it. w_scale / w_scale_out are NULL for
+ * MOE_BF16. Input and output must not overlap. Requirements as for
+ * moe_grouped_gemm's weights (k % 32 == 0, 16-byte aligned rows). */
+moe_status moe_pack_weights(int32_t w_dtype, int32_t num_experts, int64_t n, int64_t k,
+                            const void* w, int64_t w_stride_e, int64_t w_ld,
+                            const uint8_t* w_scale, int64_t w_scale_stride_e,
+                            int64_t w_scale_ld, void* w_out, uint8_t* w_scale_out,
+                            moe_stream_t stream);
+
+/* Expert strides of moe_pack_weights' dense output: *w_units =
+ * ceil(k/64) * n * R storage units, *scale_bytes = ceil(k/64) * 2n (0 for
+ * MOE_BF16). Either pointer (host) may be NULL. Returns MOE_OK, or
+ * MOE_ERR_INVALID_ARGUMENT for a bad dtype or size. */
+moe_status moe_packed_sizes(int32_t w_dtype, int64_t n, int64_t k, int64_t* w_units,
+                            int64_t* scale_bytes);
 
 /* ------------------------------------------------------------------------
  * Top-k combine (the method's final step; [TRT] Description: the padded

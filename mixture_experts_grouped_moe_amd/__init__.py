@@ -19,6 +19,7 @@ __all__ = [
     "moe_bucket_round_up", "moe_bucket_enumerate", "moe_padding_supported",
     "moe_align_max_blocks", "moe_gemm_block_m", "moe_wgrad_block_m", "moe_decode_max_tokens",
     "moe_align", "moe_grouped_gemm", "moe_grouped_gemm_prepare", "moe_combine", "moe_wgrad",
+    "moe_pack_weights", "moe_packed_sizes", "PackedWeights", "MOE_LAYOUT_ROWS", "MOE_LAYOUT_KBLOCK",
     "moe_w4a16_layer",
     "LIB_PATH",
 ]
@@ -26,6 +27,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_BF16, MOE_FP32, MOE_E4M3, MOE_E2M1X2, MOE_E8M0, MOE_I32 = 1, 2, 3, 4, 5, 6
+MOE_LAYOUT_ROWS, MOE_LAYOUT_KBLOCK = 0, 1
 _W_DTYPES = {"bf16": MOE_BF16, "e4m3": MOE_E4M3, "e2m1x2": MOE_E2M1X2}
 _EPILOGUES = {"none": 0, "swiglu": 1}
 
@@ -45,7 +47,7 @@ class MoeGemmArgs(ctypes.Structure):
         ("n", ctypes.c_int64), ("k", ctypes.c_int64),
         ("a_dtype", ctypes.c_int32), ("a_row_div", ctypes.c_int32),
         ("a", ctypes.c_void_p), ("a_ld", ctypes.c_int64),
-        ("w_dtype", ctypes.c_int32), ("w", ctypes.c_void_p),
+        ("w_dtype", ctypes.c_int32), ("w_layout", ctypes.c_int32), ("w", ctypes.c_void_p),
         ("w_stride_e", ctypes.c_int64), ("w_ld", ctypes.c_int64),
         ("w_scale", ctypes.c_void_p), ("w_scale_stride_e", ctypes.c_int64), ("w_scale_ld", ctypes.c_int64),
         ("bias", ctypes.c_void_p), ("bias_stride_e", ctypes.c_int64), ("bias_stride_n", ctypes.c_int64),
@@ -60,7 +62,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first with "
-            "`python -m mixture_experts_grouped_moe_amd._build` (or __graft_entry__.build())")
+            "`python mixture_experts_grouped_moe_amd/_build.py` (or __graft_entry__.build())")
     L = ctypes.CDLL(LIB_PATH)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     sig = {
@@ -77,6 +79,8 @@ def _load():
         "moe_grouped_gemm": (i32, [ctypes.POINTER(MoeGemmArgs), vp]),
         "moe_combine": (i32, [vp, i64, vp, i64, i32, i64, vp, i64, vp]),
         "moe_wgrad": (i32, [vp, i64, vp, i64, vp, vp, vp, i64, i32, i32, i64, i64, i32, i64, vp, vp]),
+        "moe_pack_weights": (i32, [i32, i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp, vp]),
+        "moe_packed_sizes": (i32, [i32, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -158,7 +162,56 @@ def moe_decode_max_tokens():
     return int(lib.moe_decode_max_tokens())
 
 
+def moe_packed_sizes(w_dtype, n, k):
+    """Per-expert (storage units, scale bytes) of moe_pack_weights' output."""
+    wu, sb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib.moe_packed_sizes(int(_W_DTYPES[w_dtype]), int(n), int(k), ctypes.byref(wu), ctypes.byref(sb)))
+    return wu.value, sb.value
+
+
 # ---------------------------------------------------------------- device calls
+
+class PackedWeights:
+    """Expert weights in the K-block layout (MOE_LAYOUT_KBLOCK of moe.h).
+
+    codes: [E, ceil(K/64), N, R] (R = 64 elements, or 32 bytes of E2M1 pairs);
+    scales: uint8 [E, ceil(K/64), N, 2] or None for bf16. n and k are the
+    logical weight shape [E, N, K]. Accepted by moe_grouped_gemm in place of
+    a rows-layout weight tensor (then w_scale is not passed).
+    """
+
+    def __init__(self, codes, scales, w_dtype, n, k):
+        self.codes, self.scales, self.w_dtype, self.n, self.k = codes, scales, w_dtype, int(n), int(k)
+
+    @property
+    def num_experts(self):
+        return self.codes.shape[0]
+
+
+def moe_pack_weights(w, w_dtype, w_scale=None, stream=None):
+    """Repack rows-layout weights [E, N, K] (and E8M0 scales [E, N, K/32])
+    into the K-block layout; returns a PackedWeights. A copy, run once when
+    the weights are loaded."""
+    wd = _W_DTYPES[w_dtype]
+    _need(w, "w", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 3)
+    E, N = w.shape[0], w.shape[1]
+    K = w.shape[2] * (2 if w_dtype == "e2m1x2" else 1)
+    nblk = (K + 63) // 64
+    R = 32 if w_dtype == "e2m1x2" else 64
+    codes = torch.empty((E, nblk, N, R), dtype=w.dtype, device=w.device)
+    scales = None
+    if w_dtype != "bf16":
+        _need(w_scale, "w_scale", torch.uint8, 3)
+        if tuple(w_scale.shape) != (E, N, K // 32):
+            raise ValueError(f"w_scale must be [E, N, K/32] = {(E, N, K // 32)}")
+        scales = torch.empty((E, nblk, N, 2), dtype=torch.uint8, device=w.device)
+    _check(lib.moe_pack_weights(wd, E, N, K, _ptr(w), w.stride(0), w.stride(1),
+                                _ptr(w_scale), w_scale.stride(0) if scales is not None else 0,
+                                w_scale.stride(1) if scales is not None else 0,
+                                _ptr(codes), _ptr(scales), _stream(stream)))
+    return PackedWeights(codes, scales, w_dtype, N, K)
+
+
 
 def moe_align(topk_ids, num_experts, block_m, num_tokens=None, out=None, stream=None):
     """Sort slots by expert and pad each expert to block_m.
@@ -217,18 +270,29 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     """
     wd = _W_DTYPES[w_dtype]
     _need(a, "a", torch.bfloat16, 2)
-    _need(w, "w", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 3)
-    E, N = w.shape[0], w.shape[1]
     K = a.shape[1]
     S = int(num_tokens) * int(top_k)
-    if w.shape[2] * (2 if w_dtype == "e2m1x2" else 1) != K:
-        raise ValueError("w's K does not match a's")
+    packed = isinstance(w, PackedWeights)
+    if packed:
+        if w.w_dtype != w_dtype or w.k != K:
+            raise ValueError("packed weights do not match w_dtype / a's K")
+        if w_scale is not None:
+            raise ValueError("packed weights carry their own scales")
+        E, N = w.num_experts, w.n
+        w_t, w_scale = w.codes, w.scales
+        _need(w_t, "w.codes", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 4)
+    else:
+        w_t = w
+        _need(w_t, "w", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 3)
+        E, N = w_t.shape[0], w_t.shape[1]
+        if w_t.shape[2] * (2 if w_dtype == "e2m1x2" else 1) != K:
+            raise ValueError("w's K does not match a's")
+        if w_dtype != "bf16":
+            _need(w_scale, "w_scale", torch.uint8, 3)
+            if tuple(w_scale.shape) != (E, N, K // 32):
+                raise ValueError(f"w_scale must be [E, N, K/32] = {(E, N, K // 32)}")
     if a.shape[0] * int(a_row_div) < S:
         raise ValueError("a has too few rows for num_tokens * top_k slots")
-    if w_dtype != "bf16":
-        _need(w_scale, "w_scale", torch.uint8, 3)
-        if tuple(w_scale.shape) != (E, N, K // 32):
-            raise ValueError(f"w_scale must be [E, N, K/32] = {(E, N, K // 32)}")
     if bias is not None:
         if bias.dtype != torch.bfloat16 or not bias.is_cuda or tuple(bias.shape) != (E, N):
             raise TypeError("bias must be a bf16 [E, N] device tensor")
@@ -247,7 +311,8 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     g.num_tokens, g.top_k, g.num_experts = int(num_tokens), int(top_k), int(num_experts)
     g.n, g.k = N, K
     g.a_dtype, g.a_row_div, g.a, g.a_ld = MOE_BF16, int(a_row_div), a.data_ptr(), a.stride(0)
-    g.w_dtype, g.w, g.w_stride_e, g.w_ld = wd, w.data_ptr(), w.stride(0), w.stride(1)
+    g.w_dtype, g.w, g.w_stride_e, g.w_ld = wd, w_t.data_ptr(), w_t.stride(0), w_t.stride(1)
+    g.w_layout = MOE_LAYOUT_KBLOCK if packed else MOE_LAYOUT_ROWS
     if w_scale is not None:
         g.w_scale, g.w_scale_stride_e, g.w_scale_ld = w_scale.data_ptr(), w_scale.stride(0), w_scale.stride(1)
     if bias is not None:
@@ -258,7 +323,7 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     g.block_m, g.max_blocks = int(bm), expert_ids.numel()
     st = _stream(stream)
     ref = ctypes.byref(g)
-    keep = (a, w, w_scale, bias, out, routing)  # the call holds its tensors alive
+    keep = (a, w_t, w_scale, bias, out, routing)  # the call holds its tensors alive
 
     def call():
         _check(lib.moe_grouped_gemm(ref, st))
@@ -313,7 +378,8 @@ _warned_padding = False
 def moe_w4a16_layer(x, topk_ids, topk_w, w1, s1, w2, s2, b1=None, b2=None, num_tokens=None,
                     pad_token_dim=False, stream=None):
     """The W4A16 MXFP4 expert layer: align -> gate+up GEMM with SwiGLU ->
-    down GEMM -> top-k combine. Returns y bf16 [num_tokens, H].
+    down GEMM -> top-k combine. Returns y bf16 [num_tokens, H]. w1 / w2 are
+    rows-layout codes with scales s1 / s2, or PackedWeights (s1 / s2 None).
 
     With pad_token_dim, the token dimension is run at its bucket
     (moe_bucket_round_up): the caller's x / topk_ids / topk_w must hold at
@@ -336,7 +402,7 @@ def moe_w4a16_layer(x, topk_ids, topk_w, w1, s1, w2, s2, b1=None, b2=None, num_t
     if x.shape[0] < Tr or topk_ids.shape[0] < Tr:
         raise ValueError(f"pad_token_dim needs {Tr} rows in x and topk_ids (bucket of {T})")
     k = topk_ids.shape[1]
-    E = w1.shape[0]
+    E = w1.num_experts if isinstance(w1, PackedWeights) else w1.shape[0]
     bm = moe_gemm_block_m("e2m1x2", Tr)
     routing = moe_align(topk_ids, E, bm, num_tokens=Tr, stream=stream)
     h = moe_grouped_gemm(x, w1, "e2m1x2", routing, Tr, k, E, a_row_div=k, w_scale=s1, bias=b1,

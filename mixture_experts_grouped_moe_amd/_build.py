@@ -1,6 +1,8 @@
 """Build libmoe.so (the C-ABI library of HIP kernels for gfx950) in-tree.
 
-    python -m mixture_experts_grouped_moe_amd._build
+    python mixture_experts_grouped_moe_amd/_build.py
+
+(run as a script: importing the package loads the library this builds)
 
 compiles every source under csrc/ with hipcc for gfx950 and links
 mixture_experts_grouped_moe_amd/libmoe.so. Objects go to _build/ at the
@@ -28,7 +30,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["api.cpp", "align.hip", "gemm.hip", "decode.hip", "combine.hip", "wgrad.hip"]
+SOURCES = ["api.cpp", "align.hip", "gemm.hip", "decode.hip", "combine.hip", "wgrad.hip", "pack.hip"]
 
 
 def _hipcc():

@@ -172,15 +172,26 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "a_row_div must be 1 or top_k");
   if (a.a_ld < a.k || a.a_ld % 8 != 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "a_ld must be >= k and a multiple of 8");
-  const int64_t w_row_units = a.w_dtype == MOE_E2M1X2 ? a.k / 2 : a.k;
+  if (a.w_layout != MOE_LAYOUT_ROWS && a.w_layout != MOE_LAYOUT_KBLOCK)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown w_layout %d", a.w_layout);
+  const bool kblock = a.w_layout == MOE_LAYOUT_KBLOCK;
   const int64_t w_elem_bytes = a.w_dtype == MOE_BF16 ? 2 : 1;
-  if (a.w_ld < w_row_units || (a.w_ld * w_elem_bytes) % 16 != 0)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a row and be a multiple of 16 bytes");
-  if (a.w_stride_e < a.n * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < n * w_ld");
+  const int64_t blk_units = a.w_dtype == MOE_E2M1X2 ? 32 : 64;  // units per row per 64-element K block
+  const int64_t nblk = (a.k + 63) / 64;
+  if ((a.w_ld * w_elem_bytes) % 16 != 0 || (a.w_stride_e * w_elem_bytes) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld and w_stride_e must be multiples of 16 bytes");
+  if (!kblock) {
+    if (a.w_ld < a.k * blk_units / 64) return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a row");
+    if (a.w_stride_e < a.n * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < n * w_ld");
+  } else {
+    if (a.w_ld < a.n * blk_units) return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a K block of n rows");
+    if (a.w_stride_e < nblk * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < ceil(k/64) * w_ld");
+  }
   if (a.w_dtype != MOE_BF16) {
     if (a.w_scale == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale is null");
-    if (a.w_scale_ld < a.k / 32 || a.w_scale_stride_e < a.n * a.w_scale_ld)
-      return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale strides too small");
+    const bool ok = !kblock ? (a.w_scale_ld >= a.k / 32 && a.w_scale_stride_e >= a.n * a.w_scale_ld)
+                            : (a.w_scale_ld >= 2 * a.n && a.w_scale_stride_e >= nblk * a.w_scale_ld);
+    if (!ok) return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale strides too small");
   }
   if (a.bias != nullptr && (a.bias_stride_e < 0 || a.bias_stride_n < 0))
     return fail(MOE_ERR_INVALID_ARGUMENT, "negative bias stride");
@@ -202,8 +213,9 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   // scales through 32-bit buffer offsets
   const int64_t a_rows = S > 0 ? (S - 1) / a.a_row_div + 1 : 0;
   constexpr int64_t kBufMax = (int64_t)0xFFFFFFF0;
-  if (a_rows * a.a_ld * 2 >= kBufMax || a.n * a.w_ld * w_elem_bytes >= kBufMax ||
-      (a.w_dtype != MOE_BF16 && a.n * a.w_scale_ld >= kBufMax))
+  const int64_t w_span = (kblock ? nblk : a.n) * a.w_ld * w_elem_bytes;
+  const int64_t ws_span = a.w_dtype == MOE_BF16 ? 0 : (kblock ? nblk : a.n) * a.w_scale_ld;
+  if (a_rows * a.a_ld * 2 >= kBufMax || w_span >= kBufMax || ws_span >= kBufMax)
     return fail(MOE_ERR_UNSUPPORTED, "A, one expert's weights or its scales exceed 4 GB");
   moe_status st = check_device();
   if (st != MOE_OK) return st;
@@ -218,10 +230,14 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   p.a_row_div = a.a_row_div;
   p.w = static_cast<const uint8_t*>(a.w);
   p.w_stride_e = a.w_stride_e * w_elem_bytes;
-  p.w_ld = a.w_ld * w_elem_bytes;
+  p.w_row = kblock ? blk_units * w_elem_bytes : a.w_ld * w_elem_bytes;
+  p.w_blk = kblock ? a.w_ld * w_elem_bytes : blk_units * w_elem_bytes;
+  p.w_span = w_span;
   p.ws = a.w_scale;
   p.ws_stride_e = a.w_scale_stride_e;
-  p.ws_ld = a.w_scale_ld;
+  p.ws_row = kblock ? 2 : a.w_scale_ld;
+  p.ws_blk = kblock ? a.w_scale_ld : 2;
+  p.ws_span = ws_span;
   p.bias = static_cast<const uint16_t*>(a.bias);
   p.bias_se = a.bias_stride_e;
   p.bias_sn = a.bias_stride_n;
@@ -238,6 +254,50 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   return hip_status(decode ? moe::launch_gemm_decode(p, a.w_dtype, swiglu, bias, (hipStream_t)stream)
                            : moe::launch_gemm_large(p, a.w_dtype, swiglu, bias, (hipStream_t)stream),
                     "moe_grouped_gemm launch");
+}
+
+moe_status moe_packed_sizes(int32_t w_dtype, int64_t n, int64_t k, int64_t* w_units, int64_t* scale_bytes) {
+  if (!valid_w_dtype(w_dtype)) return fail(MOE_ERR_INVALID_ARGUMENT, "w_dtype %d not supported", w_dtype);
+  if (n < 1 || n >= INT32_MAX || k < 32 || k % 32 != 0 || k >= INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "need n >= 1 and k a positive multiple of 32");
+  const int64_t nblk = (k + 63) / 64;
+  if (w_units) *w_units = nblk * n * (w_dtype == MOE_E2M1X2 ? 32 : 64);
+  if (scale_bytes) *scale_bytes = w_dtype == MOE_BF16 ? 0 : nblk * 2 * n;
+  return ok();
+}
+
+moe_status moe_pack_weights(int32_t w_dtype, int32_t num_experts, int64_t n, int64_t k, const void* w,
+                            int64_t w_stride_e, int64_t w_ld, const uint8_t* w_scale, int64_t w_scale_stride_e,
+                            int64_t w_scale_ld, void* w_out, uint8_t* w_scale_out, moe_stream_t stream) {
+  int64_t out_units = 0, out_scale = 0;
+  moe_status st = moe_packed_sizes(w_dtype, n, k, &out_units, &out_scale);
+  if (st != MOE_OK) return st;
+  if (num_experts < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_experts < 0");
+  const int64_t eb = w_dtype == MOE_BF16 ? 2 : 1;
+  const int64_t row_units = w_dtype == MOE_E2M1X2 ? k / 2 : k;
+  if (w_ld < row_units || w_stride_e < n * w_ld || (w_ld * eb) % 16 != 0 || (w_stride_e * eb) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w strides must cover the rows and be multiples of 16 bytes");
+  if (w_dtype != MOE_BF16) {
+    if (w_scale == nullptr || w_scale_out == nullptr)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "scales are required for block-scaled weights");
+    if (w_scale_ld < k / 32 || w_scale_stride_e < n * w_scale_ld)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale strides too small");
+  }
+  if (num_experts == 0) return ok();
+  if (w == nullptr || w_out == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (((uintptr_t)w | (uintptr_t)w_out) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w and w_out must be 16-byte aligned");
+  const uint8_t* wi = static_cast<const uint8_t*>(w);
+  const uint8_t* wo = static_cast<const uint8_t*>(w_out);
+  const int64_t in_bytes = ((int64_t)num_experts - 1) * w_stride_e * eb + n * w_ld * eb;
+  const int64_t out_bytes = (int64_t)num_experts * out_units * eb;
+  if (wi < wo + out_bytes && wo < wi + in_bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "w and w_out overlap");
+  st = check_device();
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_pack(wi, w_stride_e * eb, w_ld * eb, w_scale, w_scale_stride_e, w_scale_ld,
+                                     num_experts, (int32_t)n, (int32_t)k, (int32_t)((w_dtype == MOE_E2M1X2 ? 32 : 64) * eb),
+                                     static_cast<uint8_t*>(w_out), w_scale_out, (hipStream_t)stream),
+                    "moe_pack_weights launch");
 }
 
 moe_status moe_combine(const void* c, int64_t c_ld, const float* topk_w, int64_t num_tokens, int32_t top_k,

@@ -90,19 +90,21 @@ __global__ __launch_bounds__(kThreadsDec) void moe_decode_kernel(GemmParams p) {
       for (int i = 0; i < kPer; ++i) {
         const int k = kc + 8 * (lane + kWave * i);
         const bool ok = wrow[r] >= 0 && k < p.K;
-        const uint8_t* rowp = w_base + (int64_t)(ok ? wrow[r] : 0) * p.w_ld;
+        // codes of row wrow[r], K block k / 64, element k % 64
+        const int64_t wb = (int64_t)(ok ? wrow[r] : 0) * p.w_row + (int64_t)(k / 64) * p.w_blk;
         if constexpr (WDT == W_BF16) {
-          const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(rowp + (int64_t)k * 2) : u32x4_t{0, 0, 0, 0};
+          const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(w_base + wb + (k % 64) * 2) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
           for (int q = 0; q < 4; ++q) wraw[r][i][q] = v[q];
         } else if constexpr (WDT == W_E4M3) {
-          const u32x2_t v = ok ? *reinterpret_cast<const u32x2_t*>(rowp + k) : u32x2_t{0, 0};
+          const u32x2_t v = ok ? *reinterpret_cast<const u32x2_t*>(w_base + wb + k % 64) : u32x2_t{0, 0};
           wraw[r][i][0] = v[0];
           wraw[r][i][1] = v[1];
         } else {
-          wraw[r][i][0] = ok ? *reinterpret_cast<const uint32_t*>(rowp + k / 2) : 0u;
+          wraw[r][i][0] = ok ? *reinterpret_cast<const uint32_t*>(w_base + wb + (k % 64) / 2) : 0u;
         }
-        if constexpr (WDT != W_BF16) sraw[r][i] = ok ? ws_base[(int64_t)wrow[r] * p.ws_ld + k / 32] : 127u;
+        if constexpr (WDT != W_BF16)
+          sraw[r][i] = ok ? ws_base[(int64_t)wrow[r] * p.ws_row + (int64_t)(k / 64) * p.ws_blk + (k % 64) / 32] : 127u;
       }
     }
     // 2. stage the real slots' activations for this pass

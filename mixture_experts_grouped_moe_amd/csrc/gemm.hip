@@ -177,11 +177,11 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmParams p) {
       (void*)p.a, 0, (int)(uint32_t)(p.a_rows * p.a_ld * 2), 0x00020000);
   const uint8_t* w_base = p.w + (int64_t)e * p.w_stride_e;
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)w_base, 0, (int)(uint32_t)((int64_t)p.N * p.w_ld), 0x00020000);
+      (void*)w_base, 0, (int)(uint32_t)p.w_span, 0x00020000);
   __amdgpu_buffer_rsrc_t s_rsrc = w_rsrc;
   if constexpr (WDT != W_BF16)
     s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.ws + (int64_t)e * p.ws_stride_e), 0,
-                                               (int)(uint32_t)((int64_t)p.N * p.ws_ld), 0x00020000);
+                                               (int)(uint32_t)p.ws_span, 0x00020000);
 
   // ---- per-lane load descriptors: each load instruction of a wave fills one
   //      1 KB block of the stage, 16 bytes per lane in lane order
@@ -205,15 +205,19 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmParams p) {
     const int u = swz<UW>(row, pu);
     const int32_t wr = tile_w_row<NT, SWIGLU>(row, tile_n, p.N);
     w_k[i] = u * KPU;
-    w_off[i] = wr >= 0 ? (uint32_t)((int64_t)wr * p.w_ld + u * 16) : kOOB;
+    w_off[i] = wr >= 0 ? (uint32_t)((int64_t)wr * p.w_row + u * 16) : kOOB;
   }
   int32_t my_wrow[NT];
   uint32_t s_off[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     my_wrow[nt] = tile_w_row<NT, SWIGLU>(wave * WN + nt * 32 + l32, tile_n, p.N);
-    s_off[nt] = my_wrow[nt] >= 0 ? (uint32_t)((int64_t)my_wrow[nt] * p.ws_ld + h) : kOOB;
+    s_off[nt] = my_wrow[nt] >= 0 ? (uint32_t)((int64_t)my_wrow[nt] * p.ws_row + h) : kOOB;
   }
+  const uint32_t w_blk = (uint32_t)p.w_blk, ws_blk = (uint32_t)p.ws_blk;
+  // a wave whose columns all lie past N (in the last N tile) computes nothing;
+  // it still loads its share of the activation tile and joins every barrier
+  const bool wave_live = tile_w_row<NT, SWIGLU>(wave * WN, tile_n, p.N) >= 0;
 
   const int nsteps = (p.K + kBK - 1) / kBK;
   const int nsteps_pad = ((nsteps + kStages - 1) / kStages) * kStages;
@@ -238,14 +242,14 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmParams p) {
     }
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i) {
-      const uint32_t off = (live && k0 + w_k[i] < p.K && w_off[i] != kOOB) ? w_off[i] + step * RB : kOOB;
+      const uint32_t off = (live && k0 + w_k[i] < p.K && w_off[i] != kOOB) ? w_off[i] + step * w_blk : kOOB;
       dma16(w_rsrc, off, base + A_BYTES + (wave * W_LOADS + i) * 1024);
     }
     if constexpr (WDT != W_BF16) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const bool ok = live && s_off[nt] != kOOB && k0 + 32 * h < p.K;
-        sc[ST][nt] = load_byte(s_rsrc, ok ? s_off[nt] + 2 * step : kOOB);
+        sc[ST][nt] = load_byte(s_rsrc, ok ? s_off[nt] + step * ws_blk : kOOB);
       }
     }
   };
@@ -316,13 +320,13 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmParams p) {
   for (int step = 0; step < nsteps_pad; step += kStages) {
     wait_loads_barrier<LOADS>(sc[0]);
     issue(step + 2, S2{});
-    compute(S0{});
+    if (wave_live) compute(S0{});
     wait_loads_barrier<LOADS>(sc[1]);
     issue(step + 3, S0{});
-    compute(S1{});
+    if (wave_live) compute(S1{});
     wait_loads_barrier<LOADS>(sc[2]);
     issue(step + 4, S1{});
-    compute(S2{});
+    if (wave_live) compute(S2{});
   }
   // drain the look-ahead loads (all of them read as zeros past the last step)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

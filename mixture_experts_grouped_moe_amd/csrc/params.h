@@ -12,12 +12,18 @@ struct GemmParams {
   int64_t a_ld;        // elements
   int64_t a_rows;      // rows of A that slots can address: ceil(S / a_row_div)
   int32_t a_row_div;   // slot s reads row s / a_row_div
-  const uint8_t* w;    // weight codes
-  int64_t w_stride_e;  // bytes
-  int64_t w_ld;        // bytes
-  const uint8_t* ws;   // E8M0 scales
+  // Weight codes of (e, n, 64-element K block kb) start at byte
+  // e * w_stride_e + n * w_row + kb * w_blk, and the block's two scale bytes
+  // at e * ws_stride_e + n * ws_row + kb * ws_blk (+0, +1); both layouts of
+  // the API are these strides. w_span / ws_span bound one expert's bytes.
+  const uint8_t* w;
+  int64_t w_stride_e;
+  int64_t w_row, w_blk;
+  int64_t w_span;
+  const uint8_t* ws;
   int64_t ws_stride_e;
-  int64_t ws_ld;
+  int64_t ws_row, ws_blk;
+  int64_t ws_span;
   const uint16_t* bias;  // bf16 or null
   int64_t bias_se, bias_sn;
   uint16_t* c;         // bf16 output rows
@@ -50,6 +56,10 @@ hipError_t launch_gemm_decode(const GemmParams& p, int wdt, bool swiglu, bool bi
 hipError_t launch_combine(const uint16_t* c, int64_t c_ld, const float* w, int64_t T, int32_t top_k,
                           int64_t N, uint16_t* y, int64_t y_ld, hipStream_t stream);
 hipError_t launch_wgrad(const WgradParams& p, hipStream_t stream);
+// Copy one block of rows-layout codes/scales into the K-block layout.
+hipError_t launch_pack(const uint8_t* w, int64_t w_stride_e, int64_t w_ld, const uint8_t* ws,
+                       int64_t ws_stride_e, int64_t ws_ld, int32_t E, int32_t N, int32_t K, int32_t row_bytes,
+                       uint8_t* w_out, uint8_t* ws_out, hipStream_t stream);
 int gemm_block_m_large();
 int gemm_block_m_decode();
 int wgrad_block_m();

@@ -25,8 +25,9 @@ other than itself:
     gemm.combine            pinned  (identity at k = 1, hand-worked example, linearity)
     wgrad.wgrad             pinned  (constant input, linearity, zero/PAD slots, Fraction brute force)
     layer.w4a16_layer       pinned  (composition of pinned functions; padded == unpadded)
+    layout.pack_kblock      pinned  (per-element loop over the layout's index formula)
 """
 
-from . import formats, bucket, align, gemm, wgrad, layer  # noqa: F401
+from . import formats, bucket, align, gemm, wgrad, layer, layout  # noqa: F401
 
-__all__ = ["formats", "bucket", "align", "gemm", "wgrad", "layer"]
+__all__ = ["formats", "bucket", "align", "gemm", "wgrad", "layer", "layout"]

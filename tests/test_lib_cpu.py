@@ -39,7 +39,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol():
     syms = _declared_symbols()
-    assert len(syms) == 13, syms
+    assert len(syms) == 15, syms
     for name in syms:
         assert hasattr(L, name), name
 
@@ -164,6 +164,46 @@ def test_grouped_gemm_rejects(no_device):
     assert _gemm(w_dtype=moe.MOE_FP32) == UNSUPPORTED
     assert _gemm(num_tokens=-1) == INVALID
     assert _gemm(bias=0x100000, bias_stride_e=-1) == INVALID
+    assert _gemm(w_layout=2) == INVALID
+    assert _gemm(w_stride_e=256 * 64 + 8) == INVALID   # not a multiple of 16 bytes
+    # K-block layout: w_ld is the K-block stride (>= n * 32 bytes for E2M1 pairs)
+    assert _gemm(w_layout=moe.MOE_LAYOUT_KBLOCK) == INVALID                 # rows-layout strides
+    assert _gemm(w_layout=moe.MOE_LAYOUT_KBLOCK, w_ld=256 * 32, w_stride_e=2 * 256 * 32 - 16,
+                 w_scale_ld=512, w_scale_stride_e=1024) == INVALID            # expert stride too small
+    assert _gemm(w_layout=moe.MOE_LAYOUT_KBLOCK, w_ld=256 * 32, w_stride_e=2 * 256 * 32,
+                 w_scale_ld=500, w_scale_stride_e=1024) == INVALID            # scale block stride < 2n
+
+
+def test_packed_sizes():
+    assert moe.moe_packed_sizes("e2m1x2", 256, 128) == (2 * 256 * 32, 2 * 256 * 2)
+    assert moe.moe_packed_sizes("e4m3", 10, 96) == (2 * 10 * 64, 2 * 10 * 2)
+    assert moe.moe_packed_sizes("bf16", 3, 64) == (3 * 64, 0)
+    i64 = ctypes.c_int64
+    assert L.moe_packed_sizes(moe.MOE_E4M3, 10, 100, ctypes.byref(i64()), None) == INVALID
+    assert L.moe_packed_sizes(moe.MOE_FP32, 10, 64, None, None) == INVALID
+    assert L.moe_packed_sizes(moe.MOE_E4M3, 0, 64, None, None) == INVALID
+
+
+def test_pack_weights_rejects(no_device):
+    p = L.moe_pack_weights
+    E4 = moe.MOE_E4M3
+
+    def call(wd=E4, E=2, n=16, k=128, w=FAKE, se=16 * 128, ld=128, s=FAKE, sse=16 * 4, sld=4,
+             wo=ctypes.c_void_p(0x10000000), so=FAKE):
+        return p(wd, E, n, k, w, se, ld, s, sse, sld, wo, so, None)
+
+    assert call(k=100) == INVALID
+    assert call(E=-1) == INVALID
+    assert call(ld=64) == INVALID              # row shorter than k
+    assert call(se=100) == INVALID
+    assert call(ld=136) == INVALID             # not a multiple of 16 bytes
+    assert call(s=None) == INVALID
+    assert call(so=None) == INVALID
+    assert call(sld=2) == INVALID
+    assert call(w=None) == INVALID
+    assert call(wo=FAKE) == INVALID            # output overlaps the input
+    assert call(w=ctypes.c_void_p(0x100008)) == INVALID
+    assert call(wd=moe.MOE_FP32) == INVALID
 
 
 def test_combine_rejects(no_device):
