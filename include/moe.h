@@ -212,8 +212,9 @@ typedef struct {
 
 /* Requirements: k % 32 == 0 and k >= 32; n >= 1 (even with SwiGLU);
  * a_row_div in {1, top_k}; 16-byte aligned a and w rows (a_ld a multiple of
- * 8; w_ld a multiple of 16 bytes); c_ld >= the output width; one expert's
- * weights and scales each span less than 4 GB. No workspace. */
+ * 8; w_ld a multiple of 16 bytes); c_ld >= the output width; A, one
+ * expert's weights and one expert's scales each span less than 2 GB.
+ * No workspace. */
 moe_status moe_grouped_gemm(const moe_gemm_args* args, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------

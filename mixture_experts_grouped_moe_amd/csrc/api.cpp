@@ -212,11 +212,11 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   // the large-M kernel addresses A, one expert's weights and one expert's
   // scales through 32-bit buffer offsets
   const int64_t a_rows = S > 0 ? (S - 1) / a.a_row_div + 1 : 0;
-  constexpr int64_t kBufMax = (int64_t)0xFFFFFFF0;
+  constexpr int64_t kBufMax = (int64_t)0x80000000;
   const int64_t w_span = (kblock ? nblk : a.n) * a.w_ld * w_elem_bytes;
   const int64_t ws_span = a.w_dtype == MOE_BF16 ? 0 : (kblock ? nblk : a.n) * a.w_scale_ld;
   if (a_rows * a.a_ld * 2 >= kBufMax || w_span >= kBufMax || ws_span >= kBufMax)
-    return fail(MOE_ERR_UNSUPPORTED, "A, one expert's weights or its scales exceed 4 GB");
+    return fail(MOE_ERR_UNSUPPORTED, "A, one expert's weights or its scales span 2 GB or more");
   moe_status st = check_device();
   if (st != MOE_OK) return st;
   if (S == 0 || a.max_blocks == 0) return ok();

@@ -11,24 +11,26 @@
 // bucketing and warmup", Description.
 //
 // Design for gfx950:
-//  * One workgroup (4 waves side by side along N) per (routing block of 64
-//    rows, N tile). The routing block is the M tile, so padding waste is at
-//    most 63 rows per expert and no tile straddles two experts.
-//  * Each 64-wide K step moves 8 KB of activations and 16 KB of weight codes
+//  * One workgroup of 8 waves (2 along M x 4 along N) per (routing block of
+//    128 rows, N tile). The routing block is the M tile, so no tile straddles
+//    two experts, and each weight tile loaded serves 128 rows. A wave whose
+//    64 rows hold only padding skips its MFMAs (real rows come first in a
+//    block), so the padding computed is below 64 rows per expert.
+//  * Each 64-wide K step moves 16 KB of activations and 16 KB of weight codes
 //    (512 rows of E2M1, 256 of E4M3) or 32 KB of bf16 weights straight from
 //    global memory into LDS with buffer_load ... lds (no registers; rows past
 //    N, PAD rows and the K tail read as zeros through the buffer bounds),
-//    three stages deep, one barrier per step.
+//    four stages deep (three for bf16), one barrier per step.
 //  * K order inside a step: lane half h of a wave handles K elements
 //    [32h, 32h + 32) and MFMA substep ks takes [32h + 8ks, 32h + 8ks + 8).
 //    Any order common to both operands gives the same dot product; this one
 //    makes a lane's weight codes for the whole step one contiguous piece
 //    (16 B of E2M1, 32 B of E4M3) governed by a single E8M0 scale (block
 //    2*step + h), read with one or two ds_read_b128.
-//  * Codes are dequantised once per M block by the wave that uses them, with
-//    the gfx950 scaled conversions (v_cvt_scalef32_pk_bf16_{fp4,fp8}); the
-//    E8M0 byte rides in the exponent field of the conversion's scale operand,
-//    which gives exactly 2^(b-127) including the 0x00 and 0xFF codes.
+//  * Codes are dequantised by the waves that use them, with the gfx950 scaled
+//    conversions (v_cvt_scalef32_pk_bf16_{fp4,fp8}), one MFMA pair ahead of
+//    their use; the E8M0 byte rides in the exponent field of the conversion's
+//    scale operand, which gives exactly 2^(b-127) including 0x00 and 0xFF.
 //  * v_mfma_f32_32x32x16_bf16, fp32 accumulators, one bf16 rounding at the
 //    store. Each wave: 64 rows x (32 * NT) columns.
 //  * LDS rows are made of 16-byte units XOR-swizzled by row so that each
@@ -47,15 +49,20 @@
 namespace moe {
 
 template <int WDT> struct WTraits;
-template <> struct WTraits<W_E2M1> { static constexpr int kRowBytes = 32, kNT = 4; };
-template <> struct WTraits<W_E4M3> { static constexpr int kRowBytes = 64, kNT = 2; };
-template <> struct WTraits<W_BF16> { static constexpr int kRowBytes = 128, kNT = 2; };
+template <> struct WTraits<W_E2M1> { static constexpr int kRowBytes = 32, kNT = 4, kStages = 3; };
+template <> struct WTraits<W_E4M3> { static constexpr int kRowBytes = 64, kNT = 2, kStages = 3; };
+template <> struct WTraits<W_BF16> { static constexpr int kRowBytes = 128, kNT = 2, kStages = 3; };
 
-constexpr int kBM = 64;
+constexpr int kWavesM = 1;                        // waves along M
+constexpr int kWavesN = 4;                        // waves along N
+constexpr int kBM = 64 * kWavesM;                 // the routing block
 constexpr int kBK = 64;
-constexpr int kThreads = 256;
-constexpr int kStages = 3;
-constexpr uint32_t kOOB = 0xFFFFFFF0u;  // a buffer offset past every buffer here: reads as 0
+constexpr int kThreads = kWave * kWavesM * kWavesN;  // 256
+constexpr int kMinBlocks = 2;                     // workgroups per CU (LDS and registers allow two)
+// A per-lane buffer offset past every buffer the kernel reads (each is below
+// 2 GB, checked by the host API), also after a scalar step offset below 2 GB
+// is added: such a lane reads zeros.
+constexpr uint32_t kOOB = 0x80000000u;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
@@ -72,19 +79,21 @@ __device__ __forceinline__ T lds_read(const lds_u8_t* p) {
 // tell the LDS stages apart and would wait for every load in flight), and the
 // loop's explicit waits below are the whole synchronisation.
 //
-// 16 bytes per lane from buffer `rsrc` at byte offset `off` into LDS at
-// `lds_base` + 16 * lane (offsets past the buffer's size read as zeros).
-// `lds_base` is uniform across the wave (the compiler cannot prove it, hence
-// the readfirstlane).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-               :: "v"(off), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc) : "m0");
+// 16 bytes per lane from buffer `rsrc` at byte offset `voff` + `soff` into
+// LDS at `lds_base` + 16 * lane; a lane whose `voff` is kOOB reads zeros.
+// `soff` (the step's advance) and `lds_base` are wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+               :: "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "m0");
 }
 
-// One byte from buffer `rsrc` at `off` into a register (zero past the end).
-__device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+// One byte from buffer `rsrc` at `voff` + `soff` into a register (zero for a
+// lane whose `voff` is kOOB).
+__device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
   uint32_t v;
-  asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rsrc));
+  asm volatile("buffer_load_ubyte %0, %1, %2, %3 offen"
+               : "=v"(v) : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)));
   return v;
 }
 
@@ -116,11 +125,20 @@ __device__ __forceinline__ int swz(int row, int u) {
   return u ^ ((row / (16 / U)) % U);
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Global weight row of local tile row r, or -1 beyond N.
 template <int NT, bool SWIGLU>
 __device__ __forceinline__ int32_t tile_w_row(int r, int tile_n, int N) {
   constexpr int WN = NT * 32;
-  constexpr int BN = 4 * WN;
+  constexpr int BN = kWavesN * WN;
   if (!SWIGLU) {
     int n = tile_n * BN + r;
     return n < N ? n : -1;
@@ -135,29 +153,28 @@ __device__ __forceinline__ int32_t tile_w_row(int r, int tile_n, int N) {
 }
 
 template <int WDT, bool SWIGLU, bool BIAS>
-__global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmParams p) {
   using Tr = WTraits<WDT>;
-  constexpr int NT = Tr::kNT, RB = Tr::kRowBytes;
-  constexpr int WN = NT * 32, BN = 4 * WN;
-  constexpr int UW = RB / 16;                  // 16-byte units per weight row per step
-  constexpr int KPU = 64 / UW;                 // K elements per weight unit
-  constexpr int A_BYTES = kBM * 128;           // 8 KB
-  constexpr int W_BYTES = BN * RB;             // 16 KB (32 KB for bf16)
-  constexpr int A_LOADS = A_BYTES / 1024 / 4;  // one 1 KB wave-wide load per instruction, 4 waves
-  constexpr int W_LOADS = W_BYTES / 1024 / 4;
-  constexpr int S_LOADS = (WDT == W_BF16) ? 0 : NT;   // scale bytes per lane per step
+  constexpr int NT = Tr::kNT, RB = Tr::kRowBytes, STAGES = Tr::kStages;
+  constexpr int WN = NT * 32, BN = kWavesN * WN;
+  constexpr int NWAVES = kWavesM * kWavesN;
+  constexpr int UW = RB / 16;                       // 16-byte units per weight row per step
+  constexpr int KPU = 64 / UW;                      // K elements per weight unit
+  constexpr int A_BYTES = kBM * 128;                // 16 KB
+  constexpr int W_BYTES = BN * RB;                  // 16 KB (32 KB for bf16)
+  constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // one 1 KB wave-wide load per instruction
+  constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;
+  constexpr int S_LOADS = (WDT == W_BF16) ? 0 : NT;  // scale bytes per lane per step
   constexpr int SC_REGS = (WDT == W_BF16) ? 1 : NT;
   constexpr int LOADS = A_LOADS + W_LOADS + S_LOADS;  // loads per step per wave
+  constexpr int PIECES = (WDT == W_BF16) ? 4 : (WDT == W_E4M3 ? 2 : 1);  // 16-byte code pieces per lane-row
+  static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
+  static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
 
-  // one LDS array per stage: [A tile | weight tile]
+  // LDS: STAGES x [A tile | weight tile], then the block's slot list
   constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE_BYTES], st1[STAGE_BYTES], st2[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][STAGE_BYTES];
   __shared__ int32_t s_slot[kBM];
-  auto stage_a = [&](auto stage_tag) -> lds_u8_t* {
-    constexpr int ST = decltype(stage_tag)::value;
-    return (lds_u8_t*)(ST == 0 ? st0 : (ST == 1 ? st1 : st2));
-  };
-  auto stage_w = [&](auto stage_tag) -> lds_u8_t* { return stage_a(stage_tag) + A_BYTES; };
 
   const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
   const int b = L % p.max_blocks;
@@ -166,11 +183,22 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmParams p) {
   if (e < 0) return;  // sentinel block
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: keeps derived addresses scalar
+  const int wm = wave / kWavesN, wn = wave % kWavesN;              // this wave's rows / columns of the tile
   const int l32 = lane % 32, h = lane / 32;
 
   if (tid < kBM) s_slot[tid] = p.sorted[(int64_t)b * kBM + tid];
   __syncthreads();
+
+  // A wave computes nothing when its 64 rows hold only PAD positions (with
+  // moe_align's routing the real rows of a block come first, so this skips
+  // the padding past the last real row in 64-row steps) or when all its
+  // columns lie past N; it still loads its share of the tiles and joins
+  // every barrier.
+  const bool rows_live = __ballot(s_slot[wm * 64 + lane] < p.S) != 0;
+  const bool cols_live = tile_w_row<NT, SWIGLU>(wn * WN, tile_n, p.N) >= 0;
+  const bool wave_live = rows_live && cols_live;
 
   // ---- buffer resources (bounds give zeros for PAD rows, rows past N, K tail)
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -211,45 +239,52 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmParams p) {
   uint32_t s_off[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    my_wrow[nt] = tile_w_row<NT, SWIGLU>(wave * WN + nt * 32 + l32, tile_n, p.N);
+    my_wrow[nt] = tile_w_row<NT, SWIGLU>(wn * WN + nt * 32 + l32, tile_n, p.N);
     s_off[nt] = my_wrow[nt] >= 0 ? (uint32_t)((int64_t)my_wrow[nt] * p.ws_row + h) : kOOB;
   }
   const uint32_t w_blk = (uint32_t)p.w_blk, ws_blk = (uint32_t)p.ws_blk;
-  // a wave whose columns all lie past N (in the last N tile) computes nothing;
-  // it still loads its share of the activation tile and joins every barrier
-  const bool wave_live = tile_w_row<NT, SWIGLU>(wave * WN, tile_n, p.N) >= 0;
 
   const int nsteps = (p.K + kBK - 1) / kBK;
-  const int nsteps_pad = ((nsteps + kStages - 1) / kStages) * kStages;
+  const int nsteps_pad = ((nsteps + STAGES - 1) / STAGES) * STAGES;
 
-  // LDS byte addresses of the stages
-  const uint32_t st_addr[3] = {(uint32_t)(uintptr_t)(lds_u8_t*)st0, (uint32_t)(uintptr_t)(lds_u8_t*)st1,
-                               (uint32_t)(uintptr_t)(lds_u8_t*)st2};
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)&lds[0][0];
   // scale bytes of this lane's weight rows (one per N sub-tile), per stage
-  uint32_t sc[kStages][SC_REGS];
+  uint32_t sc[STAGES][SC_REGS];
 
-  // Issue the loads of K step `step` into stage ST (zeros past the last step,
-  // so every step issues the same number of loads).
+  // Issue the loads of K step `step` into stage ST. A step wholly inside K
+  // uses the per-lane offsets as they are, advanced by a scalar offset; the
+  // K tail and the look-ahead steps past the last one (every step issues the
+  // same number of loads) take the checked path, whose lanes past K read
+  // zeros.
   auto issue = [&](int step, auto stage_tag) {
     constexpr int ST = decltype(stage_tag)::value;
     const int k0 = step * kBK;
-    const bool live = step < nsteps;
-    const uint32_t base = st_addr[ST];
+    const uint32_t base = lds_base + ST * STAGE_BYTES;
+    if (k0 + kBK <= p.K) {
+      const uint32_t sa = (uint32_t)k0 * 2, sw = (uint32_t)step * w_blk, ss = (uint32_t)step * ws_blk;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const uint32_t off = (live && k0 + a_k[i] < p.K && a_off[i] != kOOB) ? a_off[i] + k0 * 2 : kOOB;
-      dma16(a_rsrc, off, base + (wave * A_LOADS + i) * 1024);
-    }
+      for (int i = 0; i < A_LOADS; ++i) dma16(a_rsrc, a_off[i], sa, base + (wave * A_LOADS + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < W_LOADS; ++i) {
-      const uint32_t off = (live && k0 + w_k[i] < p.K && w_off[i] != kOOB) ? w_off[i] + step * w_blk : kOOB;
-      dma16(w_rsrc, off, base + A_BYTES + (wave * W_LOADS + i) * 1024);
-    }
-    if constexpr (WDT != W_BF16) {
+      for (int i = 0; i < W_LOADS; ++i) dma16(w_rsrc, w_off[i], sw, base + A_BYTES + (wave * W_LOADS + i) * 1024);
+      if constexpr (WDT != W_BF16) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const bool ok = live && s_off[nt] != kOOB && k0 + 32 * h < p.K;
-        sc[ST][nt] = load_byte(s_rsrc, ok ? s_off[nt] + step * ws_blk : kOOB);
+        for (int nt = 0; nt < NT; ++nt) sc[ST][nt] = load_byte(s_rsrc, s_off[nt], ss);
+      }
+    } else {
+      const bool live = k0 < p.K;
+      const uint32_t sa = live ? (uint32_t)k0 * 2 : 0u, sw = live ? (uint32_t)step * w_blk : 0u,
+                     ss = live ? (uint32_t)step * ws_blk : 0u;
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i)
+        dma16(a_rsrc, (live && k0 + a_k[i] < p.K) ? a_off[i] : kOOB, sa, base + (wave * A_LOADS + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < W_LOADS; ++i)
+        dma16(w_rsrc, (live && k0 + w_k[i] < p.K) ? w_off[i] : kOOB, sw,
+              base + A_BYTES + (wave * W_LOADS + i) * 1024);
+      if constexpr (WDT != W_BF16) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          sc[ST][nt] = load_byte(s_rsrc, (live && k0 + 32 * h < p.K) ? s_off[nt] : kOOB, ss);
       }
     }
   };
@@ -262,71 +297,95 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
 
-  // Compute one K step from stage ST.
-  auto compute = [&](auto stage_tag) {
+  // Compute one K step from stage ST for the first NMT 32-row quarters of
+  // this wave's rows (all of them: NMT = 2).
+  auto compute = [&](auto stage_tag, auto nmt_tag) {
     constexpr int ST = decltype(stage_tag)::value;
-    const lds_u8_t* As = stage_a(stage_tag);
-    const lds_u8_t* Ws = stage_w(stage_tag);
+    constexpr int NMT = decltype(nmt_tag)::value;
+    const lds_u8_t* As = (const lds_u8_t*)&lds[ST][0];
+    const lds_u8_t* Ws = As + A_BYTES;
     // this lane's weight codes for the whole step, one piece per N sub-tile
-    u32x4_t wcode[NT][(WDT == W_BF16) ? 4 : (WDT == W_E4M3 ? 2 : 1)];
+    u32x4_t wcode[NT][PIECES];
     float scl[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int row = wave * WN + nt * 32 + l32;
-      constexpr int PIECES = (WDT == W_BF16) ? 4 : (WDT == W_E4M3 ? 2 : 1);
+      const int row = wn * WN + nt * 32 + l32;
 #pragma unroll
       for (int j = 0; j < PIECES; ++j)
         wcode[nt][j] = lds_read<u32x4_t>(Ws + row * RB + swz<UW>(row, PIECES * h + j) * 16);
       if constexpr (WDT != W_BF16) scl[nt] = e8m0_as_scale(sc[ST][nt]);
     }
+    // activation fragments of substep ks (one per live 32-row quarter), read
+    // one substep ahead of their use
+    bf16x8_t af[2][NMT];
+    auto read_a = [&](int ks, bf16x8_t(&dst)[NMT]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t af[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int row = mt * 32 + l32;
-        af[mt] = lds_read<bf16x8_t>(As + row * 128 + swz<8>(row, 4 * h + ks) * 16);
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int row = wm * 64 + mt * 32 + l32;
+        dst[mt] = lds_read<bf16x8_t>(As + row * 128 + swz<8>(row, 4 * h + ks) * 16);
       }
+    };
+    // weight operand of pair j = (substep j / NT, N sub-tile j % NT), in bf16
+    auto operand = [&](int j) -> bf16x8_t {
+      const int ks = j / NT, nt = j % NT;
+      bf16x8_t bfr;
+      if constexpr (WDT == W_E2M1) {
+        bfr = dequant_e2m1x8(wcode[nt][0][ks], scl[nt]);
+      } else if constexpr (WDT == W_E4M3) {
+        const u32x4_t& v = wcode[nt][ks / 2];
+        bfr = dequant_e4m3x8(v[2 * (ks % 2)], v[2 * (ks % 2) + 1], scl[nt]);
+      } else {
+        __builtin_memcpy(&bfr, &wcode[nt][ks], 16);
+      }
+      return bfr;
+    };
+    // Pairs j = 0 .. 4*NT-1, NMT MFMAs each. The weight operand of pair j+1
+    // is dequantised while pair j's MFMAs run: a conversion feeding the very
+    // next MFMA stalls it, one pair ahead it overlaps (measured on gfx950).
+    read_a(0, af[0]);
+    bf16x8_t bq[2];
+    bq[0] = operand(0);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        bf16x8_t bfr;
-        if constexpr (WDT == W_E2M1) {
-          bfr = dequant_e2m1x8(wcode[nt][0][ks], scl[nt]);
-        } else if constexpr (WDT == W_E4M3) {
-          const u32x4_t& v = wcode[nt][ks / 2];
-          bfr = dequant_e4m3x8(v[2 * (ks % 2)], v[2 * (ks % 2) + 1], scl[nt]);
-        } else {
-          __builtin_memcpy(&bfr, &wcode[nt][ks], 16);
-        }
+    for (int j = 0; j < 4 * NT; ++j) {
+      const int ks = j / NT, nt = j % NT;
+      if (nt == 0 && ks < 3) read_a(ks + 1, af[(ks + 1) % 2]);
+      if (j + 1 < 4 * NT) bq[(j + 1) % 2] = operand(j + 1);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr, acc[mt][nt], 0, 0, 0);
+      for (int mt = 0; mt < NMT; ++mt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks % 2][mt], bq[j % 2], acc[mt][nt], 0, 0, 0);
+    }
+    if constexpr (WDT != W_BF16) {
+      // the schedule above, pinned: the step's LDS reads for the weight codes
+      // and the first activation fragments, the scale and first-operand VALU
+      // work, then per pair: (the next substep's activation reads,) the next
+      // operand's four conversions, the pair's MFMAs
+      constexpr int kDsRead = 0x100, kValu = 0x002, kMfma = 0x008;
+      __builtin_amdgcn_sched_group_barrier(kDsRead, NT * PIECES + NMT, 0);
+      __builtin_amdgcn_sched_group_barrier(kValu, 2 * NT + 4, 0);
+#pragma unroll
+      for (int j = 0; j < 4 * NT; ++j) {
+        if (j % NT == 0 && j / NT < 3) __builtin_amdgcn_sched_group_barrier(kDsRead, NMT, 0);
+        if (j + 1 < 4 * NT) __builtin_amdgcn_sched_group_barrier(kValu, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(kMfma, NMT, 0);
       }
     }
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  static_assert(kStages == 3, "the step loop below is unrolled for three stages");
+  using Two = std::integral_constant<int, 2>;
 
-  // Stage s holds step s mod 3. Before computing a step, the wave waits until
-  // only the loads of the next step are outstanding (LOADS of them), so this
-  // step's loads are done; the barrier then makes every wave's loads visible
-  // and guarantees all waves finished the previous step, whose stage the
-  // loads issued next overwrite.
-  issue(0, S0{});
-  issue(1, S1{});
-  for (int step = 0; step < nsteps_pad; step += kStages) {
-    wait_loads_barrier<LOADS>(sc[0]);
-    issue(step + 2, S2{});
-    if (wave_live) compute(S0{});
-    wait_loads_barrier<LOADS>(sc[1]);
-    issue(step + 3, S0{});
-    if (wave_live) compute(S1{});
-    wait_loads_barrier<LOADS>(sc[2]);
-    issue(step + 4, S1{});
-    if (wave_live) compute(S2{});
+  // Stage s holds steps s, s + STAGES, ... Before computing a step, the wave
+  // waits until only the loads of the STAGES - 2 steps after it are
+  // outstanding, so this step's loads are done; the barrier then makes every
+  // wave's loads visible and guarantees all waves finished the previous step,
+  // whose stage the loads issued next overwrite.
+  static_for<0, STAGES - 1>([&](auto st) { issue(decltype(st)::value, st); });
+  for (int step = 0; step < nsteps_pad; step += STAGES) {
+    static_for<0, STAGES>([&](auto st) {
+      constexpr int ST = decltype(st)::value;
+      wait_loads_barrier<LOADS * (STAGES - 2)>(sc[ST]);
+      issue(step + ST + STAGES - 1, std::integral_constant<int, (ST + STAGES - 1) % STAGES>{});
+      if (wave_live) compute(st, Two{});
+    });
   }
   // drain the look-ahead loads (all of them read as zeros past the last step)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -343,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmParams p) {
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = mt * 32 + (i / 4) * 8 + h * 4 + (i % 4);
+      const int row = wm * 64 + mt * 32 + (i / 4) * 8 + h * 4 + (i % 4);
       const int s = s_slot[row];
       if (s >= p.S) continue;
       uint16_t* crow = p.c + (int64_t)s * p.c_ld;
@@ -386,7 +445,7 @@ int gemm_block_m_large() { return kBM; }
 // Number of N tiles of the large-M kernel for this weight type.
 static int gemm_tiles_n(int wdt, int N, bool swiglu) {
   const int nt = wdt == W_E2M1 ? WTraits<W_E2M1>::kNT : (wdt == W_E4M3 ? WTraits<W_E4M3>::kNT : WTraits<W_BF16>::kNT);
-  const int bn = 4 * 32 * nt;
+  const int bn = kWavesN * 32 * nt;
   return swiglu ? (N / 2 + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
 }
 
