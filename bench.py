@@ -48,6 +48,9 @@ def parse():
                     help="expert weight layout: rows ([E][N][K]) or kblock (packed once by moe_pack_weights "
                          "before timing); auto = kblock for the large-M workloads, rows for decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters-from", metavar="DIR",
+                    help="no GPU run: read rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv files (-o fetch, -o write) "
+                         "from DIR and record the workload's per-launch HBM traffic in profiles/counters.json")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     return ap.parse_args()
 
@@ -58,6 +61,49 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, "mixture_experts_grouped_moe_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+# HBM byte counters, calibrated on a plain 1 GiB device copy (the copy
+# workload): rocprofv3 reads FETCH_SIZE = 524302 KiB for its 1 GiB of reads and
+# WRITE_SIZE = 1048576 KiB for its 1 GiB of writes.
+FETCH_FACTOR = 2.0
+WRITE_FACTOR = 1.0
+
+
+def record_counters(workload, directory):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the workload's
+    dominant kernel over the dispatches in the two rocprofv3 csv files, scale
+    them by the copy calibration and store the result in profiles/counters.json
+    under the current kernel source hash."""
+    import csv
+    key = WORKLOADS[workload].dominant
+    per = {}
+    for counter, stem in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        path = os.path.join(directory, f"{stem}_counter_collection.csv")
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and key in r["Kernel_Name"]:
+                    vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {key} in {path}")
+        per[counter] = (sum(vals.values()) / len(vals), len(vals))
+    fetch_kib, n_fetch = per["FETCH_SIZE"]
+    write_kib, n_write = per["WRITE_SIZE"]
+    hbm = (fetch_kib * FETCH_FACTOR + write_kib * WRITE_FACTOR) * 1024
+    out = os.path.join(ROOT, "profiles", "counters.json")
+    data = {}
+    if os.path.exists(out):
+        with open(out) as f:
+            data = json.load(f)
+    data[workload] = {"kernel": key, "source_hash": kernel_source_hash(),
+                      "fetch_kib_per_dispatch": round(fetch_kib, 1), "write_kib_per_dispatch": round(write_kib, 1),
+                      "dispatches": [n_fetch, n_write], "fetch_factor": FETCH_FACTOR, "write_factor": WRITE_FACTOR,
+                      "hbm_bytes_per_launch": round(hbm)}
+    with open(out, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({workload: data[workload]}))
 
 
 def load_traffic(kernel_key, launches_units):
@@ -496,6 +542,9 @@ def cpu_baseline(wl, target_s):
 
 def main():
     args = parse()
+    if args.counters_from:
+        record_counters(args.workload, args.counters_from)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of this "
                                    "build (--gpus must be 1)"}))
