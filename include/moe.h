@@ -265,8 +265,10 @@ moe_status moe_combine(const void* c, int64_t c_ld, const float* topk_w,
  * in fp32; experts with no slots are written as zeros; PAD positions are
  * skipped. x (device) bf16 [T][K], row stride x_ld; grad (device) bf16 [S][N],
  * row stride grad_ld; dw (device) fp32 [E][N][K] contiguous.
- * Requirements: block_m == moe_wgrad_block_m(); n % 32 == 0, k % 32 == 0;
- * x_ld, grad_ld multiples of 8. No workspace.
+ * Requirements: block_m == moe_wgrad_block_m(); num_experts <= 1024;
+ * n % 32 == 0, k % 32 == 0; x_ld, grad_ld multiples of 8; x, grad and dw
+ * 16-byte aligned; x and grad each span less than 2 GB.
+ * No workspace.
  * ---------------------------------------------------------------------- */
 moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad_ld,
                      const int32_t* sorted_token_ids, const int32_t* expert_ids,

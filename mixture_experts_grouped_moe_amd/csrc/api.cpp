@@ -327,6 +327,8 @@ moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad
   if (num_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens < 0");
   if (top_k < 1 || num_experts < top_k)
     return fail(MOE_ERR_INVALID_ARGUMENT, "need 1 <= top_k (%d) <= num_experts (%d)", top_k, num_experts);
+  if (num_experts > kAlignMaxExperts)
+    return fail(MOE_ERR_UNSUPPORTED, "num_experts %d > %d", num_experts, kAlignMaxExperts);
   if (n < 32 || n % 32 != 0 || k < 32 || k % 32 != 0 || n >= INT32_MAX || k >= INT32_MAX)
     return fail(MOE_ERR_INVALID_ARGUMENT, "n and k must be positive multiples of 32");
   if (x_ld < k || x_ld % 8 != 0 || grad_ld < n || grad_ld % 8 != 0)
@@ -343,10 +345,13 @@ moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad
   if (dw == nullptr || (S > 0 && (x == nullptr || grad == nullptr || sorted_token_ids == nullptr ||
                                   expert_ids == nullptr)))
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
-  if (((uintptr_t)x | (uintptr_t)grad) % 16 != 0)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "x and grad must be 16-byte aligned");
-  const int64_t grid = (int64_t)num_experts * ((n + 127) / 128) * ((k + 127) / 128);
-  if (grid >= (int64_t)UINT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
+  if (((uintptr_t)x | (uintptr_t)grad | (uintptr_t)dw) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x, grad and dw must be 16-byte aligned");
+  const int64_t tiles = (int64_t)num_experts * ((n + 127) / 128) * ((k + 127) / 128);
+  if (tiles >= (int64_t)INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "too many dW tiles");
+  // x and grad are read through 32-bit buffer offsets
+  if (num_tokens * x_ld * 2 >= (int64_t)0x80000000 || S * grad_ld * 2 >= (int64_t)0x80000000)
+    return fail(MOE_ERR_UNSUPPORTED, "x or grad spans 2 GB or more");
   (void)num_tokens_post_pad;
   moe_status st = check_device();
   if (st != MOE_OK) return st;

@@ -46,6 +46,8 @@ struct WgradParams {
   int32_t N, K;
   int32_t max_blocks;
   int32_t tiles_n, tiles_k;
+  uint32_t topk_magic;  // slot s's token row s / top_k = (s * topk_magic) >> topk_shift
+  int32_t topk_shift;
   float* dw;
 };
 

@@ -6,148 +6,313 @@
 // atomics needed dW reset between benchmark trials or results were corrupted)
 // and Tests & Benchmarks (constant input, linearity, zero-padded tokens).
 //
-// Design for gfx950: every workgroup owns one (expert, 128 x 128) tile of dW
-// and loops over that expert's routing blocks (64 slots each), contracting
-// over slots on v_mfma_f32_32x32x16_bf16; it writes its tile once, so dW is
-// overwritten (never accumulated into), empty experts get zeros, nothing is
-// atomic and repeated calls give identical bits. The contraction runs over
-// the slot dimension, which is strided in both operands, so the slot-major
-// tiles are transposed on their way into LDS. The expert's block range is
-// found by a 64-way search of expert_ids by one wave.
+// Design for gfx950:
+//  * dW is cut into (expert, 128 x 128) tiles. A persistent grid (two
+//    workgroups per CU) walks them; each tile is accumulated over its
+//    expert's routing blocks on v_mfma_f32_32x32x16_bf16 and written once, so
+//    dW is overwritten (never accumulated into), empty experts get zeros,
+//    nothing is atomic and repeated calls give identical bits.
+//  * Slot rows of grad (128 columns) and x (128 columns) go straight from
+//    global memory into LDS with buffer_load ... lds, slot-major as they lie
+//    in memory, 32 slots per pipeline unit in four stages (three units ahead,
+//    across tile boundaries, one barrier per unit).
+//  * The contraction runs over slots, so an MFMA operand needs 8 consecutive
+//    slots of one column: gfx950's transposing LDS read (ds_read_b64_tr_b16)
+//    gathers them. Within each 16-lane group, lane j receives element j % 4
+//    of the 8-byte reads of lanes j/4, j/4 + 4, j/4 + 8, j/4 + 12 (measured);
+//    lane s of the group therefore points at slot (s / 4) and columns
+//    4 (s % 4) .. + 3, and lane j ends up with column j of four consecutive
+//    slots. Two such reads make one operand.
+//  * Each store instruction writes two dW rows' 128-byte stretches (the
+//    MFMA output holds one column per lane), non-temporal; writing four
+//    adjacent columns per lane instead (16-byte stores, 32-byte stretches)
+//    measured six times slower.
+//  * The 16-byte units of each 256-byte LDS row are XOR-swizzled by slot.
+//  * Tiles are numbered expert-major, then in groups of 8 N tiles walked
+//    N-fastest, and each XCD takes consecutive tiles: the 64 workgroups an
+//    XCD runs at once cover 8 x 8 tiles of one expert, whose 8 grad and 8 x
+//    slices (2 MB) stay in its L2.
+//  * Every expert's block range comes from one pass over expert_ids (sorted
+//    by expert, sentinels last) into an LDS table at the start; slot ids are
+//    read with scalar loads one unit ahead of their use, so the only
+//    vector-memory operations in the pipeline are its own loads and the tile
+//    stores.
 #include "common.h"
 #include "params.h"
 
 namespace moe {
 
-constexpr int kWgBM = 64;   // routing block (contraction step)
-constexpr int kWgTN = 128;  // dW rows (N) per workgroup
-constexpr int kWgTK = 128;  // dW columns (K) per workgroup
-constexpr int kWgPitch = kWgBM + 8;  // LDS row pitch (bf16) of the transposed tiles
+constexpr int kWgBM = 64;                  // routing block
+constexpr int kWgUM = 32;                  // slots per pipeline unit
+constexpr int kWgTN = 128;                 // dW rows (N) per tile
+constexpr int kWgTK = 128;                 // dW columns (K) per tile
+constexpr int kWgRowB = 256;               // bytes of one slot row of a tile (128 bf16)
+constexpr int kWgUnitB = kWgUM * kWgRowB;  // 8 KB
+constexpr int kWgStages = 4;
+constexpr int kWgLoads = 4;                // DMA instructions per wave per unit (2 grad + 2 x)
+constexpr int kWgStores = 64;              // stores per lane per tile
+constexpr int kWgPerCU = 2;                // resident workgroups per CU
+constexpr int kWgMaxExperts = 1024;
+constexpr int kWgGroupN = 8;               // N tiles per group of the tile order
+constexpr uint32_t kWgOOB = 0x80000000u;   // buffer offset past x and grad (each below 2 GB): reads 0
 
+typedef __attribute__((address_space(3))) uint8_t wg_lds_u8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short wg_s16x4_t;
 
-// First block index b in [0, nb) whose expert is >= target (sentinel -1
-// blocks count as +infinity); nb when there is none. Called by one full wave.
-__device__ int first_block_at_least(const int32_t* expert_ids, int nb, int target, int lane) {
-  int lo = 0, hi = nb;  // answer in [lo, hi]
-  while (hi - lo > kWave) {
-    const int step = (hi - lo + kWave - 1) / kWave;
-    const int idx = lo + lane * step;
-    bool ge = true;
-    if (idx < hi) {
-      const int v = expert_ids[idx];
-      ge = (v < 0) || (v >= target);
-    }
-    const uint64_t m = __ballot(ge);
-    const int f = m ? __ffsll((unsigned long long)m) - 1 : kWave;  // first sample >= target
-    if (f == 0) return lo;  // key(lo) >= target
-    const int new_lo = lo + (f - 1) * step + 1;
-    const int new_hi = min(hi, lo + f * step);
-    lo = new_lo;
-    hi = new_hi;
-  }
-  const int idx = lo + lane;
-  bool ge = true;
-  if (idx < hi) {
-    const int v = expert_ids[idx];
-    ge = (v < 0) || (v >= target);
-  }
-  const uint64_t m = __ballot(ge && idx < hi);
-  return m ? lo + __ffsll((unsigned long long)m) - 1 : hi;
+// Physical 16-byte unit of logical unit u in tile row (slot) m. A
+// transposing read covers 4 consecutive slots x 4 consecutive units per half
+// wave; XOR-ing the unit with 4 (m % 4) puts those 16 on distinct banks.
+__device__ __forceinline__ int wg_swz(int m, int u) { return u ^ ((m % 4) * 4); }
+
+// 16 bytes per lane from `rsrc` at `voff` into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void wg_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc) : "m0");
 }
 
-__global__ __launch_bounds__(256) void wgrad_kernel(WgradParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t gt[kWgTN][kWgPitch];  // grad^T tile [n][slot]
-  __shared__ __attribute__((aligned(16))) uint16_t xt[kWgTK][kWgPitch];  // x^T tile [k][slot]
-  __shared__ int32_t s_slot[kWgBM];
-  __shared__ int32_t s_range[2];
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int wg_i32x8_t;
 
-  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_e = p.tiles_n * p.tiles_k;
-  const int e = L / per_e;
-  const int rem = L % per_e;
-  const int tn = rem / p.tiles_k, tk = rem % p.tiles_k;
-  const int n0 = tn * kWgTN, k0 = tk * kWgTK;
+// 8 consecutive int32 at byte `off` of buffer `rsrc` through the scalar
+// cache (a read). Asynchronous: the result must not be used before an
+// lgkmcnt(0) wait that lists it (wg_wait_barrier).
+__device__ __forceinline__ wg_i32x8_t wg_scalar_ids8(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+  wg_i32x8_t v;
+  asm volatile("s_buffer_load_dwordx8 %0, %1, %2"
+               : "=s"(v) : "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(off)));
+  return v;
+}
+
+// Wait until at most N of this wave's vector-memory operations are in
+// flight and every LDS and scalar-memory operation is done, then barrier;
+// `ids` (a prefetched scalar load) is final from here on.
+template <int N>
+__device__ __forceinline__ void wg_wait_barrier(wg_i32x8_t& ids) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%1) lgkmcnt(0)\n\ts_barrier" : "+s"(ids) : "n"(N) : "memory");
+}
+
+// Operand of 8 consecutive slots [m0, m0 + 8) of tile column c0 + lane % 32,
+// for the 32-wide MFMA fragment: lane l takes column c0 + l % 32 and slots
+// m0 + 8 (l / 32) + i. Built from two transposing reads (slots +0..3, +4..7).
+__device__ __forceinline__ bf16x8_t wg_operand(const wg_lds_u8_t* tile, int c0, int m0, int lane) {
+  const int g = lane / 16, s = lane % 16;
+  const int col = c0 + 16 * (g % 2) + 4 * (s % 4);
+  const int slot = m0 + 8 * (g / 2) + s / 4;
+  bf16x8_t r;
+  wg_s16x4_t v[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int m = slot + 4 * half;
+    const int byte = m * kWgRowB + wg_swz(m, col / 8) * 16 + (col % 8) * 2;
+    v[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) wg_s16x4_t*)(tile + byte));
+  }
+  __builtin_memcpy(&r, v, 16);
+  return r;
+}
+
+// A tile of dW and its expert's block range.
+struct WgTile {
+  int e, n0, k0, b0, b1;
+};
+
+__global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
+  // four stages of [grad unit | x unit], slot-major, 8 KB each
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kWgStages][2][kWgUnitB];
+  __shared__ int32_t s_start[kWgMaxExperts + 1];  // first block of expert e (s_start[E] = end)
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l32 = lane % 32, h = lane / 32;
-  if (wave == 0) {
-    const int b0 = first_block_at_least(p.expert_ids, p.max_blocks, e, lane);
-    if (lane == 0) s_range[0] = b0;
-  } else if (wave == 1) {
-    const int b1 = first_block_at_least(p.expert_ids, p.max_blocks, e + 1, lane);
-    if (lane == 0) s_range[1] = b1;
+
+  // ---- expert block ranges: experts (lo, hi] start at every block b where
+  //      the expert id changes (lo = previous id, hi = this id, or E for the
+  //      first sentinel); experts past the last boundary start at max_blocks
+  for (int e = tid; e <= p.E; e += 256) s_start[e] = p.max_blocks;
+  __syncthreads();
+  for (int b = tid; b < p.max_blocks; b += 256) {
+    const int cur = p.expert_ids[b];
+    const int prev = b > 0 ? p.expert_ids[b - 1] : -1;
+    const int hi = (cur < 0 || cur > p.E) ? p.E : cur;
+    const int lo = (b == 0 || prev < 0) ? -1 : prev;
+    if ((b == 0 || prev != cur) && !(prev < 0 && cur < 0 && b > 0))
+      for (int e = lo + 1; e <= hi; ++e) s_start[e] = b;
   }
   __syncthreads();
-  const int b0 = s_range[0], b1 = s_range[1];
 
-  // waves 2 x 2: wave (wn, wk) computes rows n0 + wn*64 .. and cols k0 + wk*64 ..
-  const int wn = wave / 2, wk = wave % 2;
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // Tile order: expert-major; within an expert, groups of kWgGroupN N tiles
+  // walked N-fastest then K, so any kWgGroupN x (64 / kWgGroupN) consecutive
+  // tiles share a few grad and x slices. XCD x (= hardware id % 8) owns the
+  // x-th eighth of the sequence, and its G/8 workgroups take consecutive
+  // tiles of it round by round (G = gridDim.x).
+  const int per_e = p.tiles_n * p.tiles_k;
+  const int total = p.E * per_e;  // below 2^31 (checked by the host API)
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  const int chunk = (total + 7) / 8;
+  auto tile_index = [&](int it) -> int {
+    const int q = it * (G / 8) + local;
+    const int T = xcd * chunk + q;
+    return (q < chunk && T < total) ? T : total;
+  };
+  auto tile_at = [&](int T) {
+    WgTile t;
+    t.e = T / per_e;
+    const int r = T % per_e;
+    const int in_group = kWgGroupN * p.tiles_k;
+    const int first_n = (r / in_group) * kWgGroupN;
+    const int gsize = min(p.tiles_n - first_n, kWgGroupN);
+    t.n0 = (first_n + (r % in_group) % gsize) * kWgTN;
+    t.k0 = ((r % in_group) / gsize) * kWgTK;
+    t.b0 = __builtin_amdgcn_readfirstlane(s_start[t.e]);
+    t.b1 = __builtin_amdgcn_readfirstlane(s_start[t.e + 1]);
+    return t;
+  };
 
-  for (int b = b0; b < b1; ++b) {
-    __syncthreads();
-    if (tid < kWgBM) s_slot[tid] = p.sorted[(int64_t)b * kWgBM + tid];
-    __syncthreads();
-    // load 64 slot rows x 128 columns of grad and of x (16-byte chunks),
-    // write them transposed: gt[n][m], xt[k][m]
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // 1024 chunks: 64 slot rows x 16 column chunks; a wave takes one chunk
-      // column of all 64 rows so its transposed LDS writes are consecutive.
-      const int m = lane, c = wave + 4 * i;
-      const int s = s_slot[m];
-      u32x4_t gv = {0, 0, 0, 0}, xv = {0, 0, 0, 0};
-      if (s < p.S) {
-        const int gn = n0 + c * 8, xk = k0 + c * 8;
-        if (gn < p.N) gv = *reinterpret_cast<const u32x4_t*>(p.grad + (int64_t)s * p.grad_ld + gn);
-        if (xk < p.K) xv = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)(s / p.top_k) * p.x_ld + xk);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        gt[c * 8 + 2 * q][m] = (uint16_t)(gv[q] & 0xffffu);
-        gt[c * 8 + 2 * q + 1][m] = (uint16_t)(gv[q] >> 16);
-        xt[c * 8 + 2 * q][m] = (uint16_t)(xv[q] & 0xffffu);
-        xt[c * 8 + 2 * q + 1][m] = (uint16_t)(xv[q] >> 16);
-      }
+  const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.grad, 0, (int)(uint32_t)((int64_t)p.S * p.grad_ld * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.x, 0, (int)(uint32_t)((int64_t)(p.S / p.top_k) * p.x_ld * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sorted_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.sorted, 0, (int)(uint32_t)((int64_t)p.max_blocks * kWgBM * 4), 0x00020000);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(wg_lds_u8_t*)&lds[0][0][0];
+
+  // ---- loader: walks the same tiles' units kWgStages - 1 units ahead of the
+  //      computation. Unit u of a tile is slots [32u, 32u + 32) of its block
+  //      list. Each unit is 8 DMA instructions per tile part (4 slot rows of
+  //      16 units each); wave w issues instructions 2w, 2w+1 of both parts.
+  //      Past the last tile it issues loads that read zeros, so every unit
+  //      costs the same number of loads.
+  // loader state: the unit to issue next and its slot ids (this wave's 8
+  // rows), prefetched by a scalar load when the previous unit was issued
+  int ld_it = 0;
+  WgTile ld = tile_at(tile_index(0));
+  int ld_u = 0;
+  auto ld_skip_empty = [&]() {  // move to the next tile with a unit left (empty experts have none)
+    while (tile_index(ld_it) < total && ld_u >= 2 * (ld.b1 - ld.b0)) {
+      ++ld_it;
+      ld_u = 0;
+      if (tile_index(ld_it) < total) ld = tile_at(tile_index(ld_it));
     }
-    __syncthreads();
+  };
+  auto ld_ids = [&]() {
+    wg_i32x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (tile_index(ld_it) < total)
+      v = wg_scalar_ids8(sorted_rsrc, (uint32_t)((ld.b0 * kWgBM + ld_u * kWgUM + wave * 8) * 4));
+    return v;
+  };
+  ld_skip_empty();
+  wg_i32x8_t ids = ld_ids();
+  wg_wait_barrier<0>(ids);
+  const int lrow = lane / 16, lpu = lane % 16;
+  auto issue_next = [&](int stage) {
+    const bool live = tile_index(ld_it) < total;
+    const uint32_t dst = lds_base + (uint32_t)(stage * 2 * kWgUnitB);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int m0 = ks * 16 + h * 8;
-      bf16x8_t af[2], bfr[2];
+    for (int i = 0; i < 2; ++i) {
+      const int m = (wave * 2 + i) * 4 + lrow;  // slot row of the unit
+      const int u = wg_swz(m, lpu);             // logical 16-byte unit this lane fetches
+      uint32_t goff = kWgOOB, xoff = kWgOOB;
+      if (live) {
+        const int s = lrow == 0 ? ids[4 * i] : (lrow == 1 ? ids[4 * i + 1] : (lrow == 2 ? ids[4 * i + 2] : ids[4 * i + 3]));
+        if (s < p.S) {
+          if (ld.n0 + u * 8 < p.N) goff = (uint32_t)s * (uint32_t)(p.grad_ld * 2) + (uint32_t)(ld.n0 + u * 8) * 2;
+          if (ld.k0 + u * 8 < p.K) {
+            // token row of slot s: s / top_k by multiply-high (exact for s < 2^31)
+            const uint32_t xrow = (uint32_t)(((uint64_t)(uint32_t)s * p.topk_magic) >> p.topk_shift);
+            xoff = xrow * (uint32_t)(p.x_ld * 2) + (uint32_t)(ld.k0 + u * 8) * 2;
+          }
+        }
+      }
+      wg_dma16(g_rsrc, goff, dst + (uint32_t)((wave * 2 + i) * 1024));
+      wg_dma16(x_rsrc, xoff, dst + (uint32_t)(kWgUnitB + (wave * 2 + i) * 1024));
+    }
+    if (live) {
+      ++ld_u;
+      ld_skip_empty();
+      ids = ld_ids();  // completes by the next wait
+    }
+  };
+
+  // waves 2 x 2: wave (wn, wk) computes dW rows n0 + wn*64 .. and columns k0 + wk*64 ..
+  const int wn = wave / 2, wk = wave % 2;
+  f32x16_t acc[2][2];  // [n sub-tile][k sub-tile]
+  auto contract = [&](int stage) {
+    const wg_lds_u8_t* gt = (const wg_lds_u8_t*)&lds[stage][0][0];
+    const wg_lds_u8_t* xt = (const wg_lds_u8_t*)&lds[stage][1][0];
+    // every operand of the unit first (their LDS latency overlaps), then the MFMAs
+    constexpr int KS = kWgUM / 16;
+    bf16x8_t af[KS][2], bfr[KS][2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&gt[wn * 64 + i * 32 + l32][m0]);
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&xt[wk * 64 + j * 32 + l32][m0]);
+      for (int i = 0; i < 2; ++i) af[ks][i] = wg_operand(gt, wn * 64 + i * 32, ks * 16, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfr[ks][j] = wg_operand(xt, wk * 64 + j * 32, ks * 16, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+  };
 
-  float* out = p.dw + (int64_t)e * p.N * p.K;
+  // ---- computation. Before unit c the wave waits until only the loads of
+  //      units c+1, c+2 (and the stores of a tile finished just before) are in
+  //      flight; the barrier then makes every wave's DMA visible and
+  //      guarantees all waves finished unit c-1, whose stage the loads issued
+  //      next overwrite.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int q = 0; q < kWgStages - 1; ++q) {
+    issue_next(q);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(ids));
+  }
+  int c = 0;
+  bool stored = false;
+  for (int it = 0; tile_index(it) < total; ++it) {
+    const WgTile t = tile_at(tile_index(it));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int k = k0 + wk * 64 + j * 32 + l32;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = n0 + wn * 64 + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
-        if (n < p.N && k < p.K) out[(int64_t)n * p.K + k] = acc[i][j][r];
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int nu = 2 * (t.b1 - t.b0);
+    for (int u = 0; u < nu; ++u, ++c) {
+      if (stored) {
+        // (more stores than the counter can express: waiting for 63 younger
+        // operations may also wait for a few stores, never too few)
+        constexpr int kAfterStores = kWgLoads * (kWgStages - 2) + kWgStores;
+        wg_wait_barrier<(kAfterStores > 63 ? 63 : kAfterStores)>(ids);
+        stored = false;
+      } else {
+        wg_wait_barrier<kWgLoads * (kWgStages - 2)>(ids);
       }
+      issue_next((c + kWgStages - 1) % kWgStages);
+      contract(c % kWgStages);
     }
+    // store the tile: lane (l32, h) holds dW column k0 + wk*64 + j*32 + l32
+    // of rows n0 + wn*64 + i*32 + 8 (r/4) + 4h + r%4, so each store writes
+    // two rows' 128-byte stretches
+    float* out = p.dw + (int64_t)t.e * p.N * p.K;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int k = t.k0 + wk * 64 + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = t.n0 + wn * 64 + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+          if (n < p.N && k < p.K) __builtin_nontemporal_store(acc[i][j][r], &out[(int64_t)n * p.K + k]);
+        }
+      }
+    stored = true;
+  }
+  // drain the look-ahead loads (past the last tile they read zeros)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 int wgrad_block_m() { return kWgBM; }
@@ -156,8 +321,24 @@ hipError_t launch_wgrad(const WgradParams& p_in, hipStream_t stream) {
   WgradParams p = p_in;
   p.tiles_n = (p.N + kWgTN - 1) / kWgTN;
   p.tiles_k = (p.K + kWgTK - 1) / kWgTK;
-  const int64_t grid = (int64_t)p.E * p.tiles_n * p.tiles_k;
-  if (grid == 0) return hipSuccess;
+  // division by top_k as a multiply-high: with l = ceil(log2 d) and
+  // m = ceil(2^(31+l) / d), floor(s / d) = (s m) >> (31 + l) for every
+  // s < 2^31 (Granlund and Montgomery, "Division by invariant integers using
+  // multiplication", 1994, Theorem 4.2 with N = 31)
+  int l = 0;
+  while ((1 << l) < p.top_k) ++l;
+  p.topk_magic = (uint32_t)((((uint64_t)1 << (31 + l)) + (uint64_t)p.top_k - 1) / (uint64_t)p.top_k);
+  p.topk_shift = 31 + l;
+  const int64_t tiles = (int64_t)p.E * p.tiles_n * p.tiles_k;
+  if (tiles == 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  // a persistent grid: kWgPerCU workgroups per CU, a multiple of 8 (one
+  // stretch of tiles per XCD per round)
+  int64_t grid = (int64_t)cus * kWgPerCU;
+  grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL(wgrad_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

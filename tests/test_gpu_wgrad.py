@@ -27,7 +27,8 @@ def run_wgrad(d, out=None):
     return dw
 
 
-@pytest.mark.parametrize("T,k,E,N,K", [(300, 4, 8, 256, 384), (97, 2, 5, 160, 96), (1000, 8, 32, 64, 128)])
+@pytest.mark.parametrize("T,k,E,N,K", [(300, 4, 8, 256, 384), (97, 2, 5, 160, 96), (1000, 8, 32, 64, 128),
+                                       (130, 3, 7, 96, 160), (64, 6, 12, 64, 64), (1, 1, 1, 32, 32)])
 def test_small_full(T, k, E, N, K):
     d = synth.config5(seed=T, T=T, E=E, N=N, K=K, k=k, device="cuda")
     poison = torch.full((E, N, K), float("nan"), device="cuda")
