@@ -55,10 +55,18 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+# sources whose change can change a workload's dominant kernel
+KERNEL_SOURCES = {"decode": ["decode.hip"], "w4a16": ["gemm.hip"], "mxfp8": ["gemm.hip"],
+                  "wgrad": ["wgrad.hip"], "copy": []}
+
+
+def kernel_source_hash(workload):
+    """Hash of the source files the workload's dominant kernel is built from
+    (its own file plus the shared headers)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.join(ROOT, "mixture_experts_grouped_moe_amd", "csrc"))):
-        with open(os.path.join(ROOT, "mixture_experts_grouped_moe_amd", "csrc", name), "rb") as f:
+    csrc = os.path.join(ROOT, "mixture_experts_grouped_moe_amd", "csrc")
+    for name in KERNEL_SOURCES[workload] + (["common.h", "params.h"] if KERNEL_SOURCES[workload] else []):
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
@@ -96,7 +104,7 @@ def record_counters(workload, directory):
     if os.path.exists(out):
         with open(out) as f:
             data = json.load(f)
-    data[workload] = {"kernel": key, "source_hash": kernel_source_hash(),
+    data[workload] = {"kernel": key, "source_hash": kernel_source_hash(workload),
                       "fetch_kib_per_dispatch": round(fetch_kib, 1), "write_kib_per_dispatch": round(write_kib, 1),
                       "dispatches": [n_fetch, n_write], "fetch_factor": FETCH_FACTOR, "write_factor": WRITE_FACTOR,
                       "hbm_bytes_per_launch": round(hbm)}
@@ -115,7 +123,7 @@ def load_traffic(kernel_key, launches_units):
     with open(path) as f:
         data = json.load(f)
     ent = data.get(kernel_key)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel_key):
         return None
     return ent.get("hbm_bytes_per_launch")
 
