@@ -186,3 +186,34 @@ def test_empty_token_guard():
     y = moe.moe_combine(out, d["topk_w"], 2)
     torch.cuda.synchronize()
     assert y.shape == (0, 128)
+
+
+def test_config4_mxfp8_full_size_sampled():
+    # The MXFP8 workload at its full size (E=256, top-8, K=7168, N=4096,
+    # T=4096, Zipf routing with 16 empty experts) in the launch configuration
+    # the benchmark times (packed weights), checked on sampled slots: the
+    # hottest expert, the highest-numbered routed expert (its weights start
+    # past 2^31 elements) and two more, first / middle / last slot of each.
+    moe = _moe()
+    from helpers import LazyRows
+    d = synth.config4(device="cuda")
+    T, k, E = 4096, 8, 256
+    pw = moe.moe_pack_weights(d["w"], "e4m3", w_scale=d["w_scale"])
+    bm = moe.moe_gemm_block_m("e4m3", T)
+    routing = moe.moe_align(d["ids"], E, bm)
+    C = torch.full((T * k, 4096), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(d["x"], pw, "e4m3", routing, T, k, E, k, out=C)
+    torch.cuda.synchronize()
+    ids = synth.bits(d["ids"]).reshape(-1)
+    counts = np.bincount(ids, minlength=E)
+    routed = np.nonzero(counts)[0]
+    experts = {int(np.argmax(counts)), int(routed.max()), int(routed[len(routed) // 3]), int(routed[2 * len(routed) // 3])}
+    slots = []
+    for e in sorted(experts):
+        es = np.nonzero(ids == e)[0]
+        slots += [int(es[0]), int(es[len(es) // 2]), int(es[-1])]
+    slots = sorted(set(slots))
+    ref, routed_mask = ogemm.grouped_gemm(synth.bits(d["x"]), k, LazyRows(d["w"]), "e4m3", LazyRows(d["w_scale"]),
+                                          ids, E, slots=slots)
+    assert routed_mask[slots].all()
+    assert_parity(bf16_to_f64(C[slots]), ref[slots], what="config4 sampled slots")
