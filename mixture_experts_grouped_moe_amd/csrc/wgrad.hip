@@ -7,15 +7,16 @@
 // and Tests & Benchmarks (constant input, linearity, zero-padded tokens).
 //
 // Design for gfx950:
-//  * dW is cut into (expert, 128 x 128) tiles. A persistent grid (two
+//  * dW is cut into (expert, 128 x 256) tiles. A persistent grid (two
 //    workgroups per CU) walks them; each tile is accumulated over its
 //    expert's routing blocks on v_mfma_f32_32x32x16_bf16 and written once, so
 //    dW is overwritten (never accumulated into), empty experts get zeros,
 //    nothing is atomic and repeated calls give identical bits.
-//  * Slot rows of grad (128 columns) and x (128 columns) go straight from
-//    global memory into LDS with buffer_load ... lds, slot-major as they lie
-//    in memory, 32 slots per pipeline unit in four stages (three units ahead,
-//    across tile boundaries, one barrier per unit).
+//  * Slot rows of grad (128 columns, 256 B) and x (256 columns, 512 B) go
+//    straight from global memory into LDS with buffer_load ... lds,
+//    slot-major as they lie in memory, 32 slots per pipeline unit in three
+//    24 KB stages (two units ahead, across tile boundaries, one barrier per
+//    unit). Each wave computes 64 x 128 of the tile: 16 MFMAs per unit.
 //  * The contraction runs over slots, so an MFMA operand needs 8 consecutive
 //    slots of one column: gfx950's transposing LDS read (ds_read_b64_tr_b16)
 //    gathers them. Within each 16-lane group, lane j receives element j % 4
@@ -23,45 +24,59 @@
 //    lane s of the group therefore points at slot (s / 4) and columns
 //    4 (s % 4) .. + 3, and lane j ends up with column j of four consecutive
 //    slots. Two such reads make one operand.
-//  * Each store instruction writes two dW rows' 128-byte stretches (the
-//    MFMA output holds one column per lane), non-temporal; writing four
-//    adjacent columns per lane instead (16-byte stores, 32-byte stretches)
-//    measured six times slower.
-//  * The 16-byte units of each 256-byte LDS row are XOR-swizzled by slot.
+//  * A finished tile goes out through LDS: the MFMA output holds one column
+//    per lane, so each wave passes 8 rows at a time through a scratch area
+//    (the stage the next unit's loads will fill, free at that point) and
+//    writes whole 512-byte row pieces with 16-byte non-temporal stores.
+//    Storing the MFMA output as it lies (one dword per lane, 128-byte row
+//    stretches) issues four times the store instructions; four adjacent
+//    columns per lane from swapped operands (32-byte stretches) measured
+//    slower still.
+//  * The 16-byte units of each LDS row are XOR-swizzled by slot.
 //  * Tiles are numbered expert-major, then in groups of 8 N tiles walked
 //    N-fastest, and each XCD takes consecutive tiles: the 64 workgroups an
-//    XCD runs at once cover 8 x 8 tiles of one expert, whose 8 grad and 8 x
-//    slices (2 MB) stay in its L2.
+//    XCD runs at once cover 8 x 8 tiles of one expert, whose grad and x
+//    slices stay in its L2.
 //  * Every expert's block range comes from one pass over expert_ids (sorted
 //    by expert, sentinels last) into an LDS table at the start; slot ids are
-//    read with scalar loads one unit ahead of their use, so the only
-//    vector-memory operations in the pipeline are its own loads and the tile
-//    stores.
+//    read with scalar loads one unit ahead of their use and turned into row
+//    offsets on the scalar unit (the token row s / top_k by a multiply-high),
+//    so a load costs each lane only a select and an add. PAD slots and the
+//    look-ahead past the last tile read zeros through the buffer bounds;
+//    columns past N or K read whatever follows in memory and only reach dW
+//    rows and columns that are never stored.
 #include "common.h"
 #include "params.h"
 
 namespace moe {
 
-constexpr int kWgBM = 64;                  // routing block
-constexpr int kWgUM = 32;                  // slots per pipeline unit
-constexpr int kWgTN = 128;                 // dW rows (N) per tile
-constexpr int kWgTK = 128;                 // dW columns (K) per tile
-constexpr int kWgRowB = 256;               // bytes of one slot row of a tile (128 bf16)
-constexpr int kWgUnitB = kWgUM * kWgRowB;  // 8 KB
-constexpr int kWgStages = 4;
-constexpr int kWgLoads = 4;                // DMA instructions per wave per unit (2 grad + 2 x)
-constexpr int kWgStores = 64;              // stores per lane per tile
-constexpr int kWgPerCU = 2;                // resident workgroups per CU
+constexpr int kWgBM = 64;                    // routing block
+constexpr int kWgUM = 32;                    // slots per pipeline unit
+constexpr int kWgTN = 128;                   // dW rows (N) per tile
+constexpr int kWgTK = 256;                   // dW columns (K) per tile
+constexpr int kWgGRowB = kWgTN * 2;          // 256 B: a slot's grad piece
+constexpr int kWgXRowB = kWgTK * 2;          // 512 B: a slot's x piece
+constexpr int kWgGUnitB = kWgUM * kWgGRowB;  // 8 KB
+constexpr int kWgXUnitB = kWgUM * kWgXRowB;  // 16 KB
+constexpr int kWgStageB = kWgGUnitB + kWgXUnitB;
+constexpr int kWgStages = 3;
+constexpr int kWgGLoads = kWgGUnitB / 1024 / 4;  // DMA instructions per wave per unit: 2 grad
+constexpr int kWgXLoads = kWgXUnitB / 1024 / 4;  //   + 4 x
+constexpr int kWgLoads = kWgGLoads + kWgXLoads;
+constexpr int kWgStores = 8 * 4;             // stores per lane per tile
+constexpr int kWgPerCU = 2;                  // resident workgroups per CU
 constexpr int kWgMaxExperts = 1024;
-constexpr int kWgGroupN = 8;               // N tiles per group of the tile order
-constexpr uint32_t kWgOOB = 0x80000000u;   // buffer offset past x and grad (each below 2 GB): reads 0
+constexpr int kWgGroupN = 8;                 // N tiles per group of the tile order
+constexpr uint32_t kWgOOB = 0x80000000u;     // buffer offset past x and grad (each below 2 GB): reads 0
+static_assert(kWgGLoads == 2 && kWgXLoads == 4, "each wave loads the same 8 slot rows of both parts");
 
 typedef __attribute__((address_space(3))) uint8_t wg_lds_u8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short wg_s16x4_t;
 
-// Physical 16-byte unit of logical unit u in tile row (slot) m. A
-// transposing read covers 4 consecutive slots x 4 consecutive units per half
-// wave; XOR-ing the unit with 4 (m % 4) puts those 16 on distinct banks.
+// Physical 16-byte unit of logical unit u in LDS row (slot) m. A
+// transposing read covers 4 consecutive slots x 2 consecutive units per
+// 16-lane group; XOR-ing the unit with 4 (m % 4) moves the four slots' pieces
+// 64 bytes apart, onto distinct banks (rows are 256 or 512 bytes long).
 __device__ __forceinline__ int wg_swz(int m, int u) { return u ^ ((m % 4) * 4); }
 
 // 16 bytes per lane from `rsrc` at `voff` into LDS at lds_base + 16 * lane.
@@ -93,8 +108,10 @@ __device__ __forceinline__ void wg_wait_barrier(wg_i32x8_t& ids) {
 
 // Operand of 8 consecutive slots [m0, m0 + 8) of tile column c0 + lane % 32,
 // for the 32-wide MFMA fragment: lane l takes column c0 + l % 32 and slots
-// m0 + 8 (l / 32) + i. Built from two transposing reads (slots +0..3, +4..7).
-__device__ __forceinline__ bf16x8_t wg_operand(const wg_lds_u8_t* tile, int c0, int m0, int lane) {
+// m0 + 8 (l / 32) + i. Built from two transposing reads (slots +0..3, +4..7)
+// of an LDS part whose rows are ROWB bytes.
+template <int ROWB>
+__device__ __forceinline__ bf16x8_t wg_operand(const wg_lds_u8_t* part, int c0, int m0, int lane) {
   const int g = lane / 16, s = lane % 16;
   const int col = c0 + 16 * (g % 2) + 4 * (s % 4);
   const int slot = m0 + 8 * (g / 2) + s / 4;
@@ -103,9 +120,9 @@ __device__ __forceinline__ bf16x8_t wg_operand(const wg_lds_u8_t* tile, int c0, 
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int m = slot + 4 * half;
-    const int byte = m * kWgRowB + wg_swz(m, col / 8) * 16 + (col % 8) * 2;
+    const int byte = m * ROWB + wg_swz(m, col / 8) * 16 + (col % 8) * 2;
     v[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) wg_s16x4_t*)(tile + byte));
+        (__attribute__((address_space(3))) wg_s16x4_t*)(part + byte));
   }
   __builtin_memcpy(&r, v, 16);
   return r;
@@ -117,8 +134,8 @@ struct WgTile {
 };
 
 __global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
-  // four stages of [grad unit | x unit], slot-major, 8 KB each
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kWgStages][2][kWgUnitB];
+  // three stages of [grad unit | x unit], slot-major
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kWgStages][kWgStageB];
   __shared__ int32_t s_start[kWgMaxExperts + 1];  // first block of expert e (s_start[E] = end)
 
   const int tid = threadIdx.x;
@@ -176,139 +193,176 @@ __global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
       (void*)p.x, 0, (int)(uint32_t)((int64_t)(p.S / p.top_k) * p.x_ld * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t sorted_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.sorted, 0, (int)(uint32_t)((int64_t)p.max_blocks * kWgBM * 4), 0x00020000);
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(wg_lds_u8_t*)&lds[0][0][0];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(wg_lds_u8_t*)&lds[0][0];
+  const uint32_t g_row = (uint32_t)(p.grad_ld * 2), x_row = (uint32_t)(p.x_ld * 2);
 
   // ---- loader: walks the same tiles' units kWgStages - 1 units ahead of the
   //      computation. Unit u of a tile is slots [32u, 32u + 32) of its block
-  //      list. Each unit is 8 DMA instructions per tile part (4 slot rows of
-  //      16 units each); wave w issues instructions 2w, 2w+1 of both parts.
+  //      list; wave w loads slot rows 8w .. 8w + 7 of both parts (grad: two
+  //      instructions of 4 rows x 16 lanes, x: four of 2 rows x 32 lanes).
   //      Past the last tile it issues loads that read zeros, so every unit
   //      costs the same number of loads.
-  // loader state: the unit to issue next and its slot ids (this wave's 8
-  // rows), prefetched by a scalar load when the previous unit was issued
+  // The 16-byte unit each lane fetches, as a byte offset within the row
+  // piece (the LDS side is lane order, the global side the swizzled unit):
+  // grad rows have row % 4 = lane / 16; x load i has row % 4 = 2 (i % 2) + lane / 32.
+  const uint32_t g_col = (uint32_t)wg_swz(lane / 16, lane % 16) * 16;
+  const uint32_t x_col0 = (uint32_t)wg_swz(lane / 32, lane % 32) * 16;
+  const uint32_t x_col1 = (uint32_t)wg_swz(2 + lane / 32, lane % 32) * 16;
+  // all-ones masks of the lanes that take the second, third and fourth row
+  // of a grad load and the second row of an x load (selects by bit logic,
+  // one VALU operation each)
+  const uint32_t gm1 = lane / 16 == 1 ? ~0u : 0u, gm2 = lane / 16 == 2 ? ~0u : 0u, gm3 = lane / 16 == 3 ? ~0u : 0u;
+  const uint32_t xm1 = lane >= 32 ? ~0u : 0u;
+  auto pick = [](uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); };
+
   int ld_it = 0;
   WgTile ld = tile_at(tile_index(0));
   int ld_u = 0;
+  bool ld_live = tile_index(0) < total;
   auto ld_skip_empty = [&]() {  // move to the next tile with a unit left (empty experts have none)
-    while (tile_index(ld_it) < total && ld_u >= 2 * (ld.b1 - ld.b0)) {
+    while (ld_live && ld_u >= 2 * (ld.b1 - ld.b0)) {
       ++ld_it;
       ld_u = 0;
-      if (tile_index(ld_it) < total) ld = tile_at(tile_index(ld_it));
+      const int T = tile_index(ld_it);
+      ld_live = T < total;
+      if (ld_live) ld = tile_at(T);
     }
   };
   auto ld_ids = [&]() {
     wg_i32x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (tile_index(ld_it) < total)
-      v = wg_scalar_ids8(sorted_rsrc, (uint32_t)((ld.b0 * kWgBM + ld_u * kWgUM + wave * 8) * 4));
+    if (ld_live) v = wg_scalar_ids8(sorted_rsrc, (uint32_t)((ld.b0 * kWgBM + ld_u * kWgUM + wave * 8) * 4));
     return v;
   };
   ld_skip_empty();
   wg_i32x8_t ids = ld_ids();
   wg_wait_barrier<0>(ids);
-  const int lrow = lane / 16, lpu = lane % 16;
+
   auto issue_next = [&](int stage) {
-    const bool live = tile_index(ld_it) < total;
-    const uint32_t dst = lds_base + (uint32_t)(stage * 2 * kWgUnitB);
+    // scalar row offsets of the wave's 8 slots within the tile's column
+    // range (a PAD slot s = S lands at or past the end of both buffers)
+    // (past the last tile the ids are 0 and the bases put every lane past
+    // the buffers: s * row + kWgOOB stays below 2^32)
+    const uint32_t g_base = ld_live ? (uint32_t)ld.n0 * 2 : kWgOOB;
+    const uint32_t x_base = ld_live ? (uint32_t)ld.k0 * 2 : kWgOOB;
+    uint32_t go[8], xo[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int m = (wave * 2 + i) * 4 + lrow;  // slot row of the unit
-      const int u = wg_swz(m, lpu);             // logical 16-byte unit this lane fetches
-      uint32_t goff = kWgOOB, xoff = kWgOOB;
-      if (live) {
-        const int s = lrow == 0 ? ids[4 * i] : (lrow == 1 ? ids[4 * i + 1] : (lrow == 2 ? ids[4 * i + 2] : ids[4 * i + 3]));
-        if (s < p.S) {
-          if (ld.n0 + u * 8 < p.N) goff = (uint32_t)s * (uint32_t)(p.grad_ld * 2) + (uint32_t)(ld.n0 + u * 8) * 2;
-          if (ld.k0 + u * 8 < p.K) {
-            // token row of slot s: s / top_k by multiply-high (exact for s < 2^31)
-            const uint32_t xrow = (uint32_t)(((uint64_t)(uint32_t)s * p.topk_magic) >> p.topk_shift);
-            xoff = xrow * (uint32_t)(p.x_ld * 2) + (uint32_t)(ld.k0 + u * 8) * 2;
-          }
-        }
-      }
-      wg_dma16(g_rsrc, goff, dst + (uint32_t)((wave * 2 + i) * 1024));
-      wg_dma16(x_rsrc, xoff, dst + (uint32_t)(kWgUnitB + (wave * 2 + i) * 1024));
+    for (int r = 0; r < 8; ++r) {
+      const uint32_t s = (uint32_t)ids[r];
+      const uint64_t prod = ((uint64_t)__umulhi(s, p.topk_magic) << 32) | (s * p.topk_magic);
+      const uint32_t xrow = (uint32_t)(prod >> p.topk_shift);
+      go[r] = s * g_row + g_base;
+      xo[r] = xrow * x_row + x_base;
     }
-    if (live) {
+    const uint32_t dst = lds_base + (uint32_t)(stage * kWgStageB);
+#pragma unroll
+    for (int i = 0; i < kWgGLoads; ++i) {
+      const uint32_t row = pick(gm3, go[4 * i + 3], pick(gm2, go[4 * i + 2], pick(gm1, go[4 * i + 1], go[4 * i])));
+      wg_dma16(g_rsrc, row + g_col, dst + (uint32_t)((wave * kWgGLoads + i) * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < kWgXLoads; ++i) {
+      const uint32_t row = pick(xm1, xo[2 * i + 1], xo[2 * i]);
+      wg_dma16(x_rsrc, row + (i % 2 ? x_col1 : x_col0),
+               dst + (uint32_t)(kWgGUnitB + (wave * kWgXLoads + i) * 1024));
+    }
+    if (ld_live) {
       ++ld_u;
       ld_skip_empty();
       ids = ld_ids();  // completes by the next wait
     }
   };
 
-  // waves 2 x 2: wave (wn, wk) computes dW rows n0 + wn*64 .. and columns k0 + wk*64 ..
+  // waves 2 x 2: wave (wn, wk) computes dW rows n0 + wn*64 .. + 63 and
+  // columns k0 + wk*128 .. + 127
   const int wn = wave / 2, wk = wave % 2;
-  f32x16_t acc[2][2];  // [n sub-tile][k sub-tile]
+  f32x16_t acc[2][4];  // [n sub-tile][k sub-tile]
   auto contract = [&](int stage) {
-    const wg_lds_u8_t* gt = (const wg_lds_u8_t*)&lds[stage][0][0];
-    const wg_lds_u8_t* xt = (const wg_lds_u8_t*)&lds[stage][1][0];
+    const wg_lds_u8_t* gt = (const wg_lds_u8_t*)&lds[stage][0];
+    const wg_lds_u8_t* xt = gt + kWgGUnitB;
     // every operand of the unit first (their LDS latency overlaps), then the MFMAs
     constexpr int KS = kWgUM / 16;
-    bf16x8_t af[KS][2], bfr[KS][2];
+    bf16x8_t af[KS][2], bfr[KS][4];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[ks][i] = wg_operand(gt, wn * 64 + i * 32, ks * 16, lane);
+      for (int i = 0; i < 2; ++i) af[ks][i] = wg_operand<kWgGRowB>(gt, wn * 64 + i * 32, ks * 16, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[ks][j] = wg_operand(xt, wk * 64 + j * 32, ks * 16, lane);
+      for (int j = 0; j < 4; ++j) bfr[ks][j] = wg_operand<kWgXRowB>(xt, wk * 128 + j * 32, ks * 16, lane);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
   };
 
-  // ---- computation. Before unit c the wave waits until only the loads of
-  //      units c+1, c+2 (and the stores of a tile finished just before) are in
+  // ---- computation. Before a unit the wave waits until only the loads of
+  //      the next unit (and the stores of a tile finished just before) are in
   //      flight; the barrier then makes every wave's DMA visible and
-  //      guarantees all waves finished unit c-1, whose stage the loads issued
-  //      next overwrite.
+  //      guarantees all waves finished the previous unit, whose stage the
+  //      loads issued next overwrite.
 #pragma unroll
   for (int q = 0; q < kWgStages - 1; ++q) {
     issue_next(q);
     asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(ids));
   }
-  int c = 0;
+  int st = 0;  // stage of the next unit computed
   bool stored = false;
   for (int it = 0; tile_index(it) < total; ++it) {
     const WgTile t = tile_at(tile_index(it));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int nu = 2 * (t.b1 - t.b0);
-    for (int u = 0; u < nu; ++u, ++c) {
+    for (int u = 0; u < nu; ++u) {
       if (stored) {
         // (more stores than the counter can express: waiting for 63 younger
-        // operations may also wait for a few stores, never too few)
+        // operations may also wait for some stores, never too few)
         constexpr int kAfterStores = kWgLoads * (kWgStages - 2) + kWgStores;
         wg_wait_barrier<(kAfterStores > 63 ? 63 : kAfterStores)>(ids);
         stored = false;
       } else {
         wg_wait_barrier<kWgLoads * (kWgStages - 2)>(ids);
       }
-      issue_next((c + kWgStages - 1) % kWgStages);
-      contract(c % kWgStages);
+      issue_next(st == 0 ? kWgStages - 1 : st - 1);  // the stage computed last, now free
+      contract(st);
+      st = st == kWgStages - 1 ? 0 : st + 1;
     }
-    // store the tile: lane (l32, h) holds dW column k0 + wk*64 + j*32 + l32
-    // of rows n0 + wn*64 + i*32 + 8 (r/4) + 4h + r%4, so each store writes
-    // two rows' 128-byte stretches
-    float* out = p.dw + (int64_t)t.e * p.N * p.K;
+    // store the tile through LDS: the stage the next unit's loads will go
+    // to is free once every wave is past its last contraction. Each wave
+    // passes 8 rows at a time through its own 5 KB of it (rows padded to
+    // 640 bytes, so the two row halves of a write land on distinct banks)
+    // and writes whole 512-byte row pieces with 16-byte stores.
+    __syncthreads();
+    {
+      float* out = p.dw + (int64_t)t.e * p.N * p.K;
+      constexpr int kRowPad = 160;  // floats per scratch row
+      const int free_stage = st == 0 ? kWgStages - 1 : st - 1;
+      __attribute__((address_space(3))) float* scr =
+          (__attribute__((address_space(3))) float*)&lds[free_stage][wave * 8 * kRowPad * 4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int pass = 0; pass < 8; ++pass) {
+        const int i = pass / 4, q = pass % 4;
+        // lane (l32, h) holds rows i*32 + 8q + 4h + (0..3) of columns j*32 + l32
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int k = t.k0 + wk * 64 + j * 32 + l32;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = t.n0 + wn * 64 + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
-          if (n < p.N && k < p.K) __builtin_nontemporal_store(acc[i][j][r], &out[(int64_t)n * p.K + k]);
+          for (int r = 0; r < 4; ++r) scr[(4 * h + r) * kRowPad + j * 32 + l32] = acc[i][j][4 * q + r];
+#pragma unroll
+        for (int rd = 0; rd < 4; ++rd) {
+          const int lr = 2 * rd + h;  // local row 0..7 of the pass
+          const f32x4_t v = *(const __attribute__((address_space(3))) f32x4_t*)&scr[lr * kRowPad + 4 * l32];
+          const int n = t.n0 + wn * 64 + i * 32 + 8 * q + lr;
+          const int k = t.k0 + wk * 128 + 4 * l32;
+          if (n < p.N && k < p.K) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(&out[(int64_t)n * p.K + k]));
         }
       }
+    }
     stored = true;
   }
   // drain the look-ahead loads (past the last tile they read zeros)
