@@ -347,7 +347,7 @@ moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (((uintptr_t)x | (uintptr_t)grad | (uintptr_t)dw) % 16 != 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "x, grad and dw must be 16-byte aligned");
-  const int64_t tiles = (int64_t)num_experts * ((n + 127) / 128) * ((k + 255) / 256);
+  const int64_t tiles = (int64_t)num_experts * ((n + 255) / 256) * ((k + 255) / 256);
   if (tiles >= (int64_t)INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "too many dW tiles");
   // x and grad are read through 32-bit buffer offsets
   if (num_tokens * x_ld * 2 >= (int64_t)0x80000000 || S * grad_ld * 2 >= (int64_t)0x80000000)

@@ -7,16 +7,21 @@
 // and Tests & Benchmarks (constant input, linearity, zero-padded tokens).
 //
 // Design for gfx950:
-//  * dW is cut into (expert, 128 x 256) tiles. A persistent grid (two
-//    workgroups per CU) walks them; each tile is accumulated over its
-//    expert's routing blocks on v_mfma_f32_32x32x16_bf16 and written once, so
-//    dW is overwritten (never accumulated into), empty experts get zeros,
-//    nothing is atomic and repeated calls give identical bits.
-//  * Slot rows of grad (128 columns, 256 B) and x (256 columns, 512 B) go
+//  * dW is cut into (expert, 256 x 256) tiles. A persistent grid (one
+//    workgroup of 8 waves per CU) walks them; each tile is accumulated over
+//    its expert's routing blocks on v_mfma_f32_32x32x16_bf16 and written
+//    once, so dW is overwritten (never accumulated into), empty experts get
+//    zeros, nothing is atomic and repeated calls give identical bits.
+//  * Slot rows of grad (256 columns) and x (256 columns), 512 bytes each, go
 //    straight from global memory into LDS with buffer_load ... lds,
 //    slot-major as they lie in memory, 32 slots per pipeline unit in three
-//    24 KB stages (two units ahead, across tile boundaries, one barrier per
-//    unit). Each wave computes 64 x 128 of the tile: 16 MFMAs per unit.
+//    32 KB stages (two units ahead, across tile boundaries, one barrier per
+//    unit). Each wave computes 64 x 128 of the tile: 16 MFMAs per unit. The
+//    tile size is what the operand traffic asks for: loading both operands
+//    costs (rows + columns) bytes per slot for rows x columns products, and
+//    256 x 256 measured faster than 128 x 256 at two workgroups per CU
+//    (5.7 against 6.5 ms on the E=256 gradient); larger tiles would need
+//    more accumulator registers than two waves per SIMD allow.
 //  * The contraction runs over slots, so an MFMA operand needs 8 consecutive
 //    slots of one column: gfx950's transposing LDS read (ds_read_b64_tr_b16)
 //    gathers them. Within each 16-lane group, lane j receives element j % 4
@@ -26,8 +31,10 @@
 //    slots. Two such reads make one operand.
 //  * A finished tile goes out through LDS: the MFMA output holds one column
 //    per lane, so each wave passes 8 rows at a time through a scratch area
-//    (the stage the next unit's loads will fill, free at that point) and
-//    writes whole 512-byte row pieces with 16-byte non-temporal stores.
+//    (the stage the next unit's loads will fill, free at that point; rows
+//    4..7 of a pass XOR their columns with 32 so both halves of a write hit
+//    distinct banks) and writes whole 512-byte row pieces with 16-byte
+//    non-temporal stores.
 //    Storing the MFMA output as it lies (one dword per lane, 128-byte row
 //    stretches) issues four times the store instructions; four adjacent
 //    columns per lane from swapped operands (32-byte stretches) measured
@@ -52,23 +59,25 @@ namespace moe {
 
 constexpr int kWgBM = 64;                    // routing block
 constexpr int kWgUM = 32;                    // slots per pipeline unit
-constexpr int kWgTN = 128;                   // dW rows (N) per tile
+constexpr int kWgTN = 256;                   // dW rows (N) per tile
 constexpr int kWgTK = 256;                   // dW columns (K) per tile
-constexpr int kWgGRowB = kWgTN * 2;          // 256 B: a slot's grad piece
+constexpr int kWgGRowB = kWgTN * 2;          // 512 B: a slot's grad piece
 constexpr int kWgXRowB = kWgTK * 2;          // 512 B: a slot's x piece
-constexpr int kWgGUnitB = kWgUM * kWgGRowB;  // 8 KB
+constexpr int kWgGUnitB = kWgUM * kWgGRowB;  // 16 KB
 constexpr int kWgXUnitB = kWgUM * kWgXRowB;  // 16 KB
 constexpr int kWgStageB = kWgGUnitB + kWgXUnitB;
 constexpr int kWgStages = 3;
-constexpr int kWgGLoads = kWgGUnitB / 1024 / 4;  // DMA instructions per wave per unit: 2 grad
-constexpr int kWgXLoads = kWgXUnitB / 1024 / 4;  //   + 4 x
+constexpr int kWgWaves = 8;
+constexpr int kWgThreads = kWgWaves * 64;
+constexpr int kWgGLoads = kWgGUnitB / 1024 / kWgWaves;  // DMA instructions per wave per unit: 2 grad
+constexpr int kWgXLoads = kWgXUnitB / 1024 / kWgWaves;  //   + 2 x (2 rows each)
 constexpr int kWgLoads = kWgGLoads + kWgXLoads;
-constexpr int kWgStores = 8 * 4;             // stores per lane per tile
-constexpr int kWgPerCU = 2;                  // resident workgroups per CU
+constexpr int kWgStores = 8 * 4;             // 16-byte stores per lane per tile
+constexpr int kWgPerCU = 1;                  // resident workgroups per CU
 constexpr int kWgMaxExperts = 1024;
 constexpr int kWgGroupN = 8;                 // N tiles per group of the tile order
 constexpr uint32_t kWgOOB = 0x80000000u;     // buffer offset past x and grad (each below 2 GB): reads 0
-static_assert(kWgGLoads == 2 && kWgXLoads == 4, "each wave loads the same 8 slot rows of both parts");
+static_assert(kWgGLoads == 2 && kWgXLoads == 2, "each wave loads the same 4 slot rows of both parts");
 
 typedef __attribute__((address_space(3))) uint8_t wg_lds_u8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short wg_s16x4_t;
@@ -85,14 +94,14 @@ __device__ __forceinline__ void wg_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t v
                :: "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc) : "m0");
 }
 
-typedef __attribute__((__vector_size__(8 * sizeof(int)))) int wg_i32x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int wg_i32x4_t;
 
-// 8 consecutive int32 at byte `off` of buffer `rsrc` through the scalar
+// 4 consecutive int32 at byte `off` of buffer `rsrc` through the scalar
 // cache (a read). Asynchronous: the result must not be used before an
 // lgkmcnt(0) wait that lists it (wg_wait_barrier).
-__device__ __forceinline__ wg_i32x8_t wg_scalar_ids8(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
-  wg_i32x8_t v;
-  asm volatile("s_buffer_load_dwordx8 %0, %1, %2"
+__device__ __forceinline__ wg_i32x4_t wg_scalar_ids4(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+  wg_i32x4_t v;
+  asm volatile("s_buffer_load_dwordx4 %0, %1, %2"
                : "=s"(v) : "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(off)));
   return v;
 }
@@ -101,7 +110,7 @@ __device__ __forceinline__ wg_i32x8_t wg_scalar_ids8(__amdgpu_buffer_rsrc_t rsrc
 // flight and every LDS and scalar-memory operation is done, then barrier;
 // `ids` (a prefetched scalar load) is final from here on.
 template <int N>
-__device__ __forceinline__ void wg_wait_barrier(wg_i32x8_t& ids) {
+__device__ __forceinline__ void wg_wait_barrier(wg_i32x4_t& ids) {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%1) lgkmcnt(0)\n\ts_barrier" : "+s"(ids) : "n"(N) : "memory");
 }
@@ -133,7 +142,7 @@ struct WgTile {
   int e, n0, k0, b0, b1;
 };
 
-__global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
+__global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams p) {
   // three stages of [grad unit | x unit], slot-major
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kWgStages][kWgStageB];
   __shared__ int32_t s_start[kWgMaxExperts + 1];  // first block of expert e (s_start[E] = end)
@@ -146,9 +155,9 @@ __global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
   // ---- expert block ranges: experts (lo, hi] start at every block b where
   //      the expert id changes (lo = previous id, hi = this id, or E for the
   //      first sentinel); experts past the last boundary start at max_blocks
-  for (int e = tid; e <= p.E; e += 256) s_start[e] = p.max_blocks;
+  for (int e = tid; e <= p.E; e += kWgThreads) s_start[e] = p.max_blocks;
   __syncthreads();
-  for (int b = tid; b < p.max_blocks; b += 256) {
+  for (int b = tid; b < p.max_blocks; b += kWgThreads) {
     const int cur = p.expert_ids[b];
     const int prev = b > 0 ? p.expert_ids[b - 1] : -1;
     const int hi = (cur < 0 || cur > p.E) ? p.E : cur;
@@ -198,20 +207,17 @@ __global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
 
   // ---- loader: walks the same tiles' units kWgStages - 1 units ahead of the
   //      computation. Unit u of a tile is slots [32u, 32u + 32) of its block
-  //      list; wave w loads slot rows 8w .. 8w + 7 of both parts (grad: two
-  //      instructions of 4 rows x 16 lanes, x: four of 2 rows x 32 lanes).
+  //      list; wave w loads slot rows 4w .. 4w + 3 of both parts (two
+  //      instructions of 2 rows x 32 lanes each).
   //      Past the last tile it issues loads that read zeros, so every unit
   //      costs the same number of loads.
   // The 16-byte unit each lane fetches, as a byte offset within the row
   // piece (the LDS side is lane order, the global side the swizzled unit):
-  // grad rows have row % 4 = lane / 16; x load i has row % 4 = 2 (i % 2) + lane / 32.
-  const uint32_t g_col = (uint32_t)wg_swz(lane / 16, lane % 16) * 16;
+  // load i of either part has row % 4 = 2 (i % 2) + lane / 32.
   const uint32_t x_col0 = (uint32_t)wg_swz(lane / 32, lane % 32) * 16;
   const uint32_t x_col1 = (uint32_t)wg_swz(2 + lane / 32, lane % 32) * 16;
-  // all-ones masks of the lanes that take the second, third and fourth row
-  // of a grad load and the second row of an x load (selects by bit logic,
-  // one VALU operation each)
-  const uint32_t gm1 = lane / 16 == 1 ? ~0u : 0u, gm2 = lane / 16 == 2 ? ~0u : 0u, gm3 = lane / 16 == 3 ? ~0u : 0u;
+  // all-ones mask of the lanes that take the second row of a load (a
+  // select by bit logic, one VALU operation)
   const uint32_t xm1 = lane >= 32 ? ~0u : 0u;
   auto pick = [](uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); };
 
@@ -229,12 +235,12 @@ __global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
     }
   };
   auto ld_ids = [&]() {
-    wg_i32x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (ld_live) v = wg_scalar_ids8(sorted_rsrc, (uint32_t)((ld.b0 * kWgBM + ld_u * kWgUM + wave * 8) * 4));
+    wg_i32x4_t v = {0, 0, 0, 0};
+    if (ld_live) v = wg_scalar_ids4(sorted_rsrc, (uint32_t)((ld.b0 * kWgBM + ld_u * kWgUM + wave * 4) * 4));
     return v;
   };
   ld_skip_empty();
-  wg_i32x8_t ids = ld_ids();
+  wg_i32x4_t ids = ld_ids();
   wg_wait_barrier<0>(ids);
 
   auto issue_next = [&](int stage) {
@@ -244,9 +250,9 @@ __global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
     // the buffers: s * row + kWgOOB stays below 2^32)
     const uint32_t g_base = ld_live ? (uint32_t)ld.n0 * 2 : kWgOOB;
     const uint32_t x_base = ld_live ? (uint32_t)ld.k0 * 2 : kWgOOB;
-    uint32_t go[8], xo[8];
+    uint32_t go[4], xo[4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const uint32_t s = (uint32_t)ids[r];
       const uint64_t prod = ((uint64_t)__umulhi(s, p.topk_magic) << 32) | (s * p.topk_magic);
       const uint32_t xrow = (uint32_t)(prod >> p.topk_shift);
@@ -255,16 +261,13 @@ __global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
     }
     const uint32_t dst = lds_base + (uint32_t)(stage * kWgStageB);
 #pragma unroll
-    for (int i = 0; i < kWgGLoads; ++i) {
-      const uint32_t row = pick(gm3, go[4 * i + 3], pick(gm2, go[4 * i + 2], pick(gm1, go[4 * i + 1], go[4 * i])));
-      wg_dma16(g_rsrc, row + g_col, dst + (uint32_t)((wave * kWgGLoads + i) * 1024));
-    }
+    for (int i = 0; i < kWgGLoads; ++i)
+      wg_dma16(g_rsrc, pick(xm1, go[2 * i + 1], go[2 * i]) + (i % 2 ? x_col1 : x_col0),
+               dst + (uint32_t)((wave * kWgGLoads + i) * 1024));
 #pragma unroll
-    for (int i = 0; i < kWgXLoads; ++i) {
-      const uint32_t row = pick(xm1, xo[2 * i + 1], xo[2 * i]);
-      wg_dma16(x_rsrc, row + (i % 2 ? x_col1 : x_col0),
+    for (int i = 0; i < kWgXLoads; ++i)
+      wg_dma16(x_rsrc, pick(xm1, xo[2 * i + 1], xo[2 * i]) + (i % 2 ? x_col1 : x_col0),
                dst + (uint32_t)(kWgGUnitB + (wave * kWgXLoads + i) * 1024));
-    }
     if (ld_live) {
       ++ld_u;
       ld_skip_empty();
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
     }
   };
 
-  // waves 2 x 2: wave (wn, wk) computes dW rows n0 + wn*64 .. + 63 and
+  // waves 4 x 2: wave (wn, wk) computes dW rows n0 + wn*64 .. + 63 and
   // columns k0 + wk*128 .. + 127
   const int wn = wave / 2, wk = wave % 2;
   f32x16_t acc[2][4];  // [n sub-tile][k sub-tile]
@@ -335,28 +338,27 @@ __global__ __launch_bounds__(256, kWgPerCU) void wgrad_kernel(WgradParams p) {
     }
     // store the tile through LDS: the stage the next unit's loads will go
     // to is free once every wave is past its last contraction. Each wave
-    // passes 8 rows at a time through its own 5 KB of it (rows padded to
-    // 640 bytes, so the two row halves of a write land on distinct banks)
-    // and writes whole 512-byte row pieces with 16-byte stores.
+    // passes 8 rows at a time through its own 4 KB of it and writes whole
+    // 512-byte row pieces with 16-byte stores.
     __syncthreads();
     {
       float* out = p.dw + (int64_t)t.e * p.N * p.K;
-      constexpr int kRowPad = 160;  // floats per scratch row
       const int free_stage = st == 0 ? kWgStages - 1 : st - 1;
       __attribute__((address_space(3))) float* scr =
-          (__attribute__((address_space(3))) float*)&lds[free_stage][wave * 8 * kRowPad * 4];
+          (__attribute__((address_space(3))) float*)&lds[free_stage][wave * 8 * 512];
 #pragma unroll
       for (int pass = 0; pass < 8; ++pass) {
         const int i = pass / 4, q = pass % 4;
-        // lane (l32, h) holds rows i*32 + 8q + 4h + (0..3) of columns j*32 + l32
+        // lane (l32, h) holds rows i*32 + 8q + 4h + (0..3) of columns j*32 + l32;
+        // rows 4..7 of the scratch are stored with columns XOR 32 (distinct banks)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) scr[(4 * h + r) * kRowPad + j * 32 + l32] = acc[i][j][4 * q + r];
+          for (int r = 0; r < 4; ++r) scr[(4 * h + r) * 128 + ((j * 32 + l32) ^ (32 * h))] = acc[i][j][4 * q + r];
 #pragma unroll
         for (int rd = 0; rd < 4; ++rd) {
           const int lr = 2 * rd + h;  // local row 0..7 of the pass
-          const f32x4_t v = *(const __attribute__((address_space(3))) f32x4_t*)&scr[lr * kRowPad + 4 * l32];
+          const f32x4_t v = *(const __attribute__((address_space(3))) f32x4_t*)&scr[lr * 128 + ((4 * l32) ^ (32 * (lr / 4)))];
           const int n = t.n0 + wn * 64 + i * 32 + 8 * q + lr;
           const int k = t.k0 + wk * 128 + 4 * l32;
           if (n < p.N && k < p.K) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(&out[(int64_t)n * p.K + k]));
@@ -393,7 +395,7 @@ hipError_t launch_wgrad(const WgradParams& p_in, hipStream_t stream) {
   // stretch of tiles per XCD per round)
   int64_t grid = (int64_t)cus * kWgPerCU;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL(wgrad_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(wgrad_kernel, dim3((uint32_t)grid), dim3(kWgThreads), 0, stream, p);
   return hipGetLastError();
 }
 
