@@ -11,16 +11,19 @@
 // bucketing and warmup", Description.
 //
 // Design for gfx950:
-//  * One workgroup of 8 waves (2 along M x 4 along N) per (routing block of
-//    128 rows, N tile). The routing block is the M tile, so no tile straddles
-//    two experts, and each weight tile loaded serves 128 rows. A wave whose
-//    64 rows hold only padding skips its MFMAs (real rows come first in a
-//    block), so the padding computed is below 64 rows per expert.
-//  * Each 64-wide K step moves 16 KB of activations and 16 KB of weight codes
+//  * One workgroup of 4 waves (each 64 rows x 32*NT columns) per (routing
+//    block of 64 rows, N tile); two workgroups per CU. The routing block is
+//    the M tile, so no tile straddles two experts. A wave whose columns lie
+//    past N, or whose 64 rows hold only padding (real rows come first in a
+//    block), skips its MFMAs but still loads its share and joins every
+//    barrier.
+//  * Each 64-wide K step moves 8 KB of activations and 16 KB of weight codes
 //    (512 rows of E2M1, 256 of E4M3) or 32 KB of bf16 weights straight from
 //    global memory into LDS with buffer_load ... lds (no registers; rows past
 //    N, PAD rows and the K tail read as zeros through the buffer bounds),
-//    four stages deep (three for bf16), one barrier per step.
+//    three stages deep, one barrier per step. The E8M0 bytes of a lane's
+//    weight rows arrive in registers with byte loads of the same step (a
+//    variant that brought them by DMA into LDS measured no faster).
 //  * K order inside a step: lane half h of a wave handles K elements
 //    [32h, 32h + 32) and MFMA substep ks takes [32h + 8ks, 32h + 8ks + 8).
 //    Any order common to both operands gives the same dot product; this one
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   constexpr int NWAVES = kWavesM * kWavesN;
   constexpr int UW = RB / 16;                       // 16-byte units per weight row per step
   constexpr int KPU = 64 / UW;                      // K elements per weight unit
-  constexpr int A_BYTES = kBM * 128;                // 16 KB
+  constexpr int A_BYTES = kBM * 128;                // 8 KB
   constexpr int W_BYTES = BN * RB;                  // 16 KB (32 KB for bf16)
   constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // one 1 KB wave-wide load per instruction
   constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;
