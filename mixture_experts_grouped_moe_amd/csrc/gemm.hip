@@ -53,7 +53,7 @@ namespace moe {
 
 template <int WDT> struct WTraits;
 template <> struct WTraits<W_E2M1> { static constexpr int kRowBytes = 32, kNT = 4, kStages = 3; };
-template <> struct WTraits<W_E4M3> { static constexpr int kRowBytes = 64, kNT = 2, kStages = 3; };
+template <> struct WTraits<W_E4M3> { static constexpr int kRowBytes = 64, kNT = 4, kStages = 2; };
 template <> struct WTraits<W_BF16> { static constexpr int kRowBytes = 128, kNT = 2, kStages = 3; };
 
 constexpr int kWavesM = 1;                        // waves along M
@@ -174,10 +174,12 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
   static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
 
-  // LDS: STAGES x [A tile | weight tile], then the block's slot list
+  // LDS: STAGES x [A tile | weight tile] (E4M3: two 40 KB stages, so two
+  // workgroups fill a CU's 160 KB exactly; the block's slot list is read from
+  // global memory until the epilogue, which keeps it in stage 0)
   constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][STAGE_BYTES];
-  __shared__ int32_t s_slot[kBM];
+  static_assert(kMinBlocks * STAGES * STAGE_BYTES <= 160 * 1024 || WDT == W_BF16, "two workgroups per CU");
 
   const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
   const int b = L % p.max_blocks;
@@ -191,15 +193,14 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   const int wm = wave / kWavesN, wn = wave % kWavesN;              // this wave's rows / columns of the tile
   const int l32 = lane % 32, h = lane / 32;
 
-  if (tid < kBM) s_slot[tid] = p.sorted[(int64_t)b * kBM + tid];
-  __syncthreads();
+  const int32_t* blk_slots = p.sorted + (int64_t)b * kBM;  // the block's slot ids
 
   // A wave computes nothing when its 64 rows hold only PAD positions (with
   // moe_align's routing the real rows of a block come first, so this skips
   // the padding past the last real row in 64-row steps) or when all its
   // columns lie past N; it still loads its share of the tiles and joins
   // every barrier.
-  const bool rows_live = __ballot(s_slot[wm * 64 + lane] < p.S) != 0;
+  const bool rows_live = __ballot(blk_slots[wm * 64 + lane] < p.S) != 0;
   const bool cols_live = tile_w_row<NT, SWIGLU>(wn * WN, tile_n, p.N) >= 0;
   const bool wave_live = rows_live && cols_live;
 
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
     const int q = (wave * A_LOADS + i) * 64 + lane;  // physical unit in the stage
     const int row = q / 8, pu = q % 8;
     const int u = swz<8>(row, pu);
-    const int s = s_slot[row];
+    const int s = blk_slots[row];
     a_k[i] = u * 8;
     a_off[i] = s < p.S ? (uint32_t)((int64_t)(s / p.a_row_div) * p.a_ld * 2 + u * 16) : kOOB;
   }
@@ -390,8 +391,13 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
       if (wave_live) compute(st, Two{});
     });
   }
-  // drain the look-ahead loads (all of them read as zeros past the last step)
+  // drain the look-ahead loads (all of them read as zeros past the last step),
+  // then keep the slot list in stage 0 once every wave is done with it
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int32_t* s_slot = reinterpret_cast<int32_t*>(&lds[0][0]);
+  if (tid < kBM) s_slot[tid] = blk_slots[tid];
+  __syncthreads();
 
   // ---- epilogue: bias, SwiGLU, one bf16 rounding, store real rows only
   float bv[NT];
