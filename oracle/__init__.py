@@ -26,8 +26,11 @@ other than itself:
     wgrad.wgrad             pinned  (constant input, linearity, zero/PAD slots, Fraction brute force)
     layer.w4a16_layer       pinned  (composition of pinned functions; padded == unpadded)
     layout.pack_kblock      pinned  (per-element loop over the layout's index formula)
+    quant.mx_quantize_e4m3  pinned  (every code round-trips at a known shared exponent;
+                                     scale rule, ties, saturation, zero and clamped
+                                     blocks; torch's float8_e4m3fn cast in range)
 """
 
-from . import formats, bucket, align, gemm, wgrad, layer, layout  # noqa: F401
+from . import formats, bucket, align, gemm, wgrad, layer, layout, quant  # noqa: F401
 
-__all__ = ["formats", "bucket", "align", "gemm", "wgrad", "layer", "layout"]
+__all__ = ["formats", "bucket", "align", "gemm", "wgrad", "layer", "layout", "quant"]
