@@ -243,6 +243,26 @@ moe_status moe_packed_sizes(int32_t w_dtype, int64_t n, int64_t k, int64_t* w_un
                             int64_t* scale_bytes);
 
 /* ------------------------------------------------------------------------
+ * MXFP8 conversion of bf16 activations ([AIT] Summary and second review:
+ * moe_gemm_mxfp8 takes both operands as E4M3 codes with one E8M0 scale per
+ * 32 K-elements, a_scale and b_scale; the pages do not give the conversion,
+ * this is the OCP Microscaling v1.0 one). For every row r < rows and block
+ * b < k/32, with v = x[r][32b .. 32b+31]:
+ *   X = floor(log2(max |v|)) - 8, clamped to [-127, 127]; -127 if all zero
+ *   scales[r][b] = X + 127
+ *   q[r][32b + i] = E4M3 nearest to v_i / 2^X (ties to even, saturating at
+ *                   +-448, sign bit when v_i < 0)
+ * x (device) bf16 rows with stride x_ld elements; q (device) uint8 rows with
+ * stride q_ld bytes; scales (device) uint8 rows with stride scales_ld.
+ * Requirements: k % 32 == 0, k >= 32; x_ld >= k and a multiple of 8; q_ld >= k
+ * and a multiple of 16; scales_ld >= k / 32; x and q 16-byte aligned.
+ * Otherwise MOE_ERR_INVALID_ARGUMENT, nothing launched. Inputs are finite.
+ * ---------------------------------------------------------------------- */
+moe_status moe_quantize_mxfp8(const void* x, int64_t x_ld, int64_t rows, int64_t k,
+                              void* q, int64_t q_ld, uint8_t* scales, int64_t scales_ld,
+                              moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Top-k combine (the method's final step; [TRT] Description: the padded
  * rows are sliced off after the grouped GEMMs).
  *   y[t][n] = bf16( sum_{j < top_k, ascending} topk_w[t][j] * C[t*top_k + j][n] )

@@ -78,6 +78,7 @@ def _load():
         "moe_align": (i32, [vp, i64, i32, i32, i32, vp, vp, vp, i64, vp]),
         "moe_grouped_gemm": (i32, [ctypes.POINTER(MoeGemmArgs), vp]),
         "moe_combine": (i32, [vp, i64, vp, i64, i32, i64, vp, i64, vp]),
+        "moe_quantize_mxfp8": (i32, [vp, i64, i64, i64, vp, i64, vp, i64, vp]),
         "moe_wgrad": (i32, [vp, i64, vp, i64, vp, vp, vp, i64, i32, i32, i64, i64, i32, i64, vp, vp]),
         "moe_pack_weights": (i32, [i32, i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp, vp]),
         "moe_packed_sizes": (i32, [i32, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
@@ -348,6 +349,24 @@ def moe_combine(c, topk_w, top_k, num_tokens=None, out=None, stream=None):
     _check(lib.moe_combine(_ptr(c), c.stride(0), _ptr(topk_w), T, int(top_k), N,
                            _ptr(out), out.stride(0), _stream(stream)))
     return out
+
+
+def moe_quantize_mxfp8(x, out=None, out_scales=None, stream=None):
+    """bf16 [R, K] -> (E4M3 codes uint8 [R, K], E8M0 scales uint8 [R, K / 32]):
+    the OCP MX conversion, one scale per 32 consecutive K elements."""
+    _need(x, "x", torch.bfloat16, 2)
+    R, K = x.shape
+    if out is None:
+        out = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+    if out_scales is None:
+        out_scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    _need(out, "out", torch.uint8, 2)
+    _need(out_scales, "out_scales", torch.uint8, 2)
+    if out.shape[0] < R or out_scales.shape[0] < R:
+        raise ValueError("out / out_scales have fewer rows than x")
+    _check(lib.moe_quantize_mxfp8(_ptr(x), x.stride(0), R, K, _ptr(out), out.stride(0), _ptr(out_scales),
+                                  out_scales.stride(0), _stream(stream)))
+    return out, out_scales
 
 
 def moe_wgrad(x, grad, routing, num_tokens, top_k, num_experts, out=None, stream=None):

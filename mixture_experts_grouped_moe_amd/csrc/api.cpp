@@ -319,6 +319,24 @@ moe_status moe_combine(const void* c, int64_t c_ld, const float* topk_w, int64_t
                     "moe_combine launch");
 }
 
+moe_status moe_quantize_mxfp8(const void* x, int64_t x_ld, int64_t rows, int64_t k, void* q, int64_t q_ld,
+                              uint8_t* scales, int64_t scales_ld, moe_stream_t stream) {
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "rows < 0");
+  if (k < 32 || k % 32 != 0 || k >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "k must be a positive multiple of 32");
+  if (x_ld < k || x_ld % 8 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "x_ld must be >= k and a multiple of 8");
+  if (q_ld < k || q_ld % 16 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "q_ld must be >= k and a multiple of 16");
+  if (scales_ld < k / 32) return fail(MOE_ERR_INVALID_ARGUMENT, "scales_ld must be >= k / 32");
+  if (rows > 0 && (x == nullptr || q == nullptr || scales == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (((uintptr_t)x | (uintptr_t)q) % 16 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "x and q must be 16-byte aligned");
+  if (rows > INT64_MAX / k) return fail(MOE_ERR_INVALID_ARGUMENT, "rows * k overflows");
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_quant_mxfp8(static_cast<const uint16_t*>(x), x_ld, rows, k, static_cast<uint8_t*>(q),
+                                            q_ld, scales, scales_ld, (hipStream_t)stream),
+                    "moe_quantize_mxfp8 launch");
+}
+
 moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad_ld,
                      const int32_t* sorted_token_ids, const int32_t* expert_ids,
                      const int32_t* num_tokens_post_pad, int64_t num_tokens, int32_t top_k,

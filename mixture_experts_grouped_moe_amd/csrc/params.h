@@ -62,6 +62,8 @@ hipError_t launch_wgrad(const WgradParams& p, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* w, int64_t w_stride_e, int64_t w_ld, const uint8_t* ws,
                        int64_t ws_stride_e, int64_t ws_ld, int32_t E, int32_t N, int32_t K, int32_t row_bytes,
                        uint8_t* w_out, uint8_t* ws_out, hipStream_t stream);
+hipError_t launch_quant_mxfp8(const uint16_t* x, int64_t x_ld, int64_t rows, int64_t k, uint8_t* q, int64_t q_ld,
+                              uint8_t* s, int64_t s_ld, hipStream_t stream);
 int gemm_block_m_large();
 int gemm_block_m_decode();
 int wgrad_block_m();

@@ -39,7 +39,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol():
     syms = _declared_symbols()
-    assert len(syms) == 15, syms
+    assert len(syms) == 16, syms
     for name in syms:
         assert hasattr(L, name), name
 
@@ -204,6 +204,25 @@ def test_pack_weights_rejects(no_device):
     assert call(wo=FAKE) == INVALID            # output overlaps the input
     assert call(w=ctypes.c_void_p(0x100008)) == INVALID
     assert call(wd=moe.MOE_FP32) == INVALID
+
+
+def test_quantize_mxfp8_rejects(no_device):
+    qz = L.moe_quantize_mxfp8
+    Q = ctypes.c_void_p(0x10000000)
+
+    def call(x=FAKE, x_ld=256, rows=10, k=256, q=Q, q_ld=256, s=FAKE, s_ld=8):
+        return qz(x, x_ld, rows, k, q, q_ld, s, s_ld, None)
+
+    assert call(rows=-1) == INVALID
+    assert call(k=100) == INVALID              # not a multiple of 32
+    assert call(k=0) == INVALID
+    assert call(x_ld=128) == INVALID           # row shorter than k
+    assert call(x_ld=260) == INVALID           # not a multiple of 8 elements
+    assert call(q_ld=264) == INVALID           # not a multiple of 16 bytes
+    assert call(s_ld=7) == INVALID             # fewer than k / 32 scales
+    assert call(x=None) == INVALID
+    assert call(s=None) == INVALID
+    assert call(q=ctypes.c_void_p(0x10000008)) == INVALID  # not 16-byte aligned
 
 
 def test_combine_rejects(no_device):
