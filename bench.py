@@ -1,6 +1,6 @@
 """Benchmark of the MoE expert-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|w4a16|mxfp8|wgrad]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|w4a16|mxfp8|mxfp8a|wgrad]
 
 Prints one JSON line. The default workload is the bf16 decode MoE
 (E=128, N=1856, K=2048, top-6) at the MTP6 verify token counts
@@ -8,8 +8,9 @@ M = 1, 7, 14, 21, 28: one step runs, for each M, moe_align -> decode grouped
 GEMM -> moe_combine on a fresh routing (a seeded set of routings is cycled).
 `value` is the step's algorithmic HBM bytes over its time (GB/s); the
 per-call microseconds are reported beside it. The other workloads (the
-gpt-oss-shaped W4A16 MXFP4 layer, the 256-expert MXFP8 grouped GEMM, the
-weight gradient) are selected with --workload and report TFLOP/s.
+gpt-oss-shaped W4A16 MXFP4 layer, the 256-expert MXFP8 grouped GEMM with
+bf16 or MXFP8 activations, the weight gradient) are selected with --workload
+and report TFLOP/s.
 
 Inputs are synthetic (seeded), generated on the device before the timed
 region. Steps are replayed from HIP graphs captured once per routing variant.
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode", choices=["decode", "w4a16", "mxfp8", "wgrad", "copy"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "w4a16", "mxfp8", "mxfp8a", "wgrad", "copy"])
     ap.add_argument("--variants", type=int, default=4, help="routing variants cycled across steps")
     ap.add_argument("--launch-reps", type=int, default=10,
                     help="back-to-back launches per event pair when timing the dominant kernel")
@@ -56,7 +57,8 @@ def parse():
 
 
 # sources whose change can change a workload's dominant kernel
-KERNEL_SOURCES = {"decode": ["decode.hip"], "w4a16": ["gemm.hip"], "mxfp8": ["gemm.hip"],
+KERNEL_SOURCES = {"decode": ["decode.hip"], "w4a16": ["gemm.hip", "gemm_util.h"],
+                  "mxfp8": ["gemm.hip", "gemm_util.h"], "mxfp8a": ["gemm_f8.hip", "gemm_util.h"],
                   "wgrad": ["wgrad.hip"], "copy": []}
 
 
@@ -159,7 +161,7 @@ class Workload:
         raise NotImplementedError
 
 
-LAYOUT = {"decode": "rows", "w4a16": "kblock", "mxfp8": "kblock"}  # resolved --layout per workload
+LAYOUT = {"decode": "rows", "w4a16": "kblock", "mxfp8": "kblock", "mxfp8a": "kblock"}  # resolved --layout per workload
 
 
 def _gemm_weights(moe, name, w, w_dtype, w_scale):
@@ -413,6 +415,76 @@ class MXFP8(Workload):
         return items, run, "TFLOP/s"
 
 
+class MXFP8A(MXFP8):
+    """The MXFP8 workload with MXFP8 activations: each step converts the bf16
+    activations (E4M3 codes + E8M0 per 32 along K) and runs the both-operands
+    MXFP8 grouped GEMM on the scaled fp8 MFMA."""
+    name = "mxfp8a"
+    cpu_sample_desc = ("MXFP8 conversion of the activation rows and grouped GEMM over all slots of the "
+                       "median-load and the top-load expert")
+    dominant = "moe_gemm_f8_kernel"
+    bound = "hbm"
+
+    def __init__(self, torch, dev, variants, bias=False):
+        super().__init__(torch, dev, variants, bias)
+        moe = self.moe
+        self.bm = moe.moe_gemm_block_m("e4m3", self.T, moe.MOE_E4M3)
+        self.routing = _routing_buffers(torch, self.T, self.k, self.E, self.bm, dev)
+        self.q = torch.empty((self.T, self.K), dtype=torch.uint8, device=dev)
+        self.qs = torch.empty((self.T, self.K // 32), dtype=torch.uint8, device=dev)
+        moe.moe_align(self.d["ids"], self.E, self.bm, out=self.routing)
+        moe.moe_quantize_mxfp8(self.d["x"], out=self.q, out_scales=self.qs)
+
+    def gemm_bytes(self):
+        w = self.touched * self.N * self.K * (1 + 1 / 32)
+        return int(w + self.T * self.K * (1 + 1 / 32) + self.T * self.k * self.N * 2)
+
+    def step_bytes(self, v):
+        return self.gemm_bytes() + self.T * self.K * 2  # + the conversion's bf16 reads
+
+    def _gemm(self):
+        return self.moe.moe_grouped_gemm(self.q, self.wg, "e4m3", self.routing, self.T, self.k, self.E, self.k,
+                                         w_scale=self.sg, bias=self.d["bias"], out=self.C, a_scale=self.qs)
+
+    def step(self, v):
+        self.moe.moe_align(self.d["ids"], self.E, self.bm, out=self.routing)
+        self.moe.moe_quantize_mxfp8(self.d["x"], out=self.q, out_scales=self.qs)
+        self._gemm()
+
+    def cpu_sample(self):
+        import numpy as np
+        import synth
+        from oracle import gemm as ogemm
+        from oracle import quant as oquant
+        d = self.d
+        ids = synth.bits(d["ids"])
+        flat = ids.reshape(-1)
+        x = d["x"]
+        w, ws = LazyRows(d["w"]), LazyRows(d["w_scale"])
+        counts = np.bincount(flat, minlength=self.E)
+        order = np.argsort(counts)
+        experts = [int(order[len(order) // 2]), int(order[-1])]
+        items = []
+        for e in experts:
+            slots = np.nonzero(flat == e)[0]
+            rows = np.unique(slots // self.k)
+            items.append((slots, rows, x[torch_index(rows)].float().cpu().double().numpy()))
+
+        def run(item):
+            slots, rows, xr = item
+            q = np.zeros((self.T, self.K), dtype=np.uint8)
+            s = np.zeros((self.T, self.K // 32), dtype=np.uint8)
+            q[rows], s[rows] = oquant.mx_quantize_e4m3(xr)
+            ogemm.grouped_gemm(q, self.k, w, "e4m3", ws, ids, self.E, a_dtype="e4m3", a_scale=s, slots=slots)
+            return 2 * len(slots) * self.N * self.K
+        return items, run, "TFLOP/s"
+
+
+def torch_index(rows):
+    import torch
+    return torch.from_numpy(rows.astype("int64"))
+
+
 class Wgrad(Workload):
     name = "wgrad"
     cpu_sample_desc = "dW of experts 0, 128 and 255"
@@ -511,11 +583,13 @@ class Copy(Workload):
         return [0], run, "GB/s"
 
 
-WORKLOADS = {"decode": Decode, "w4a16": W4A16, "mxfp8": MXFP8, "wgrad": Wgrad, "copy": Copy}
+WORKLOADS = {"decode": Decode, "w4a16": W4A16, "mxfp8": MXFP8, "mxfp8a": MXFP8A, "wgrad": Wgrad, "copy": Copy}
 CONFIG_NAMES = {
     "decode": "decode bf16 MoE, E=128 N=1856 K=2048 top-6, M in {1,7,14,21,28}",
     "w4a16": "W4A16 MXFP4 MoE layer (gpt-oss-shaped), E=128 top-4 H=2880, gate+up 5760 -> SwiGLU -> down 2880, T~U[6554,8192] bucketed",
     "mxfp8": "MXFP8 grouped GEMM, E=256 top-8 K=7168 N=4096 T=4096, Zipf(1.1) routing with 16 empty experts",
+    "mxfp8a": "MXFP8 grouped GEMM with MXFP8 activations (bf16 converted each step), E=256 top-8 K=7168 N=4096 "
+              "T=4096, Zipf(1.1) routing with 16 empty experts",
     "wgrad": "moe_wgrad, E=256 top-8 T=16384, x [T,7168], grad [8T,2048], fp32 dW [256,2048,7168]",
     "copy": "device-to-device copy of 1 GiB (counter calibration)",
 }
@@ -642,8 +716,11 @@ def main():
         unit_v = "TFLOP/s"
         extra = wl.extra(None)
         extra["mfma_frac_step_bf16"] = round(value / PEAK_BF16_TFLOPS, 4)
+        if args.workload == "mxfp8a":
+            extra["mfma_frac_step_fp8"] = round(value / (2 * PEAK_BF16_TFLOPS), 4)
         extra["hbm_GBps_step"] = round(step_bytes / dt / 1e9, 1)
         dtype = {"w4a16": "bf16 x e2m1 (bf16 MFMA)", "mxfp8": "bf16 x e4m3 (bf16 MFMA)",
+                 "mxfp8a": "e4m3 x e4m3, E8M0 per 32 (scaled fp8 MFMA)",
                  "wgrad": "bf16 (bf16 MFMA, fp32 out)"}[args.workload]
 
     cpu = None

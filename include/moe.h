@@ -163,8 +163,12 @@ moe_status moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t top_k,
  *
  * For every block b with e = expert_ids[b] >= 0 and every position r of it
  * with slot s = sorted_token_ids[b * block_m + r] < PAD:
- *   pre[n] = sum_k A[s / a_row_div][k] * W_hat[e][n][k] + bias[e][n]
+ *   pre[n] = sum_k A_hat[s / a_row_div][k] * W_hat[e][n][k] + bias[e][n]
  *   W_hat[e][n][k] = dec(W[e][n][k]) * 2^(w_scale[e][n][k / 32] - 127)
+ *   A_hat = A (bf16), or dec(A[r][k]) * 2^(a_scale[r][k / 32] - 127) for
+ *   MOE_E4M3 activations (both operands MXFP8: the kernel feeds codes and
+ *   scale bytes to gfx950's scaled fp8 MFMA, the a_scale / b_scale form of
+ *   [AIT]'s kernel; moe_quantize_mxfp8 makes such activations)
  *   C[s][:] = bf16(pre) (MOE_EPILOGUE_NONE) or bf16(swiglu(pre)) (width N/2)
  * accumulated in fp32, rounded once to bf16 (nearest-even) at the store.
  * Rows of C for PAD positions and unrouted slots are not written.
@@ -178,11 +182,15 @@ typedef struct {
   int64_t n;              /* N: weight rows per expert (pre-epilogue width) */
   int64_t k;              /* K: contraction length */
 
-  int32_t a_dtype;        /* MOE_BF16 */
+  int32_t a_dtype;        /* MOE_BF16, or MOE_E4M3 (MXFP8 activations, with
+                             MOE_E4M3 weights only) */
   int32_t a_row_div;      /* slot s reads A row s / a_row_div: top_k (A = token
                              rows) or 1 (A = slot rows, e.g. the second GEMM) */
   const void* a;          /* (device) A rows, row r at a + r * a_ld elements */
   int64_t a_ld;           /* >= k */
+  const uint8_t* a_scale; /* (device) MOE_E4M3 activations: E8M0 [rows][k/32],
+                             row r at a_scale + r * a_scale_ld; else ignored */
+  int64_t a_scale_ld;     /* >= k / 32 */
 
   int32_t w_dtype;        /* MOE_BF16, MOE_E4M3 or MOE_E2M1X2 */
   int32_t w_layout;       /* moe_layout of w and w_scale */
@@ -214,6 +222,10 @@ typedef struct {
  * a_row_div in {1, top_k}; 16-byte aligned a and w rows (a_ld a multiple of
  * 8; w_ld a multiple of 16 bytes); c_ld >= the output width; A, one
  * expert's weights and one expert's scales each span less than 2 GB.
+ * MOE_E4M3 activations: w_dtype MOE_E4M3, a_ld a multiple of 16, a_scale
+ * non-null with a_scale_ld >= k / 32, the scales under 2 GB; every token
+ * count runs the large-M kernel (no decode variant), so block_m is the
+ * large-M one for every num_tokens. Other combinations: MOE_ERR_UNSUPPORTED.
  * No workspace. */
 moe_status moe_grouped_gemm(const moe_gemm_args* args, moe_stream_t stream);
 

@@ -19,6 +19,7 @@ __all__ = [
     "moe_bucket_round_up", "moe_bucket_enumerate", "moe_padding_supported",
     "moe_align_max_blocks", "moe_gemm_block_m", "moe_wgrad_block_m", "moe_decode_max_tokens",
     "moe_align", "moe_grouped_gemm", "moe_grouped_gemm_prepare", "moe_combine", "moe_wgrad",
+    "moe_quantize_mxfp8",
     "moe_pack_weights", "moe_packed_sizes", "PackedWeights", "MOE_LAYOUT_ROWS", "MOE_LAYOUT_KBLOCK",
     "moe_w4a16_layer",
     "LIB_PATH",
@@ -47,6 +48,7 @@ class MoeGemmArgs(ctypes.Structure):
         ("n", ctypes.c_int64), ("k", ctypes.c_int64),
         ("a_dtype", ctypes.c_int32), ("a_row_div", ctypes.c_int32),
         ("a", ctypes.c_void_p), ("a_ld", ctypes.c_int64),
+        ("a_scale", ctypes.c_void_p), ("a_scale_ld", ctypes.c_int64),
         ("w_dtype", ctypes.c_int32), ("w_layout", ctypes.c_int32), ("w", ctypes.c_void_p),
         ("w_stride_e", ctypes.c_int64), ("w_ld", ctypes.c_int64),
         ("w_scale", ctypes.c_void_p), ("w_scale_stride_e", ctypes.c_int64), ("w_scale_ld", ctypes.c_int64),
@@ -246,21 +248,23 @@ def moe_align(topk_ids, num_experts, block_m, num_tokens=None, out=None, stream=
 
 def moe_grouped_gemm(a, w, w_dtype, routing, num_tokens, top_k, num_experts, a_row_div,
                      w_scale=None, bias=None, epilogue="none", out=None, block_m=None,
-                     stream=None):
+                     stream=None, a_scale=None):
     """See moe_grouped_gemm_prepare; this builds the call and runs it once."""
     call, out = moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_experts, a_row_div,
                                          w_scale=w_scale, bias=bias, epilogue=epilogue, out=out,
-                                         block_m=block_m, stream=stream)
+                                         block_m=block_m, stream=stream, a_scale=a_scale)
     call()
     return out
 
 
 def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_experts, a_row_div,
                              w_scale=None, bias=None, epilogue="none", out=None, block_m=None,
-                             stream=None):
+                             stream=None, a_scale=None):
     """Routed grouped GEMM: C[s] = epilogue(A[s // a_row_div] . W_hat[e]^T + bias[e]).
 
-    a: bf16 [rows, K]; w: [E, N, K] bf16 / uint8 E4M3 codes, or uint8 [E, N, K/2]
+    a: bf16 [rows, K], or uint8 E4M3 codes [rows, K] with a_scale uint8 E8M0
+    [rows, K/32] (MXFP8 activations, e.g. from moe_quantize_mxfp8; E4M3
+    weights only); w: [E, N, K] bf16 / uint8 E4M3 codes, or uint8 [E, N, K/2]
     packed E2M1; w_scale: uint8 E8M0 [E, N, K/32]; bias: bf16 [E, N] (any
     strides); routing: the (sorted_token_ids, expert_ids, num_tokens_post_pad)
     of moe_align with block_m = moe_gemm_block_m(w_dtype, num_tokens).
@@ -270,7 +274,19 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     loops and graph capture).
     """
     wd = _W_DTYPES[w_dtype]
-    _need(a, "a", torch.bfloat16, 2)
+    a_f8 = isinstance(a, torch.Tensor) and a.dtype == torch.uint8
+    if a_f8:
+        _need(a, "a", torch.uint8, 2)
+        _need(a_scale, "a_scale", torch.uint8, 2)
+        if w_dtype != "e4m3":
+            raise ValueError("MXFP8 activations need e4m3 weights")
+        if a_scale.shape[0] < a.shape[0] or a_scale.shape[1] < a.shape[1] // 32:
+            raise ValueError("a_scale must be at least [rows, K/32]")
+    else:
+        _need(a, "a", torch.bfloat16, 2)
+        if a_scale is not None:
+            raise ValueError("a_scale is for uint8 (E4M3) activations")
+    a_dt = MOE_E4M3 if a_f8 else MOE_BF16
     K = a.shape[1]
     S = int(num_tokens) * int(top_k)
     packed = isinstance(w, PackedWeights)
@@ -305,13 +321,15 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     if out.shape[0] < S or out.shape[1] < out_w:
         raise ValueError(f"out must be at least [{S}, {out_w}]")
     sorted_ids, expert_ids, post_pad = routing
-    if sorted_ids.numel() < expert_ids.numel() * (block_m or moe_gemm_block_m(w_dtype, num_tokens)):
+    bm = moe_gemm_block_m(w_dtype, num_tokens, a_dt) if block_m is None else block_m
+    if sorted_ids.numel() < expert_ids.numel() * bm:
         raise ValueError("routing arrays do not match block_m")
-    bm = moe_gemm_block_m(w_dtype, num_tokens) if block_m is None else block_m
     g = MoeGemmArgs()
     g.num_tokens, g.top_k, g.num_experts = int(num_tokens), int(top_k), int(num_experts)
     g.n, g.k = N, K
-    g.a_dtype, g.a_row_div, g.a, g.a_ld = MOE_BF16, int(a_row_div), a.data_ptr(), a.stride(0)
+    g.a_dtype, g.a_row_div, g.a, g.a_ld = a_dt, int(a_row_div), a.data_ptr(), a.stride(0)
+    if a_f8:
+        g.a_scale, g.a_scale_ld = a_scale.data_ptr(), a_scale.stride(0)
     g.w_dtype, g.w, g.w_stride_e, g.w_ld = wd, w_t.data_ptr(), w_t.stride(0), w_t.stride(1)
     g.w_layout = MOE_LAYOUT_KBLOCK if packed else MOE_LAYOUT_ROWS
     if w_scale is not None:
@@ -324,7 +342,7 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     g.block_m, g.max_blocks = int(bm), expert_ids.numel()
     st = _stream(stream)
     ref = ctypes.byref(g)
-    keep = (a, w_t, w_scale, bias, out, routing)  # the call holds its tensors alive
+    keep = (a, w_t, w_scale, bias, out, routing, a_scale)  # the call holds its tensors alive
 
     def call():
         _check(lib.moe_grouped_gemm(ref, st))

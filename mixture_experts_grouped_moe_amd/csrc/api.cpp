@@ -102,7 +102,9 @@ int64_t moe_align_max_blocks(int64_t num_slots, int32_t num_experts, int32_t blo
 }
 
 int32_t moe_gemm_block_m(int32_t a_dtype, int32_t w_dtype, int64_t num_tokens) {
-  if (a_dtype != MOE_BF16 || !valid_w_dtype(w_dtype) || num_tokens < 0) return -1;
+  if (num_tokens < 0) return -1;
+  if (a_dtype == MOE_E4M3 && w_dtype == MOE_E4M3) return moe::gemm_block_m_large();  // no decode variant
+  if (a_dtype != MOE_BF16 || !valid_w_dtype(w_dtype)) return -1;
   return num_tokens <= kDecodeMaxTokens ? moe::gemm_block_m_decode() : moe::gemm_block_m_large();
 }
 
@@ -156,8 +158,11 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   if (a.num_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens < 0");
   if (a.top_k < 1 || a.num_experts < a.top_k)
     return fail(MOE_ERR_INVALID_ARGUMENT, "need 1 <= top_k (%d) <= num_experts (%d)", a.top_k, a.num_experts);
-  if (a.a_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "a_dtype must be MOE_BF16");
+  const bool a_f8 = a.a_dtype == MOE_E4M3;
+  if (a.a_dtype != MOE_BF16 && !a_f8) return fail(MOE_ERR_UNSUPPORTED, "a_dtype must be MOE_BF16 or MOE_E4M3");
   if (!valid_w_dtype(a.w_dtype)) return fail(MOE_ERR_UNSUPPORTED, "w_dtype %d not supported", a.w_dtype);
+  if (a_f8 && a.w_dtype != MOE_E4M3)
+    return fail(MOE_ERR_UNSUPPORTED, "MXFP8 activations need MOE_E4M3 weights");
   if (a.n < 1 || a.n >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "n out of range");
   if (a.k < 32 || a.k % 32 != 0 || a.k >= INT32_MAX)
     return fail(MOE_ERR_INVALID_ARGUMENT, "k (%lld) must be a positive multiple of 32", (long long)a.k);
@@ -170,8 +175,10 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   if (S >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens * top_k must be < 2^31");
   if (a.a_row_div != 1 && a.a_row_div != a.top_k)
     return fail(MOE_ERR_INVALID_ARGUMENT, "a_row_div must be 1 or top_k");
-  if (a.a_ld < a.k || a.a_ld % 8 != 0)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "a_ld must be >= k and a multiple of 8");
+  if (a.a_ld < a.k || a.a_ld % (a_f8 ? 16 : 8) != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "a_ld must be >= k and a multiple of %d", a_f8 ? 16 : 8);
+  if (a_f8 && (a.a_scale == nullptr || a.a_scale_ld < a.k / 32))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "MXFP8 activations need a_scale with a_scale_ld >= k / 32");
   if (a.w_layout != MOE_LAYOUT_ROWS && a.w_layout != MOE_LAYOUT_KBLOCK)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown w_layout %d", a.w_layout);
   const bool kblock = a.w_layout == MOE_LAYOUT_KBLOCK;
@@ -215,8 +222,9 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   constexpr int64_t kBufMax = (int64_t)0x80000000;
   const int64_t w_span = (kblock ? nblk : a.n) * a.w_ld * w_elem_bytes;
   const int64_t ws_span = a.w_dtype == MOE_BF16 ? 0 : (kblock ? nblk : a.n) * a.w_scale_ld;
-  if (a_rows * a.a_ld * 2 >= kBufMax || w_span >= kBufMax || ws_span >= kBufMax)
-    return fail(MOE_ERR_UNSUPPORTED, "A, one expert's weights or its scales span 2 GB or more");
+  if (a_rows * a.a_ld * (a_f8 ? 1 : 2) >= kBufMax || w_span >= kBufMax || ws_span >= kBufMax ||
+      (a_f8 && a_rows * a.a_scale_ld >= kBufMax))
+    return fail(MOE_ERR_UNSUPPORTED, "A, its scales, one expert's weights or its scales span 2 GB or more");
   moe_status st = check_device();
   if (st != MOE_OK) return st;
   if (S == 0 || a.max_blocks == 0) return ok();
@@ -227,6 +235,8 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   p.a = static_cast<const uint16_t*>(a.a);
   p.a_ld = a.a_ld;
   p.a_rows = a_rows;
+  p.as = a_f8 ? a.a_scale : nullptr;
+  p.as_ld = a_f8 ? a.a_scale_ld : 0;
   p.a_row_div = a.a_row_div;
   p.w = static_cast<const uint8_t*>(a.w);
   p.w_stride_e = a.w_stride_e * w_elem_bytes;
@@ -249,8 +259,9 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   p.N = (int32_t)a.n;
   p.K = (int32_t)a.k;
   p.max_blocks = (int32_t)a.max_blocks;
-  const bool decode = a.num_tokens <= kDecodeMaxTokens;
   const bool bias = a.bias != nullptr;
+  if (a_f8) return hip_status(moe::launch_gemm_f8(p, swiglu, bias, (hipStream_t)stream), "moe_grouped_gemm launch");
+  const bool decode = a.num_tokens <= kDecodeMaxTokens;
   return hip_status(decode ? moe::launch_gemm_decode(p, a.w_dtype, swiglu, bias, (hipStream_t)stream)
                            : moe::launch_gemm_large(p, a.w_dtype, swiglu, bias, (hipStream_t)stream),
                     "moe_grouped_gemm launch");

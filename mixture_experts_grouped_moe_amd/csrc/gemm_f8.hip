@@ -1,0 +1,254 @@
+// Routed grouped GEMM with MXFP8 activations and MXFP8 (E4M3) weights: both
+// operands E4M3 codes with one E8M0 scale per 32 K-elements, the form of
+// moe_gemm_mxfp8 in ROCm/aiter PR #5310 "Add MoE GEMM variants and
+// weight-gradient kernel" (Summary: all experts in one launch, microscales
+// applied per K step, optional per-expert bias; second review: the kernel
+// decodes an a_scale and a b_scale byte per K block, sentinel blocks return at
+// once, E8M0 0x00 is 2^-127 and 0xFF NaN, bias through explicit strides).
+//
+// Design for gfx950 (the same routing, tiling and load pipeline as the bf16
+// large-M kernel in gemm.hip):
+//  * One workgroup of 4 waves (each 64 rows x 128 columns) per (routing block
+//    of 64 rows, N tile of 512 weight rows); two workgroups per CU.
+//  * Each 64-wide K step moves 4 KB of activation codes and 32 KB of weight
+//    codes straight into LDS with buffer_load ... lds, two stages deep, and
+//    the step's E8M0 bytes into the lanes that use them with byte loads.
+//  * The contraction is v_mfma_scale_f32_32x32x64_f8f6f4: one instruction
+//    per 32 x 32 output tile and K step, with the E8M0 bytes fed to it as they
+//    are (no dequantisation). Its operand layout (measured on gfx950): lane l
+//    holds row (or column) l % 32; bytes 0-15 are K elements 16h .. 16h+15
+//    and bytes 16-31 are 32 + 16h .. 32 + 16h + 15 (h = l / 32), and the
+//    scale operand of lane l is that of K block h: its 32 elements are bytes
+//    0-15 of both lane halves (h = 0) or bytes 16-31 (h = 1). So a lane reads
+//    16-byte units h and 2 + h of its row's 64-byte step piece.
+//  * fp32 accumulators, bias and SwiGLU in the epilogue, one bf16 rounding.
+#include "gemm_util.h"
+
+namespace moe {
+
+constexpr int kF8NT = 4;                        // 32-column MFMA tiles per wave
+constexpr int kF8Stages = 2;
+constexpr int kF8RowBytes = 64;                 // one row's codes per K step
+
+typedef int f8_v8i __attribute__((ext_vector_type(8)));
+
+template <bool SWIGLU, bool BIAS>
+__global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmParams p) {
+  constexpr int NT = kF8NT, STAGES = kF8Stages, RB = kF8RowBytes;
+  constexpr int WN = NT * 32, BN = kWavesN * WN;
+  constexpr int NWAVES = kWavesM * kWavesN;
+  constexpr int U = RB / 16;                        // 16-byte units per row per step
+  constexpr int A_BYTES = kBM * RB;                 // 4 KB
+  constexpr int W_BYTES = BN * RB;                  // 32 KB
+  constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // 1
+  constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;  // 8
+  constexpr int LOADS = A_LOADS + W_LOADS + NT + 2; // + weight and activation scale bytes
+  static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
+  static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
+  constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
+  static_assert(kMinBlocks * STAGES * STAGE_BYTES <= 160 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][STAGE_BYTES];
+
+  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = L % p.max_blocks;
+  const int tile_n = L / p.max_blocks;
+  const int e = p.expert_ids[b];
+  if (e < 0) return;  // sentinel block
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wn = wave % kWavesN;
+  const int l32 = lane % 32, h = lane / 32;
+  const int32_t* blk_slots = p.sorted + (int64_t)b * kBM;
+
+  // a wave with only PAD rows or only columns past N computes nothing (it
+  // still loads its share and joins every barrier)
+  const bool rows_live = __ballot(blk_slots[lane] < p.S) != 0;
+  const bool cols_live = tile_w_row<NT, SWIGLU>(wn * WN, tile_n, p.N) >= 0;
+  const bool wave_live = rows_live && cols_live;
+
+  const uint8_t* a8 = reinterpret_cast<const uint8_t*>(p.a);
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a8, 0, (int)(uint32_t)(p.a_rows * p.a_ld), 0x00020000);
+  const __amdgpu_buffer_rsrc_t as_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.as, 0, (int)(uint32_t)(p.a_rows * p.as_ld), 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.w + (int64_t)e * p.w_stride_e), 0, (int)(uint32_t)p.w_span, 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.ws + (int64_t)e * p.ws_stride_e), 0, (int)(uint32_t)p.ws_span, 0x00020000);
+
+  // ---- per-lane load descriptors (a load instruction fills one 1 KB block
+  //      of the stage, 16 bytes per lane in lane order)
+  uint32_t a_off[A_LOADS];
+  int a_k[A_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int q = (wave * A_LOADS + i) * 64 + lane;
+    const int row = q / U, u = swz<U>(row, q % U);
+    const int s = blk_slots[row];
+    a_k[i] = u * 16;
+    a_off[i] = s < p.S ? (uint32_t)((int64_t)(s / p.a_row_div) * p.a_ld + u * 16) : kOOB;
+  }
+  uint32_t w_off[W_LOADS];
+  int w_k[W_LOADS];
+#pragma unroll
+  for (int i = 0; i < W_LOADS; ++i) {
+    const int q = (wave * W_LOADS + i) * 64 + lane;
+    const int row = q / U, u = swz<U>(row, q % U);
+    const int32_t wr = tile_w_row<NT, SWIGLU>(row, tile_n, p.N);
+    w_k[i] = u * 16;
+    w_off[i] = wr >= 0 ? (uint32_t)((int64_t)wr * p.w_row + u * 16) : kOOB;
+  }
+  // scale bytes of K block 2 * step + h: the lane's weight rows (one per
+  // N sub-tile) and activation rows (one per M sub-tile)
+  int32_t my_wrow[NT];
+  uint32_t ws_off[NT], as_off[2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    my_wrow[nt] = tile_w_row<NT, SWIGLU>(wn * WN + nt * 32 + l32, tile_n, p.N);
+    ws_off[nt] = my_wrow[nt] >= 0 ? (uint32_t)((int64_t)my_wrow[nt] * p.ws_row + h) : kOOB;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int s = blk_slots[mt * 32 + l32];
+    as_off[mt] = s < p.S ? (uint32_t)((int64_t)(s / p.a_row_div) * p.as_ld + h) : kOOB;
+  }
+  const uint32_t w_blk = (uint32_t)p.w_blk, ws_blk = (uint32_t)p.ws_blk;
+
+  const int nsteps = (p.K + kBK - 1) / kBK;
+  const int nsteps_pad = ((nsteps + STAGES - 1) / STAGES) * STAGES;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)&lds[0][0];
+  uint32_t sc[STAGES][NT + 2];  // the step's scale bytes: weights (NT), then activations (2)
+
+  // Issue the loads of K step `step` into stage ST; the K tail and the
+  // look-ahead steps past the last one take the checked path (lanes past K
+  // read zeros, so do the scale bytes of a missing second block).
+  auto issue = [&](int step, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const int k0 = step * kBK;
+    const uint32_t base = lds_base + ST * STAGE_BYTES;
+    const bool full = k0 + kBK <= p.K;
+    const bool live = k0 < p.K;
+    const uint32_t sa = live ? (uint32_t)k0 : 0u, sw = live ? (uint32_t)step * w_blk : 0u,
+                   ss = live ? (uint32_t)step * ws_blk : 0u, sas = live ? (uint32_t)step * 2 : 0u;
+    const bool h_live = live && k0 + 32 * h < p.K;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      dma16(a_rsrc, (full || (live && k0 + a_k[i] < p.K)) ? a_off[i] : kOOB, sa,
+            base + (wave * A_LOADS + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < W_LOADS; ++i)
+      dma16(w_rsrc, (full || (live && k0 + w_k[i] < p.K)) ? w_off[i] : kOOB, sw,
+            base + A_BYTES + (wave * W_LOADS + i) * 1024);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sc[ST][nt] = load_byte(s_rsrc, h_live ? ws_off[nt] : kOOB, ss);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) sc[ST][NT + mt] = load_byte(as_rsrc, h_live ? as_off[mt] : kOOB, sas);
+  };
+
+  f32x16_t acc[2][NT];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
+
+  // operand of LDS row `row`: units h and 2 + h of its 64-byte step piece
+  auto operand = [&](const lds_u8_t* part, int row) -> f8_v8i {
+    const u32x4_t lo = lds_read<u32x4_t>(part + row * RB + swz<U>(row, h) * 16);
+    const u32x4_t hi = lds_read<u32x4_t>(part + row * RB + swz<U>(row, 2 + h) * 16);
+    f8_v8i r;
+    r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+    return r;
+  };
+
+  auto compute = [&](auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const lds_u8_t* As = (const lds_u8_t*)&lds[ST][0];
+    const lds_u8_t* Ws = As + A_BYTES;
+    f8_v8i af[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) af[mt] = operand(As, mt * 32 + l32);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const f8_v8i bf = operand(Ws, wn * WN + nt * 32 + l32);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            af[mt], bf, acc[mt][nt], 0, 0, 0, (int)sc[ST][NT + mt], 0, (int)sc[ST][nt]);
+    }
+  };
+
+  // two stages: wait for this step's loads (none are younger), barrier, load
+  // the next step into the other stage (every wave is past its compute),
+  // compute this one
+  static_for<0, STAGES - 1>([&](auto st) { issue(decltype(st)::value, st); });
+  for (int step = 0; step < nsteps_pad; step += STAGES) {
+    static_for<0, STAGES>([&](auto st) {
+      constexpr int ST = decltype(st)::value;
+      wait_loads_barrier<LOADS * (STAGES - 2)>(sc[ST]);
+      issue(step + ST + STAGES - 1, std::integral_constant<int, (ST + STAGES - 1) % STAGES>{});
+      if (wave_live) compute(st);
+    });
+  }
+  // drain the look-ahead loads, then keep the slot list in stage 0
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int32_t* s_slot = reinterpret_cast<int32_t*>(&lds[0][0]);
+  if (tid < kBM) s_slot[tid] = blk_slots[tid];
+  __syncthreads();
+
+  // ---- epilogue: bias, SwiGLU, one bf16 rounding, store real rows only
+  float bv[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    bv[nt] = 0.0f;
+    if (BIAS && my_wrow[nt] >= 0)
+      bv[nt] = bf16_bits_to_f32(p.bias[(int64_t)e * p.bias_se + (int64_t)my_wrow[nt] * p.bias_sn]);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = mt * 32 + (i / 4) * 8 + h * 4 + (i % 4);
+      const int s = s_slot[row];
+      if (s >= p.S) continue;
+      uint16_t* crow = p.c + (int64_t)s * p.c_ld;
+      if constexpr (!SWIGLU) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if (my_wrow[nt] >= 0) crow[my_wrow[nt]] = (uint16_t)f32_to_bf16_bits(acc[mt][nt][i] + bv[nt]);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT / 2; ++nt) {
+          if (my_wrow[nt] >= 0) {
+            const float g = acc[mt][nt][i] + bv[nt];
+            const float up = acc[mt][nt + NT / 2][i] + bv[nt + NT / 2];
+            crow[my_wrow[nt]] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * up);
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_f8(const GemmParams& p, bool swiglu, bool bias, hipStream_t stream) {
+  if (p.max_blocks <= 0) return hipSuccess;
+  const int bn = kWavesN * 32 * kF8NT;
+  const int64_t tiles = swiglu ? (p.N / 2 + bn / 2 - 1) / (bn / 2) : (p.N + bn - 1) / bn;
+  const dim3 grid((uint32_t)(tiles * p.max_blocks));
+  if (swiglu) {
+    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<true, true>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((moe_gemm_f8_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

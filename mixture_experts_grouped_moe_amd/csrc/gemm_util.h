@@ -1,0 +1,118 @@
+// Building blocks of the large-M grouped GEMM kernels (bf16 activations in
+// gemm.hip, MXFP8 activations in gemm_f8.hip): the workgroup shape, the
+// LDS-DMA and byte loads issued with inline assembly, the wait-and-barrier of
+// the K loop, the LDS swizzle and the weight rows of an N tile.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+#include "params.h"
+
+namespace moe {
+
+constexpr int kWavesM = 1;                        // waves along M
+constexpr int kWavesN = 4;                        // waves along N
+constexpr int kBM = 64 * kWavesM;                 // the routing block
+constexpr int kBK = 64;
+constexpr int kThreads = kWave * kWavesM * kWavesN;  // 256
+constexpr int kMinBlocks = 2;                     // workgroups per CU (LDS and registers allow two)
+// A per-lane buffer offset past every buffer the kernel reads (each is below
+// 2 GB, checked by the host API), also after a scalar step offset below 2 GB
+// is added: such a lane reads zeros.
+constexpr uint32_t kOOB = 0x80000000u;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// Typed reads from an LDS address (kept in the LDS address space so the
+// compiler can tell the stages apart).
+template <typename T>
+__device__ __forceinline__ T lds_read(const lds_u8_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
+}
+
+// The K loop's loads are issued with inline assembly, so the compiler does
+// not track them: it inserts no waits of its own (its alias analysis cannot
+// tell the LDS stages apart and would wait for every load in flight), and the
+// loop's explicit waits below are the whole synchronisation.
+//
+// 16 bytes per lane from buffer `rsrc` at byte offset `voff` + `soff` into
+// LDS at `lds_base` + 16 * lane; a lane whose `voff` is kOOB reads zeros.
+// `soff` (the step's advance) and `lds_base` are wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+               :: "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "m0");
+}
+
+// One byte from buffer `rsrc` at `voff` + `soff` into a register (zero for a
+// lane whose `voff` is kOOB).
+__device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+  uint32_t v;
+  asm volatile("buffer_load_ubyte %0, %1, %2, %3 offen"
+               : "=v"(v) : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)));
+  return v;
+}
+
+// Wait until at most N of this wave's loads are in flight and its LDS
+// operations are done, then barrier. The registers passed in are loads whose
+// values must not be used before this point; the "memory" clobber keeps LDS
+// accesses on their side of the barrier.
+template <int N, int R>
+__device__ __forceinline__ void wait_loads_barrier(uint32_t (&regs)[R]) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (R == 6) {
+    asm volatile("s_waitcnt vmcnt(%6) lgkmcnt(0)\n\ts_barrier"
+                 : "+v"(regs[0]), "+v"(regs[1]), "+v"(regs[2]), "+v"(regs[3]), "+v"(regs[4]), "+v"(regs[5])
+                 : "n"(N) : "memory");
+  } else if constexpr (R == 4) {
+    asm volatile("s_waitcnt vmcnt(%4) lgkmcnt(0)\n\ts_barrier"
+                 : "+v"(regs[0]), "+v"(regs[1]), "+v"(regs[2]), "+v"(regs[3]) : "n"(N) : "memory");
+  } else if constexpr (R == 2) {
+    asm volatile("s_waitcnt vmcnt(%2) lgkmcnt(0)\n\ts_barrier"
+                 : "+v"(regs[0]), "+v"(regs[1]) : "n"(N) : "memory");
+  } else {
+    static_assert(R == 1, "registers to hold until the wait: 1 (none), 2, 4 or 6");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+  }
+}
+
+// Physical 16-byte unit of logical unit u in LDS row `row` (rows of U units).
+// gfx950's LDS serves a ds_read_b128 16 lanes at a time from 64 banks
+// (256 bytes); the 16 rows one such group reads get distinct 16-byte slots
+// of that window (measured: conflict-free, where a 32-bank layout conflicts
+// two-way).
+template <int U>
+__device__ __forceinline__ int swz(int row, int u) {
+  return u ^ ((row / (16 / U)) % U);
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Global weight row of local tile row r, or -1 beyond N.
+template <int NT, bool SWIGLU>
+__device__ __forceinline__ int32_t tile_w_row(int r, int tile_n, int N) {
+  constexpr int WN = NT * 32;
+  constexpr int BN = kWavesN * WN;
+  if (!SWIGLU) {
+    int n = tile_n * BN + r;
+    return n < N ? n : -1;
+  } else {
+    const int half = N / 2;
+    const int w = r / WN, q = r % WN;
+    const bool up = q >= WN / 2;
+    const int hcol = tile_n * (BN / 2) + w * (WN / 2) + (up ? q - WN / 2 : q);
+    if (hcol >= half) return -1;
+    return up ? half + hcol : hcol;
+  }
+}
+
+}  // namespace moe

@@ -8,8 +8,10 @@
 namespace moe {
 
 struct GemmParams {
-  const uint16_t* a;   // bf16 activation rows
+  const uint16_t* a;   // bf16 activation rows (E4M3 code rows for the MXFP8-activation kernel)
   int64_t a_ld;        // elements
+  const uint8_t* as;   // E8M0 activation scales [a_rows][K/32] (MXFP8 activations only)
+  int64_t as_ld;       // bytes
   int64_t a_rows;      // rows of A that slots can address: ceil(S / a_row_div)
   int32_t a_row_div;   // slot s reads row s / a_row_div
   // Weight codes of (e, n, 64-element K block kb) start at byte
@@ -55,6 +57,8 @@ hipError_t launch_align(const int32_t* ids, int32_t S, int32_t E, int32_t B, int
                         int32_t* expert_ids, int32_t* post_pad, int32_t max_blocks, hipStream_t stream);
 hipError_t launch_gemm_large(const GemmParams& p, int wdt, bool swiglu, bool bias, hipStream_t stream);
 hipError_t launch_gemm_decode(const GemmParams& p, int wdt, bool swiglu, bool bias, hipStream_t stream);
+// MXFP8 activations x MXFP8 (E4M3) weights on the scaled fp8 MFMA
+hipError_t launch_gemm_f8(const GemmParams& p, bool swiglu, bool bias, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* c, int64_t c_ld, const float* w, int64_t T, int32_t top_k,
                           int64_t N, uint16_t* y, int64_t y_ld, hipStream_t stream);
 hipError_t launch_wgrad(const WgradParams& p, hipStream_t stream);

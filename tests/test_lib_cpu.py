@@ -78,7 +78,11 @@ def test_block_m_rule():
     assert moe.moe_decode_max_tokens() == 32 == moe.moe_bucket_round_up(32)
     for t in range(1, 2000):
         assert (t <= 32) == (moe.moe_bucket_round_up(t) <= 32)
-    assert L.moe_gemm_block_m(moe.MOE_E4M3, moe.MOE_E4M3, 100) == -1  # fp8 activations: not here
+    # MXFP8 activations run the large-M kernel at every token count, with E4M3 weights only
+    large = moe.moe_gemm_block_m("e4m3", 100)
+    assert {L.moe_gemm_block_m(moe.MOE_E4M3, moe.MOE_E4M3, t) for t in (0, 1, 32, 33, 4096)} == {large}
+    assert L.moe_gemm_block_m(moe.MOE_E4M3, moe.MOE_E2M1X2, 100) == -1
+    assert L.moe_gemm_block_m(moe.MOE_E4M3, moe.MOE_BF16, 100) == -1
     assert L.moe_gemm_block_m(moe.MOE_BF16, 99, 100) == -1
 
 
@@ -138,6 +142,23 @@ def _gemm_args(**kw):
 
 def _gemm(**kw):
     return L.moe_grouped_gemm(ctypes.byref(_gemm_args(**kw)), None)
+
+
+def test_grouped_gemm_rejects_mxfp8_activations(no_device):
+    def g8(**kw):
+        args = _gemm_args(w_dtype=moe.MOE_E4M3)
+        args.a_dtype, args.a_ld, args.a_scale, args.a_scale_ld = moe.MOE_E4M3, args.k, 0x100000, args.k // 32
+        args.block_m = L.moe_gemm_block_m(moe.MOE_E4M3, moe.MOE_E4M3, args.num_tokens)
+        args.max_blocks = moe.moe_align_max_blocks(args.num_tokens * args.top_k, args.num_experts, args.block_m)
+        for key, v in kw.items():
+            setattr(args, key, v)
+        return L.moe_grouped_gemm(ctypes.byref(args), None)
+
+    assert g8(a_scale=None) == INVALID               # scales required
+    assert g8(a_scale_ld=3) == INVALID               # fewer than k / 32
+    assert g8(a_ld=136) == INVALID                   # not a multiple of 16 bytes
+    assert g8(w_dtype=moe.MOE_E2M1X2, w_ld=64, w_stride_e=256 * 64) == UNSUPPORTED
+    assert g8(a_dtype=moe.MOE_FP32) == UNSUPPORTED
 
 
 def test_grouped_gemm_rejects(no_device):
