@@ -22,9 +22,11 @@ other than itself:
     gemm.dequant_expert     pinned  (constant-input closed form, Fraction brute force)
     gemm.grouped_gemm       pinned  (constant input, bias, linearity, Fraction brute force)
     gemm.silu / swiglu      pinned  (closed forms and the odd-part identity)
+    gemm.relu2              pinned  (closed forms; constant-input GEMM epilogue)
     gemm.combine            pinned  (identity at k = 1, hand-worked example, linearity)
     wgrad.wgrad             pinned  (constant input, linearity, zero/PAD slots, Fraction brute force)
     layer.w4a16_layer       pinned  (composition of pinned functions; padded == unpadded)
+    layer.relu2_layer       pinned  (composition of pinned functions; constant-input closed form)
     layout.pack_kblock      pinned  (per-element loop over the layout's index formula)
     quant.mx_quantize_e4m3  pinned  (every code round-trips at a known shared exponent;
                                      scale rule, ties, saturation, zero and clamped

@@ -74,6 +74,17 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
+def relu2(pre):
+    """The non-gated squared ReLU of torchada PR #115's Nemotron decode shape
+    ("Follow-up on this table": the recipe records a non-gated relu2 layer):
+    h = max(pre, 0)^2, elementwise, same width.
+
+    Pinned: tests/test_oracle_gemm.py (closed forms on both sides of 0).
+    """
+    pre = np.asarray(pre, dtype=np.float64)
+    return np.where(pre > 0, pre * pre, 0.0)
+
+
 def swiglu(pre):
     """pre [R, N] -> h [R, N/2] with h[:, j] = silu(pre[:, j]) * pre[:, N/2 + j]."""
     n = pre.shape[-1]
@@ -95,7 +106,7 @@ def grouped_gemm(a, a_row_div, w, w_dtype, w_scale, topk_ids, num_experts,
     w_scale  E8M0 bytes [E, N, K/32] (None for bf16)
     topk_ids routing [T, top_k] (or flat [S])
     bias     bf16 bit patterns [E, N] or None (added before the epilogue)
-    epilogue "none" or "swiglu" (output width N/2)
+    epilogue "none", "swiglu" (output width N/2) or "relu2" (max(pre, 0)^2)
     slots    optional subset of slots to compute (for sampled checks)
 
     Returns (C, routed): C float64 [S, N_out] (rows of unrouted or unrequested
@@ -125,6 +136,8 @@ def grouped_gemm(a, a_row_div, w, w_dtype, w_scale, topk_ids, num_experts,
             pre = pre + bf16_to_f64(bias[e])[None, :]
         if epilogue == "swiglu":
             pre = swiglu(pre)
+        elif epilogue == "relu2":
+            pre = relu2(pre)
         elif epilogue != "none":
             raise ValueError(f"unknown epilogue {epilogue}")
         C[rows] = pre

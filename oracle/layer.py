@@ -1,5 +1,5 @@
-"""The W4A16 MXFP4 expert layer as one composition (oracle; test
-infrastructure only).
+"""The W4A16 MXFP4 expert layer and the bf16 squared-ReLU decode layer as
+compositions (oracle; test infrastructure only).
 
 Source: TensorRT-LLM PR #15311 "Bound Triton MoE JIT specializations via
 token-dim bucketing and warmup", Description: W4A16 MXFP4 grouped GEMMs with
@@ -32,3 +32,20 @@ def w4a16_layer(x, topk_ids, topk_w, top_k, num_experts,
                          bias=b2, a_dtype="f64", slots=np.nonzero(routed)[0])
     y = None if slots is not None else combine(c2, topk_w, top_k)
     return h, c2, y
+
+
+def relu2_layer(x, topk_ids, topk_w, top_k, num_experts, w1, b1, w2, b2):
+    """The non-gated squared-ReLU MoE layer of torchada PR #115's Nemotron
+    shape ("Follow-up on this table": E=128, hidden 2688, N=1856, top-6,
+    non-gated relu2, bf16): up GEMM -> relu2 -> down GEMM -> top-k combine,
+    nothing rounded in between. Return (h, c2, y) in float64.
+
+    x bf16 bits [T, H]; w1 bf16 bits [E, N, H]; w2 bf16 bits [E, H, N]; b1,
+    b2 bf16 bits or None. h [S, N], c2 [S, H], y [T, H].
+    Pinned: tests/test_oracle_layer.py (the composition equals its pinned
+    parts; a constant-input closed form).
+    """
+    h, routed = grouped_gemm(x, top_k, w1, "bf16", None, topk_ids, num_experts, bias=b1, epilogue="relu2")
+    c2, _ = grouped_gemm(h, 1, w2, "bf16", None, topk_ids, num_experts, bias=b2, a_dtype="f64",
+                         slots=np.nonzero(routed)[0])
+    return h, c2, combine(c2, topk_w, top_k)

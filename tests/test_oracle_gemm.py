@@ -187,6 +187,23 @@ def test_swiglu_epilogue_in_gemm():
     np.testing.assert_allclose(h, np.full((T, 3), expect), rtol=1e-15)
 
 
+def test_relu2_closed_forms():
+    np.testing.assert_array_equal(gemm.relu2(np.array([-3.0, -0.0, 0.0, 0.5, 3.0])), [0.0, 0.0, 0.0, 0.25, 9.0])
+
+
+def test_relu2_epilogue_in_gemm():
+    # constant input: pre = K*a + bias per column; bias -1 on the first three
+    # columns (K a = 8 -> 7 -> 49) and -9 on the rest (-> -1 -> 0)
+    T, k, E, N, K, a = 4, 1, 2, 6, 32, 0.25
+    ids = np.zeros((T, k), dtype=np.int32)
+    x = np.full((T, K), _bf16_bits([a])[0], dtype=np.uint16)
+    w = np.full((E, N, K), 0x38, dtype=np.uint8)
+    ws = np.full((E, N, 1), 127, dtype=np.uint8)
+    bias = _bf16_bits(np.array([[-1, -1, -1, -9, -9, -9]] * E, dtype=np.float64))
+    h, _ = gemm.grouped_gemm(x, k, w, "e4m3", ws, ids, E, bias=bias, epilogue="relu2")
+    np.testing.assert_array_equal(h, np.tile([49.0, 49.0, 49.0, 0.0, 0.0, 0.0], (T, 1)))
+
+
 def test_combine_identity_and_example():
     c = np.arange(12, dtype=np.float64).reshape(4, 3)
     np.testing.assert_array_equal(gemm.combine(c, np.ones((4, 1)), 1), c)
