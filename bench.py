@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode", choices=["decode", "w4a16", "mxfp8", "mxfp8a", "wgrad", "copy"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "nemotron", "w4a16", "mxfp8", "mxfp8a", "wgrad", "copy"])
     ap.add_argument("--variants", type=int, default=4, help="routing variants cycled across steps")
     ap.add_argument("--launch-reps", type=int, default=10,
                     help="back-to-back launches per event pair when timing the dominant kernel")
@@ -57,7 +58,7 @@ def parse():
 
 
 # sources whose change can change a workload's dominant kernel
-KERNEL_SOURCES = {"decode": ["decode.hip"], "w4a16": ["gemm.hip", "gemm_util.h"],
+KERNEL_SOURCES = {"decode": ["decode.hip"], "nemotron": ["decode.hip"], "w4a16": ["gemm.hip", "gemm_util.h"],
                   "mxfp8": ["gemm.hip", "gemm_util.h"], "mxfp8a": ["gemm_f8.hip", "gemm_util.h"],
                   "wgrad": ["wgrad.hip"], "copy": []}
 
@@ -161,7 +162,7 @@ class Workload:
         raise NotImplementedError
 
 
-LAYOUT = {"decode": "rows", "w4a16": "kblock", "mxfp8": "kblock", "mxfp8a": "kblock"}  # resolved --layout per workload
+LAYOUT = {"decode": "rows", "nemotron": "rows", "w4a16": "kblock", "mxfp8": "kblock", "mxfp8a": "kblock"}  # resolved --layout per workload
 
 
 def _gemm_weights(moe, name, w, w_dtype, w_scale):
@@ -263,6 +264,108 @@ class Decode(Workload):
             oalign.moe_align(ids, self.E, bm)
             C, _ = ogemm.grouped_gemm(x, self.k, lw, "bf16", None, ids, self.E)
             ogemm.combine(C, tw, self.k)
+            return self._call_bytes(0, i)
+        return items, run, "GB/s"
+
+
+class Nemotron(Workload):
+    """The Nemotron-shaped non-gated squared-ReLU decode layer (E=128, top-6,
+    hidden 2688, N=1856, bf16) at M = 1, 7, 14, 21, 28: per M one step runs
+    moe_align -> up GEMM with relu2 -> down GEMM -> moe_combine, both GEMMs on
+    the decode kernel."""
+    name = "nemotron"
+    dominant = "moe_decode_kernel"
+    bound = "hbm"
+    MS = (1, 7, 14, 21, 28)
+    cpu_sample_desc = "the whole relu2 layer (align, both GEMMs, combine) for M = 1 and 7 of routing variant 0"
+
+    def __init__(self, torch, dev, variants):
+        import numpy as np
+        import mixture_experts_grouped_moe_amd as moe
+        import synth
+        self.torch, self.moe = torch, moe
+        self.E, self.H, self.N, self.k = 128, 2688, 1856, 6
+        d = synth.nemotron_layer(1, device=dev)
+        self.w1, self.w2 = d["w1"], d["w2"]
+        self.calls, self.bytes_gemm = [], []
+        for v in range(variants):
+            per_m, per_b = [], []
+            for M in self.MS:
+                dm = synth.nemotron_layer(M, seed=1006 + 100 * v, device=dev, weights=False)
+                bm = moe.moe_gemm_block_m("bf16", M)
+                S = M * self.k
+                c = dict(M=M, x=dm["x"], ids=dm["ids"], tw=dm["topk_w"], bm=bm,
+                         routing=_routing_buffers(torch, M, self.k, self.E, bm, dev),
+                         h=torch.empty((S, self.N), dtype=torch.bfloat16, device=dev),
+                         c2=torch.empty((S, self.H), dtype=torch.bfloat16, device=dev),
+                         y=torch.empty((M, self.H), dtype=torch.bfloat16, device=dev))
+                c["touched"] = len(np.unique(dm["ids"].cpu().numpy()))
+                wb = c["touched"] * self.N * self.H * 2
+                per_b.append((wb + M * self.H * 2 + S * self.N * 2, wb + S * self.N * 2 + S * self.H * 2))
+                per_m.append(c)
+            self.calls.append(per_m)
+            self.bytes_gemm.append(per_b)
+
+    def _call_bytes(self, v, i):
+        c = self.calls[v][i]
+        S = c["M"] * self.k
+        mb = c["routing"][1].numel()
+        align = S * 4 + mb * c["bm"] * 4 + mb * 4 + 4
+        combine = S * self.H * 2 + c["M"] * self.H * 2 + S * 4
+        return sum(self.bytes_gemm[v][i]) + align + combine
+
+    def step_bytes(self, v):
+        return sum(self._call_bytes(v, i) for i in range(len(self.MS)))
+
+    def step_flops(self, v):
+        return sum(2 * 2 * c["M"] * self.k * self.N * self.H for c in self.calls[v])
+
+    def _up(self, c):
+        if "up" not in c:
+            c["up"], _ = self.moe.moe_grouped_gemm_prepare(c["x"], self.w1, "bf16", c["routing"], c["M"], self.k,
+                                                           self.E, self.k, epilogue="relu2", out=c["h"])
+        return c["up"]()
+
+    def _down(self, c):
+        if "down" not in c:
+            c["down"], _ = self.moe.moe_grouped_gemm_prepare(c["h"], self.w2, "bf16", c["routing"], c["M"], self.k,
+                                                             self.E, 1, out=c["c2"])
+        return c["down"]()
+
+    def step(self, v):
+        moe = self.moe
+        for c in self.calls[v]:
+            moe.moe_align(c["ids"], self.E, c["bm"], out=c["routing"])
+            self._up(c)
+            self._down(c)
+            moe.moe_combine(c["c2"], c["tw"], self.k, out=c["y"])
+
+    def dominant_launches(self, v):
+        out = []
+        for i, c in enumerate(self.calls[v]):
+            out.append((lambda c=c: self._up(c), self.bytes_gemm[v][i][0]))
+            out.append((lambda c=c: self._down(c), self.bytes_gemm[v][i][1]))
+        return out
+
+    def extra(self, per_call_us):
+        us = {}
+        if per_call_us is not None:
+            for i, M in enumerate(self.MS):
+                us[str(M)] = {"up": round(per_call_us[2 * i], 2), "down": round(per_call_us[2 * i + 1], 2)}
+        return {"us_per_gemm": us, "touched_experts": {str(M): self.calls[0][i]["touched"] for i, M in enumerate(self.MS)}}
+
+    def cpu_sample(self):
+        import synth
+        from oracle import align as oalign, layer as olayer
+        lw1, lw2 = LazyRows(self.w1), LazyRows(self.w2)
+        items = []
+        for i, c in enumerate(self.calls[0][:2]):
+            items.append((synth.bits(c["x"]), synth.bits(c["ids"]), synth.bits(c["tw"]), c["bm"], i))
+
+        def run(item):
+            x, ids, tw, bm, i = item
+            oalign.moe_align(ids, self.E, bm)
+            olayer.relu2_layer(x, ids, tw, self.k, self.E, lw1, None, lw2, None)
             return self._call_bytes(0, i)
         return items, run, "GB/s"
 
@@ -583,9 +686,10 @@ class Copy(Workload):
         return [0], run, "GB/s"
 
 
-WORKLOADS = {"decode": Decode, "w4a16": W4A16, "mxfp8": MXFP8, "mxfp8a": MXFP8A, "wgrad": Wgrad, "copy": Copy}
+WORKLOADS = {"decode": Decode, "nemotron": Nemotron, "w4a16": W4A16, "mxfp8": MXFP8, "mxfp8a": MXFP8A, "wgrad": Wgrad, "copy": Copy}
 CONFIG_NAMES = {
     "decode": "decode bf16 MoE, E=128 N=1856 K=2048 top-6, M in {1,7,14,21,28}",
+    "nemotron": "Nemotron-shaped relu2 decode MoE layer, E=128 top-6 hidden=2688 N=1856, bf16, M in {1,7,14,21,28}",
     "w4a16": "W4A16 MXFP4 MoE layer (gpt-oss-shaped), E=128 top-4 H=2880, gate+up 5760 -> SwiGLU -> down 2880, T~U[6554,8192] bucketed",
     "mxfp8": "MXFP8 grouped GEMM, E=256 top-8 K=7168 N=4096 T=4096, Zipf(1.1) routing with 16 empty experts",
     "mxfp8a": "MXFP8 grouped GEMM with MXFP8 activations (bf16 converted each step), E=256 top-8 K=7168 N=4096 "
@@ -639,7 +743,7 @@ def main():
         for name in LAYOUT:
             LAYOUT[name] = args.layout
     wl = WORKLOADS[args.workload](torch, dev, args.variants)
-    nv = len(getattr(wl, "calls", [None])) if args.workload in ("decode", "w4a16") else 1
+    nv = len(getattr(wl, "calls", [None])) if args.workload in ("decode", "nemotron", "w4a16") else 1
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
 
@@ -705,12 +809,12 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": wl.dominant, "avg_launch_us": round(avg_launch_us, 3)}
 
-    if args.workload in ("decode", "copy"):
+    if args.workload in ("decode", "nemotron", "copy"):
         value = step_bytes / dt / 1e9
         unit_v = "GB/s"
         extra = wl.extra([sum(v) / len(v) for _, v in sorted(per_call.items())])
         extra["hbm_frac_step"] = round(value / PEAK_HBM_GBS, 4)
-        dtype = "bf16" if args.workload == "decode" else "u8"
+        dtype = "u8" if args.workload == "copy" else "bf16"
     else:
         value = step_flops / dt / 1e12
         unit_v = "TFLOP/s"

@@ -81,7 +81,11 @@ typedef enum {
   MOE_EPILOGUE_NONE = 0,
   /* h[:, j] = silu(pre[:, j]) * pre[:, N/2 + j], silu(z) = z / (1 + e^-z);
      output width N/2. Gate = first half of the N weight rows, up = second. */
-  MOE_EPILOGUE_SWIGLU = 1
+  MOE_EPILOGUE_SWIGLU = 1,
+  /* h = max(pre, 0)^2 elementwise, output width N: the non-gated squared
+     ReLU ("relu2_no_mul") of [TA] "Follow-up on this table" (the Nemotron
+     decode shape, E=128, hidden 2688, N=1856, top-6) */
+  MOE_EPILOGUE_RELU2 = 2
 } moe_epilogue;
 
 /* ------------------------------------------------------------------------
@@ -169,7 +173,8 @@ moe_status moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t top_k,
  *   MOE_E4M3 activations (both operands MXFP8: the kernel feeds codes and
  *   scale bytes to gfx950's scaled fp8 MFMA, the a_scale / b_scale form of
  *   [AIT]'s kernel; moe_quantize_mxfp8 makes such activations)
- *   C[s][:] = bf16(pre) (MOE_EPILOGUE_NONE) or bf16(swiglu(pre)) (width N/2)
+ *   C[s][:] = bf16(pre) (MOE_EPILOGUE_NONE), bf16(swiglu(pre)) (width N/2)
+ *             or bf16(max(pre, 0)^2) (MOE_EPILOGUE_RELU2)
  * accumulated in fp32, rounded once to bf16 (nearest-even) at the store.
  * Rows of C for PAD positions and unrouted slots are not written.
  * Weights are dequantized exactly into bf16 (the scale is a power of two)

@@ -21,7 +21,7 @@ __all__ = [
     "moe_align", "moe_grouped_gemm", "moe_grouped_gemm_prepare", "moe_combine", "moe_wgrad",
     "moe_quantize_mxfp8",
     "moe_pack_weights", "moe_packed_sizes", "PackedWeights", "MOE_LAYOUT_ROWS", "MOE_LAYOUT_KBLOCK",
-    "moe_w4a16_layer",
+    "moe_w4a16_layer", "moe_relu2_layer",
     "LIB_PATH",
 ]
 
@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_BF16, MOE_FP32, MOE_E4M3, MOE_E2M1X2, MOE_E8M0, MOE_I32 = 1, 2, 3, 4, 5, 6
 MOE_LAYOUT_ROWS, MOE_LAYOUT_KBLOCK = 0, 1
 _W_DTYPES = {"bf16": MOE_BF16, "e4m3": MOE_E4M3, "e2m1x2": MOE_E2M1X2}
-_EPILOGUES = {"none": 0, "swiglu": 1}
+_EPILOGUES = {"none": 0, "swiglu": 1, "relu2": 2}
 
 
 class MoeError(RuntimeError):
@@ -446,4 +446,19 @@ def moe_w4a16_layer(x, topk_ids, topk_w, w1, s1, w2, s2, b1=None, b2=None, num_t
                          epilogue="swiglu", stream=stream)
     c2 = moe_grouped_gemm(h, w2, "e2m1x2", routing, Tr, k, E, a_row_div=1, w_scale=s2, bias=b2,
                           stream=stream)
+    return moe_combine(c2, topk_w, k, num_tokens=T, stream=stream)
+
+
+def moe_relu2_layer(x, topk_ids, topk_w, w1, w2, b1=None, b2=None, num_tokens=None, stream=None):
+    """The non-gated squared-ReLU expert layer (the Nemotron decode shape):
+    align -> up GEMM with h = max(pre, 0)^2 -> down GEMM -> top-k combine, bf16
+    weights (rows layout [E, N, H] and [E, H, N], or PackedWeights). Token
+    counts up to moe_decode_max_tokens() run the decode GEMM. Returns y bf16
+    [num_tokens, H]."""
+    T = x.shape[0] if num_tokens is None else int(num_tokens)
+    k = topk_ids.shape[1]
+    E = w1.num_experts if isinstance(w1, PackedWeights) else w1.shape[0]
+    routing = moe_align(topk_ids, E, moe_gemm_block_m("bf16", T), num_tokens=T, stream=stream)
+    h = moe_grouped_gemm(x, w1, "bf16", routing, T, k, E, a_row_div=k, bias=b1, epilogue="relu2", stream=stream)
+    c2 = moe_grouped_gemm(h, w2, "bf16", routing, T, k, E, a_row_div=1, bias=b2, stream=stream)
     return moe_combine(c2, topk_w, k, num_tokens=T, stream=stream)

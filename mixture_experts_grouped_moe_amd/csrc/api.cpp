@@ -166,7 +166,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   if (a.n < 1 || a.n >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "n out of range");
   if (a.k < 32 || a.k % 32 != 0 || a.k >= INT32_MAX)
     return fail(MOE_ERR_INVALID_ARGUMENT, "k (%lld) must be a positive multiple of 32", (long long)a.k);
-  if (a.epilogue != MOE_EPILOGUE_NONE && a.epilogue != MOE_EPILOGUE_SWIGLU)
+  if (a.epilogue != MOE_EPILOGUE_NONE && a.epilogue != MOE_EPILOGUE_SWIGLU && a.epilogue != MOE_EPILOGUE_RELU2)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown epilogue %d", a.epilogue);
   const bool swiglu = a.epilogue == MOE_EPILOGUE_SWIGLU;
   if (swiglu && a.n % 2 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "SwiGLU needs an even n");
@@ -259,6 +259,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   p.N = (int32_t)a.n;
   p.K = (int32_t)a.k;
   p.max_blocks = (int32_t)a.max_blocks;
+  p.relu2 = a.epilogue == MOE_EPILOGUE_RELU2 ? 1 : 0;
   const bool bias = a.bias != nullptr;
   if (a_f8) return hip_status(moe::launch_gemm_f8(p, swiglu, bias, (hipStream_t)stream), "moe_grouped_gemm launch");
   const bool decode = a.num_tokens <= kDecodeMaxTokens;

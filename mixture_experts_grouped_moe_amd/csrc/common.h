@@ -82,6 +82,9 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t hw_id, uint32_t grid) {
   return base + hw_id / kXcd;
 }
 
+// The non-gated squared ReLU epilogue: max(z, 0)^2 (NaN -> 0, as z > 0 fails).
+__device__ __forceinline__ float relu2_f32(float z) { return z > 0.0f ? z * z : 0.0f; }
+
 __device__ __forceinline__ float silu_f32(float z) {
   return z / (1.0f + __expf(-z));
 }

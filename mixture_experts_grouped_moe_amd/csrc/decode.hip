@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreadsDec, 4) void moe_decode_kernel(GemmParams p
     if (!SWIGLU) {
 #pragma unroll
       for (int r = 0; r < kDecRowsPerWave; ++r)
-        if (ocol[r] >= 0) crow[ocol[r]] = (uint16_t)f32_to_bf16_bits(v[r]);
+        if (ocol[r] >= 0) crow[ocol[r]] = (uint16_t)f32_to_bf16_bits(p.relu2 ? relu2_f32(v[r]) : v[r]);
     } else {
 #pragma unroll
       for (int r = 0; r < 2; ++r)

@@ -220,7 +220,10 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
       if constexpr (!SWIGLU) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          if (my_wrow[nt] >= 0) crow[my_wrow[nt]] = (uint16_t)f32_to_bf16_bits(acc[mt][nt][i] + bv[nt]);
+          if (my_wrow[nt] >= 0) {
+            const float v = acc[mt][nt][i] + bv[nt];
+            crow[my_wrow[nt]] = (uint16_t)f32_to_bf16_bits(p.relu2 ? relu2_f32(v) : v);
+          }
         }
       } else {
 #pragma unroll

@@ -35,6 +35,7 @@ struct GemmParams {
   int32_t S;           // PAD value (= number of slots)
   int32_t N, K;
   int32_t max_blocks;
+  int32_t relu2;       // non-SwiGLU epilogue: store max(pre, 0)^2 instead of pre
 };
 
 struct WgradParams {

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "gen", "bf16_normal", "e4m3_normal", "e2m1_uniform", "e8m0_uniform",
     "softmax_topk_routing", "zipf_topk_routing", "uniform_topk_routing",
-    "gemm_case", "config1", "config2", "config3", "config4", "config5",
+    "gemm_case", "config1", "config2", "config3", "config4", "config5", "nemotron_layer",
     "bits", "draw_token_counts",
 ]
 
@@ -152,6 +152,22 @@ def config2(M, seed=1002, K=2048, device="cpu"):
     d["w"] = bf16_normal((128, 1856, K), 0.02, seed, "w", device)
     d["x"] = bf16_normal((M, K), 1.0, seed, f"x{M}", device)
     d["ids"], d["topk_w"] = softmax_topk_routing(M, 128, 6, seed, f"route{M}", device)
+    return d
+
+
+def nemotron_layer(M, seed=1006, device="cpu", E=128, H=2688, N=1856, k=6, bias=False, weights=True):
+    """The Nemotron-shaped non-gated squared-ReLU decode layer: E=128, top-6,
+    hidden H=2688, up N=1856 -> relu2 -> down H; W1 bf16 N(0, 0.02^2)
+    [E, N, H], W2 bf16 N(0, 0.02^2) [E, H, N], x bf16 N(0, 1) [M, H],
+    softmax top-k routing; optional bf16 N(0, 1) biases. weights=False
+    leaves out W1 and W2 (the same draws of x and the routing)."""
+    d = {"T": M, "k": k, "E": E, "H": H, "N": N}
+    d["x"] = bf16_normal((M, H), 1.0, seed, f"x{M}", device)
+    d["w1"] = bf16_normal((E, N, H), 0.02, seed, "w1", device) if weights else None
+    d["w2"] = bf16_normal((E, H, N), 0.02, seed, "w2", device) if weights else None
+    d["b1"] = bf16_normal((E, N), 1.0, seed, "b1", device) if bias else None
+    d["b2"] = bf16_normal((E, H), 1.0, seed, "b2", device) if bias else None
+    d["ids"], d["topk_w"] = softmax_topk_routing(M, E, k, seed, f"route{M}", device)
     return d
 
 
