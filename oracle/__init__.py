@@ -23,6 +23,8 @@ other than itself:
     gemm.grouped_gemm       pinned  (constant input, bias, linearity, Fraction brute force)
     gemm.silu / swiglu      pinned  (closed forms and the odd-part identity)
     gemm.relu2              pinned  (closed forms; constant-input GEMM epilogue)
+    gemm.build_block_mapping pinned (hand-worked example; every row in exactly one block)
+    gemm.grouped_gemm_per_token pinned (constant input with bias, scalar loop, empty groups)
     gemm.combine            pinned  (identity at k = 1, hand-worked example, linearity)
     wgrad.wgrad             pinned  (constant input, linearity, zero/PAD slots, Fraction brute force)
     layer.w4a16_layer       pinned  (composition of pinned functions; padded == unpadded)

@@ -156,3 +156,60 @@ def combine(c, topk_w, top_k):
     for j in range(top_k):
         y += w[:, j:j + 1] * c[:, j, :]
     return y
+
+
+def build_block_mapping(group_sizes, block_m, max_blocks):
+    """The expert block mapping of a group_sizes interface (ROCm/aiter PR
+    #5310, Notes: _build_block_mapping shared by the GEMM wrappers; second
+    review: block_expert_ids / block_token_offsets / block_token_ends, -1
+    sentinels in the padded tail). Expert e owns rows [o_e, o_e + g_e) with
+    o_e = g_0 + ... + g_{e-1}, cut into ceil(g_e / block_m) blocks in expert
+    order; block i of e starts at o_e + i * block_m and its segment ends at
+    o_e + g_e. Blocks past the used ones: expert -1, offset = end = total rows.
+
+    Returns (expert_ids, token_offsets, token_ends), int64 [max_blocks].
+    Pinned: tests/test_oracle_gemm.py (hand-worked example, empty groups,
+    every row in exactly one block).
+    """
+    g = np.asarray(group_sizes, dtype=np.int64)
+    total = int(g.sum())
+    eid = np.full(max_blocks, -1, dtype=np.int64)
+    beg = np.full(max_blocks, total, dtype=np.int64)
+    end = np.full(max_blocks, total, dtype=np.int64)
+    b, o = 0, 0
+    for e, n in enumerate(g):
+        for i in range(-(-int(n) // block_m)):
+            assert b < max_blocks, "max_blocks too small"
+            eid[b], beg[b], end[b] = e, o + i * block_m, o + n
+            b += 1
+        o += int(n)
+    return eid, beg, end
+
+
+def grouped_gemm_per_token(a_codes, a_scale, w, w_scale, group_sizes, bias=None):
+    """Per-token-scaled FP8 grouped GEMM over expert-contiguous rows (ROCm/
+    aiter PR #5310, Summary: moe_gemm_per_token, per-token activation scales
+    and per-expert weight scales applied after the FP8 dot product, a
+    group_sizes interface; Tests & Benchmarks: a bias variant):
+        C[r, n] = (sum_k dec(A[r, k]) dec(W[e, n, k])) * a_scale[r] * w_scale[e] + bias[e, n]
+    for the rows r of expert e's segment. a_codes E4M3 [R, K]; a_scale
+    float [R]; w E4M3 [E, N, K]; w_scale float [E]; bias bf16 bits [E, N] or
+    None. Returns float64 [R, N].
+    Pinned: tests/test_oracle_gemm.py (constant input, a scalar loop on a tiny
+    case, empty groups).
+    """
+    g = np.asarray(group_sizes, dtype=np.int64)
+    a_s = np.asarray(a_scale, dtype=np.float64)
+    w_s = np.asarray(w_scale, dtype=np.float64)
+    R = int(g.sum())
+    C = np.zeros((R, w.shape[1]), dtype=np.float64)
+    o = 0
+    for e, n in enumerate(g):
+        if n:
+            rows = slice(o, o + int(n))
+            acc = e4m3_to_f64(a_codes[rows]) @ e4m3_to_f64(w[e]).T
+            C[rows] = acc * a_s[rows, None] * w_s[e]
+            if bias is not None:
+                C[rows] += bf16_to_f64(bias[e])[None, :]
+        o += int(n)
+    return C

@@ -229,3 +229,62 @@ def test_nan_scale_propagates_to_its_rows_only():
     ws[0, 2, 1] = 0xFF
     C, _ = gemm.grouped_gemm(x, k, w, "e4m3", ws, ids, E)
     assert np.all(np.isnan(C[:, 2])) and not np.any(np.isnan(C[:, [0, 1, 3]]))
+
+
+def test_block_mapping_example_and_cover():
+    eid, beg, end = gemm.build_block_mapping([3, 0, 5, 1], 2, 8)
+    assert eid.tolist() == [0, 0, 2, 2, 2, 3, -1, -1]
+    assert beg.tolist() == [0, 2, 3, 5, 7, 8, 9, 9]
+    assert end.tolist() == [3, 3, 8, 8, 8, 9, 9, 9]
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        g = rng.integers(0, 9, size=int(rng.integers(1, 12)))
+        bm = int(rng.integers(1, 6))
+        mb = int(g.sum()) // bm + len(g) + 1
+        eid, beg, end = gemm.build_block_mapping(g, bm, mb)
+        covered = np.zeros(int(g.sum()), dtype=int)
+        offs = np.concatenate([[0], np.cumsum(g)])
+        for b in range(mb):
+            if eid[b] >= 0:
+                e = eid[b]
+                assert offs[e] <= beg[b] < end[b] == offs[e + 1]
+                covered[beg[b]:min(beg[b] + bm, end[b])] += 1
+        assert (covered == 1).all()
+
+
+def test_per_token_gemm_constant_input_and_bias():
+    # A = W = 1.0 (E4M3 0x38): the dot product is K, times both scales, plus bias
+    E, N, K = 3, 4, 64
+    g = [2, 0, 3]
+    a = np.full((5, K), 0x38, dtype=np.uint8)
+    a_s = np.array([1.0, 0.5, 2.0, 0.25, 4.0])
+    w = np.full((E, N, K), 0x38, dtype=np.uint8)
+    w_s = np.array([0.5, 7.0, 3.0])
+    bias = _bf16_bits(np.array([[1.0] * N, [0.0] * N, [-2.0] * N]))
+    C = gemm.grouped_gemm_per_token(a, a_s, w, w_s, g, bias=bias)
+    expect = np.array([K * 1.0 * 0.5 + 1, K * 0.5 * 0.5 + 1, K * 2.0 * 3 - 2, K * 0.25 * 3 - 2, K * 4.0 * 3 - 2])
+    np.testing.assert_array_equal(C, np.repeat(expect[:, None], N, axis=1))
+    assert gemm.grouped_gemm_per_token(a[:0], a_s[:0], w, w_s, [0, 0, 0]).shape == (0, N)
+
+
+def test_per_token_gemm_scalar_loop():
+    rng = np.random.default_rng(10)
+    E, N, K = 3, 5, 32
+    g = [1, 3, 0]
+    codes = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    a = rng.choice(codes, size=(4, K)).astype(np.uint8)
+    w = rng.choice(codes, size=(E, N, K)).astype(np.uint8)
+    a_s, w_s = rng.random(4), rng.random(E)
+    C = gemm.grouped_gemm_per_token(a, a_s, w, w_s, g)
+
+    def dec(c):  # E4M3 from its definition: sign, 4-bit exponent (bias 7), 3-bit mantissa
+        c = int(c)
+        e, m = (c >> 3) & 15, c & 7
+        v = m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        return -v if c & 0x80 else v
+    owner = [0, 1, 1, 1]
+    for r in range(4):
+        e = owner[r]
+        for n in range(N):
+            acc = sum(dec(a[r, k]) * dec(w[e, n, k]) for k in range(K))
+            assert C[r, n] == pytest.approx(acc * a_s[r] * w_s[e], rel=1e-12)
