@@ -244,7 +244,8 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, moe_stream_t stream);
  * (moe_packed_sizes returns both expert strides). When k % 64 == 32 the
  * unused upper half of the last K block is written as zero codes and zero
  * scale bytes; no kernel reads it. w_scale / w_scale_out are NULL for
- * MOE_BF16. Input and output must not overlap. Requirements as for
+ * MOE_BF16, and may both be NULL for MOE_E4M3 (codes alone: the weights of
+ * moe_grouped_gemm_per_token). Input and output must not overlap. Requirements as for
  * moe_grouped_gemm's weights (k % 32 == 0, 16-byte aligned rows). */
 moe_status moe_pack_weights(int32_t w_dtype, int32_t num_experts, int64_t n, int64_t k,
                             const void* w, int64_t w_stride_e, int64_t w_ld,
@@ -313,6 +314,81 @@ moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad
                      int64_t num_tokens, int32_t top_k, int32_t num_experts,
                      int64_t n, int64_t k, int32_t block_m, int64_t max_blocks,
                      float* dw, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Expert block mapping of the group_sizes interface ([AIT] Summary:
+ * moe_gemm_per_token takes a 1-D tensor of per-expert row counts; [AIT]
+ * Notes: one block-mapping builder shared by the GEMM wrappers; [AIT] second
+ * review: block_expert_ids / block_token_offsets / block_token_ends, -1
+ * sentinel blocks past the used ones).
+ * Rows are grouped by expert: expert e owns rows [o_e, o_e + g_e) with
+ * g_e = group_sizes[e] and o_e = g_0 + ... + g_{e-1}. Its ceil(g_e / block_m)
+ * blocks follow in expert order; block i of e has
+ *   block_expert_ids[b] = e, block_token_offsets[b] = o_e + i * block_m,
+ *   block_token_ends[b] = o_e + g_e (the end of e's rows, not of the block).
+ * Every block b past the used ones: expert -1, offset = end = total rows.
+ * group_sizes (device) int32 [num_experts]; the three outputs (device) int32
+ * [max_blocks]; total_rows (device) int32 [1] or NULL receives
+ * sum(max(g_e, 0)) (capped at 2^31 - 1), which the caller may compare with
+ * rows. The counts are expected to sum to rows; negative counts count as 0
+ * and segments are clipped to [0, rows), so a mapping never names a row at
+ * or past rows (blocks beyond max_blocks are dropped).
+ * Requirements: 1 <= num_experts <= 1024, 0 <= rows < 2^31,
+ * 1 <= block_m <= 256, max_blocks >= moe_align_max_blocks(rows, num_experts,
+ * block_m) (the same bound as moe_align: both cut per-expert groups into
+ * blocks), max_blocks * block_m < 2^31. One workgroup, no workspace.
+ * ---------------------------------------------------------------------- */
+moe_status moe_block_mapping(const int32_t* group_sizes, int32_t num_experts, int64_t rows, int32_t block_m,
+                             int32_t* block_expert_ids, int32_t* block_token_offsets,
+                             int32_t* block_token_ends, int64_t max_blocks, int32_t* total_rows,
+                             moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-token-scaled FP8 grouped GEMM ([AIT] Summary: moe_gemm_per_token,
+ * E4M3 operands, per-token activation scales and per-expert weight scales
+ * applied after the fp8 dot-product accumulation, a group_sizes interface;
+ * [AIT] Tests & Benchmarks: a bias variant, empty-token guards).
+ * For every block b with 0 <= e = block_expert_ids[b] < num_experts and
+ * every row r in [block_token_offsets[b], min(+block_m, block_token_ends[b], rows)):
+ *   C[r][n] = bf16( (sum_k dec(A[r][k]) * dec(W[e][n][k])) * a_scale[r] * w_scale[e]
+ *                   + bias[e][n] )
+ * with the dot product accumulated in fp32 (each E4M3 product is exact in
+ * fp32), the two scales multiplied in fp32 and one bf16 rounding
+ * (nearest-even). Rows no block covers are not written.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t rows;            /* R: rows of A and C, the sum of the group sizes */
+  int32_t num_experts;     /* E */
+  int64_t n;               /* N: weight rows per expert, the output width */
+  int64_t k;               /* K: contraction length */
+  const uint8_t* a;        /* (device) E4M3 codes [R][K], row r at a + r * a_ld */
+  int64_t a_ld;            /* bytes, >= k, a multiple of 16 */
+  const float* a_scale;    /* (device) fp32 [R]: the scale of each row of A */
+  int32_t w_layout;        /* MOE_LAYOUT_ROWS or MOE_LAYOUT_KBLOCK (E4M3 codes
+                              only; moe_pack_weights with both scale pointers
+                              NULL makes the latter) */
+  const uint8_t* w;        /* (device) E4M3 codes of [E][N][K] */
+  int64_t w_stride_e;      /* bytes; ROWS: >= n * w_ld; KBLOCK: >= ceil(k/64) * w_ld */
+  int64_t w_ld;            /* bytes; ROWS: row stride >= k; KBLOCK: K-block stride >= 64n */
+  const float* w_scale;    /* (device) fp32 [E]: one scale per expert */
+  const void* bias;        /* (device) bf16 [E][N] or NULL */
+  int64_t bias_stride_e;   /* in elements; any non-negative strides */
+  int64_t bias_stride_n;
+  void* c;                 /* (device) bf16 [R][N], row r at c + r * c_ld */
+  int64_t c_ld;            /* >= n, in elements */
+  const int32_t* block_expert_ids;    /* (device) from moe_block_mapping */
+  const int32_t* block_token_offsets; /* (device) */
+  const int32_t* block_token_ends;    /* (device) */
+  int32_t block_m;         /* must equal moe_gemm_block_m(MOE_E4M3, MOE_E4M3, rows) */
+  int64_t max_blocks;      /* length of the mapping, >= moe_align_max_blocks(rows, E, block_m) */
+} moe_per_token_args;
+
+/* Requirements: k % 16 == 0 (k % 32 == 0 for KBLOCK); w_ld, w_stride_e
+ * multiples of 16; a and w 16-byte aligned, c 2-byte, the scales 4-byte; A
+ * and one expert's weights each span less than 2 GB. rows = 0 or an empty
+ * mapping launch nothing. Otherwise MOE_ERR_INVALID_ARGUMENT or
+ * MOE_ERR_UNSUPPORTED, nothing launched. No workspace. */
+moe_status moe_grouped_gemm_per_token(const moe_per_token_args* args, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

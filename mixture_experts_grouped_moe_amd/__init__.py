@@ -19,7 +19,8 @@ __all__ = [
     "moe_bucket_round_up", "moe_bucket_enumerate", "moe_padding_supported",
     "moe_align_max_blocks", "moe_gemm_block_m", "moe_wgrad_block_m", "moe_decode_max_tokens",
     "moe_align", "moe_grouped_gemm", "moe_grouped_gemm_prepare", "moe_combine", "moe_wgrad",
-    "moe_quantize_mxfp8",
+    "moe_quantize_mxfp8", "moe_block_mapping", "moe_grouped_gemm_per_token",
+    "moe_grouped_gemm_per_token_prepare",
     "moe_pack_weights", "moe_packed_sizes", "PackedWeights", "MOE_LAYOUT_ROWS", "MOE_LAYOUT_KBLOCK",
     "moe_w4a16_layer", "moe_relu2_layer",
     "LIB_PATH",
@@ -60,6 +61,22 @@ class MoeGemmArgs(ctypes.Structure):
     ]
 
 
+class MoePerTokenArgs(ctypes.Structure):
+    """ctypes mirror of moe_per_token_args (include/moe.h)."""
+    _fields_ = [
+        ("rows", ctypes.c_int64), ("num_experts", ctypes.c_int32),
+        ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("a", ctypes.c_void_p), ("a_ld", ctypes.c_int64), ("a_scale", ctypes.c_void_p),
+        ("w_layout", ctypes.c_int32), ("w", ctypes.c_void_p),
+        ("w_stride_e", ctypes.c_int64), ("w_ld", ctypes.c_int64), ("w_scale", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p), ("bias_stride_e", ctypes.c_int64), ("bias_stride_n", ctypes.c_int64),
+        ("c", ctypes.c_void_p), ("c_ld", ctypes.c_int64),
+        ("block_expert_ids", ctypes.c_void_p), ("block_token_offsets", ctypes.c_void_p),
+        ("block_token_ends", ctypes.c_void_p),
+        ("block_m", ctypes.c_int32), ("max_blocks", ctypes.c_int64),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -84,6 +101,8 @@ def _load():
         "moe_wgrad": (i32, [vp, i64, vp, i64, vp, vp, vp, i64, i32, i32, i64, i64, i32, i64, vp, vp]),
         "moe_pack_weights": (i32, [i32, i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp, vp]),
         "moe_packed_sizes": (i32, [i32, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "moe_block_mapping": (i32, [vp, i32, i64, i32, vp, vp, vp, i64, vp, vp]),
+        "moe_grouped_gemm_per_token": (i32, [ctypes.POINTER(MoePerTokenArgs), vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -194,7 +213,8 @@ class PackedWeights:
 def moe_pack_weights(w, w_dtype, w_scale=None, stream=None):
     """Repack rows-layout weights [E, N, K] (and E8M0 scales [E, N, K/32])
     into the K-block layout; returns a PackedWeights. A copy, run once when
-    the weights are loaded."""
+    the weights are loaded. E4M3 codes may come without scales (the weights
+    of moe_grouped_gemm_per_token)."""
     wd = _W_DTYPES[w_dtype]
     _need(w, "w", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 3)
     E, N = w.shape[0], w.shape[1]
@@ -203,7 +223,7 @@ def moe_pack_weights(w, w_dtype, w_scale=None, stream=None):
     R = 32 if w_dtype == "e2m1x2" else 64
     codes = torch.empty((E, nblk, N, R), dtype=w.dtype, device=w.device)
     scales = None
-    if w_dtype != "bf16":
+    if w_dtype != "bf16" and not (w_dtype == "e4m3" and w_scale is None):
         _need(w_scale, "w_scale", torch.uint8, 3)
         if tuple(w_scale.shape) != (E, N, K // 32):
             raise ValueError(f"w_scale must be [E, N, K/32] = {(E, N, K // 32)}")
@@ -347,6 +367,103 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     def call():
         _check(lib.moe_grouped_gemm(ref, st))
         return keep[4]
+    call.args = g
+    return call, out
+
+
+def moe_block_mapping(group_sizes, rows, block_m=None, out=None, stream=None):
+    """Expert block mapping of per-expert row counts (the group_sizes
+    interface): rows of expert e are [o_e, o_e + g_e), cut into blocks of
+    block_m (default: the per-token GEMM's) in expert order.
+
+    group_sizes: int32 [E] on the device (summing to `rows`). Returns
+    (block_expert_ids, block_token_offsets, block_token_ends, total_rows) as
+    int32 device tensors, -1 / rows / rows past the used blocks; total_rows[0]
+    is the sum of the counts, for callers that want to check it. `out` may
+    give the four preallocated.
+    """
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    if not group_sizes.is_contiguous():
+        raise ValueError("group_sizes must be contiguous")
+    E = group_sizes.shape[0]
+    bm = moe_gemm_block_m("e4m3", rows, MOE_E4M3) if block_m is None else int(block_m)
+    mb = moe_align_max_blocks(int(rows), E, bm)
+    if out is None:
+        dev = group_sizes.device
+        out = tuple(torch.empty(max(mb, 0), dtype=torch.int32, device=dev) for _ in range(3)) + \
+            (torch.empty(1, dtype=torch.int32, device=dev),)
+    eids, offs, ends, total = out
+    if not (eids.numel() == offs.numel() == ends.numel()):
+        raise ValueError("the three mapping arrays must have one length")
+    _check(lib.moe_block_mapping(_ptr(group_sizes), E, int(rows), bm, _ptr(eids), _ptr(offs), _ptr(ends),
+                                 eids.numel(), _ptr(total), _stream(stream)))
+    return eids, offs, ends, total
+
+
+def moe_grouped_gemm_per_token(a, a_scale, w, w_scale, mapping, bias=None, out=None, stream=None):
+    """See moe_grouped_gemm_per_token_prepare; this builds the call and runs it once."""
+    call, out = moe_grouped_gemm_per_token_prepare(a, a_scale, w, w_scale, mapping, bias=bias, out=out,
+                                                   stream=stream)
+    call()
+    return out
+
+
+def moe_grouped_gemm_per_token_prepare(a, a_scale, w, w_scale, mapping, bias=None, out=None, stream=None):
+    """Per-token-scaled FP8 grouped GEMM over expert-contiguous rows:
+    C[r] = (dec(A[r]) . dec(W[e])^T) * a_scale[r] * w_scale[e] + bias[e].
+
+    a: uint8 E4M3 codes [R, K]; a_scale: float32 [R]; w: uint8 E4M3 codes
+    [E, N, K], or a PackedWeights of them (e4m3, no scales); w_scale: float32
+    [E]; mapping: moe_block_mapping's result for these R rows; bias: bf16
+    [E, N] (any strides). C is bf16 [R, N]. Returns (call, C) like
+    moe_grouped_gemm_prepare.
+    """
+    _need(a, "a", torch.uint8, 2)
+    _need(a_scale, "a_scale", torch.float32, 1)
+    _need(w_scale, "w_scale", torch.float32, 1)
+    R, K = a.shape
+    if a_scale.numel() < R or not a_scale.is_contiguous() or not w_scale.is_contiguous():
+        raise ValueError("a_scale must be a contiguous [R], w_scale a contiguous [E]")
+    packed = isinstance(w, PackedWeights)
+    if packed:
+        if w.w_dtype != "e4m3" or w.scales is not None or w.k != K:
+            raise ValueError("packed weights must be e4m3 codes without scales, with a's K")
+        E, N, w_t = w.num_experts, w.n, w.codes
+        _need(w_t, "w.codes", torch.uint8, 4)
+    else:
+        w_t = w
+        _need(w_t, "w", torch.uint8, 3)
+        E, N = w_t.shape[0], w_t.shape[1]
+        if w_t.shape[2] != K:
+            raise ValueError("w's K does not match a's")
+    if w_scale.numel() < E:
+        raise ValueError("w_scale must hold one scale per expert")
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or not bias.is_cuda or tuple(bias.shape) != (E, N):
+            raise TypeError("bias must be a bf16 [E, N] device tensor")
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.bfloat16, device=a.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if out.shape[0] < R or out.shape[1] < N:
+        raise ValueError(f"out must be at least [{R}, {N}]")
+    eids, offs, ends = mapping[0], mapping[1], mapping[2]
+    g = MoePerTokenArgs()
+    g.rows, g.num_experts, g.n, g.k = R, E, N, K
+    g.a, g.a_ld, g.a_scale = a.data_ptr(), a.stride(0), a_scale.data_ptr()
+    g.w_layout = MOE_LAYOUT_KBLOCK if packed else MOE_LAYOUT_ROWS
+    g.w, g.w_stride_e, g.w_ld, g.w_scale = w_t.data_ptr(), w_t.stride(0), w_t.stride(1), w_scale.data_ptr()
+    if bias is not None:
+        g.bias, g.bias_stride_e, g.bias_stride_n = bias.data_ptr(), bias.stride(0), bias.stride(1)
+    g.c, g.c_ld = out.data_ptr(), out.stride(0)
+    g.block_expert_ids, g.block_token_offsets, g.block_token_ends = eids.data_ptr(), offs.data_ptr(), ends.data_ptr()
+    g.block_m, g.max_blocks = moe_gemm_block_m("e4m3", R, MOE_E4M3), eids.numel()
+    st = _stream(stream)
+    ref = ctypes.byref(g)
+    keep = (a, a_scale, w_t, w_scale, bias, out, mapping)
+
+    def call():
+        _check(lib.moe_grouped_gemm_per_token(ref, st))
+        return keep[5]
     call.args = g
     return call, out
 

@@ -143,6 +143,99 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   }
 }
 
+// Expert block mapping of the group_sizes interface (ROCm/aiter PR #5310,
+// Summary: moe_gemm_per_token takes a 1-D tensor of per-expert row counts;
+// Notes: one block-mapping builder serves the GEMM wrappers; second review:
+// block_expert_ids / block_token_offsets / block_token_ends with -1 sentinel
+// blocks). Expert e owns rows [o_e, o_e + g_e), o_e the exclusive prefix sum
+// of the counts; its ceil(g_e / B) blocks follow in expert order, block i
+// starting at o_e + i * B, all ending at o_e + g_e. Negative counts count as
+// zero, and segments are clipped to [0, rows), so no block ever names a row
+// past the caller's buffers. One workgroup, one expert per thread: two
+// 64-bit/32-bit scans, then a binary search per block.
+__global__ __launch_bounds__(kAlignThreads) void block_map_kernel(
+    const int32_t* __restrict__ group_sizes, int32_t E, int32_t B, int32_t rows,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ offsets, int32_t* __restrict__ ends,
+    int32_t max_blocks, int32_t* __restrict__ total_out) {
+  __shared__ int32_t seg_beg[kAlignMaxExperts];
+  __shared__ int32_t seg_end[kAlignMaxExperts];
+  __shared__ int32_t blk_beg[kAlignMaxExperts];
+  __shared__ long long wave_rows[kAlignWaves];
+  __shared__ int32_t wave_blks[kAlignWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+
+  // 1. row segments: exclusive scan of the counts in 64 bits
+  const long long g = tid < E ? (long long)max(group_sizes[tid], 0) : 0ll;
+  long long incl = g;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const long long v = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += v;
+  }
+  if (lane == kWave - 1) wave_rows[wave] = incl;
+  __syncthreads();
+  long long before = 0, sum = 0;
+  for (int w = 0; w < kAlignWaves; ++w) {
+    if (w < wave) before += wave_rows[w];
+    sum += wave_rows[w];
+  }
+  const long long o = before + incl - g;
+  const int32_t beg = (int32_t)min(o, (long long)rows);
+  const int32_t end = (int32_t)min(o + g, (long long)rows);
+  const int32_t total = (int32_t)min(sum, (long long)rows);
+
+  // 2. block counts and their exclusive scan
+  const int32_t nb = (end - beg + B - 1) / B;
+  int32_t bincl = nb;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t v = __shfl_up(bincl, d, kWave);
+    if (lane >= d) bincl += v;
+  }
+  if (lane == kWave - 1) wave_blks[wave] = bincl;
+  __syncthreads();
+  int32_t bbefore = 0, nblocks = 0;
+  for (int w = 0; w < kAlignWaves; ++w) {
+    if (w < wave) bbefore += wave_blks[w];
+    nblocks += wave_blks[w];
+  }
+  if (tid < E) {
+    seg_beg[tid] = beg;
+    seg_end[tid] = end;
+    blk_beg[tid] = bbefore + bincl - nb;
+  }
+  if (tid == 0 && total_out != nullptr) *total_out = (int32_t)min(sum, (long long)INT32_MAX);
+  __syncthreads();
+
+  // 3. per block: the largest e with blk_beg[e] <= b owns it (and is not
+  //    empty while b < nblocks); sentinels past the used blocks
+  for (int b = tid; b < max_blocks; b += kAlignThreads) {
+    int32_t e = -1, off = total, en = total;
+    if (b < nblocks) {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (blk_beg[mid] <= b) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+      off = seg_beg[e] + (b - blk_beg[e]) * B;
+      en = seg_end[e];
+    }
+    expert_ids[b] = e;
+    offsets[b] = off;
+    ends[b] = en;
+  }
+}
+
+hipError_t launch_block_map(const int32_t* group_sizes, int32_t E, int32_t B, int32_t rows, int32_t* expert_ids,
+                            int32_t* offsets, int32_t* ends, int32_t max_blocks, int32_t* total_out,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(block_map_kernel, dim3(1), dim3(kAlignThreads), 0, stream, group_sizes, E, B, rows,
+                     expert_ids, offsets, ends, max_blocks, total_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_align(const int32_t* ids, int32_t S, int32_t E, int32_t B,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* post_pad,
                         int32_t max_blocks, hipStream_t stream) {

@@ -231,7 +231,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   const int64_t grid_guess = a.max_blocks * ((out_w + 7) / 8);
   if (grid_guess >= (int64_t)UINT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
 
-  moe::GemmParams p;
+  moe::GemmParams p{};
   p.a = static_cast<const uint16_t*>(a.a);
   p.a_ld = a.a_ld;
   p.a_rows = a_rows;
@@ -260,6 +260,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   p.K = (int32_t)a.k;
   p.max_blocks = (int32_t)a.max_blocks;
   p.relu2 = a.epilogue == MOE_EPILOGUE_RELU2 ? 1 : 0;
+  p.E = a.num_experts;
   const bool bias = a.bias != nullptr;
   if (a_f8) return hip_status(moe::launch_gemm_f8(p, swiglu, bias, (hipStream_t)stream), "moe_grouped_gemm launch");
   const bool decode = a.num_tokens <= kDecodeMaxTokens;
@@ -289,7 +290,9 @@ moe_status moe_pack_weights(int32_t w_dtype, int32_t num_experts, int64_t n, int
   const int64_t row_units = w_dtype == MOE_E2M1X2 ? k / 2 : k;
   if (w_ld < row_units || w_stride_e < n * w_ld || (w_ld * eb) % 16 != 0 || (w_stride_e * eb) % 16 != 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "w strides must cover the rows and be multiples of 16 bytes");
-  if (w_dtype != MOE_BF16) {
+  if (w_dtype == MOE_E4M3 && w_scale == nullptr && w_scale_out == nullptr) {
+    // E4M3 codes without block scales (the per-token path's weights)
+  } else if (w_dtype != MOE_BF16) {
     if (w_scale == nullptr || w_scale_out == nullptr)
       return fail(MOE_ERR_INVALID_ARGUMENT, "scales are required for block-scaled weights");
     if (w_scale_ld < k / 32 || w_scale_stride_e < n * w_scale_ld)
@@ -402,6 +405,106 @@ moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad
   p.tiles_k = 0;
   p.dw = dw;
   return hip_status(moe::launch_wgrad(p, (hipStream_t)stream), "moe_wgrad launch");
+}
+
+moe_status moe_block_mapping(const int32_t* group_sizes, int32_t num_experts, int64_t rows, int32_t block_m,
+                             int32_t* block_expert_ids, int32_t* block_token_offsets, int32_t* block_token_ends,
+                             int64_t max_blocks, int32_t* total_rows, moe_stream_t stream) {
+  if (num_experts < 1 || num_experts > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "need 1 <= num_experts <= 1024");
+  if (rows < 0 || rows >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31)");
+  if (block_m < 1 || block_m > 256) return fail(MOE_ERR_INVALID_ARGUMENT, "need 1 <= block_m <= 256");
+  const int64_t need = moe_align_max_blocks(rows, num_experts, block_m);
+  if (max_blocks < need)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks %lld < required %lld", (long long)max_blocks,
+                (long long)need);
+  if (max_blocks * block_m >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks * block_m too large");
+  if (group_sizes == nullptr ||
+      (max_blocks > 0 && (block_expert_ids == nullptr || block_token_offsets == nullptr || block_token_ends == nullptr)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_block_map(group_sizes, num_experts, block_m, (int32_t)rows, block_expert_ids,
+                                          block_token_offsets, block_token_ends, (int32_t)max_blocks, total_rows,
+                                          (hipStream_t)stream),
+                    "moe_block_mapping launch");
+}
+
+moe_status moe_grouped_gemm_per_token(const moe_per_token_args* g, moe_stream_t stream) {
+  if (g == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "args is null");
+  const moe_per_token_args& a = *g;
+  if (a.rows < 0 || a.rows >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31)");
+  if (a.num_experts < 1 || a.num_experts > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "need 1 <= num_experts <= 1024");
+  if (a.n < 1 || a.n >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "n out of range");
+  if (a.k < 16 || a.k % 16 != 0 || a.k >= INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "k (%lld) must be a positive multiple of 16", (long long)a.k);
+  if (a.a_ld < a.k || a.a_ld % 16 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "a_ld must be >= k and a multiple of 16");
+  if (a.w_layout != MOE_LAYOUT_ROWS && a.w_layout != MOE_LAYOUT_KBLOCK)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown w_layout %d", a.w_layout);
+  const bool kblock = a.w_layout == MOE_LAYOUT_KBLOCK;
+  if (kblock && a.k % 32 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "the K-block layout needs k % 32 == 0");
+  const int64_t nblk = (a.k + 63) / 64;
+  if (a.w_ld % 16 != 0 || a.w_stride_e % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld and w_stride_e must be multiples of 16 bytes");
+  if (!kblock) {
+    if (a.w_ld < a.k) return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a row");
+    if (a.w_stride_e < a.n * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < n * w_ld");
+  } else {
+    if (a.w_ld < a.n * 64) return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a K block of n rows");
+    if (a.w_stride_e < nblk * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < ceil(k/64) * w_ld");
+  }
+  if (a.bias != nullptr && (a.bias_stride_e < 0 || a.bias_stride_n < 0))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "negative bias stride");
+  if (a.c_ld < a.n) return fail(MOE_ERR_INVALID_ARGUMENT, "c_ld must be >= n");
+  if (a.block_m != moe::gemm_block_m_large())
+    return fail(MOE_ERR_INVALID_ARGUMENT, "block_m %d, expected %d", a.block_m, moe::gemm_block_m_large());
+  const int64_t need = moe_align_max_blocks(a.rows, a.num_experts, a.block_m);
+  if (a.max_blocks < need)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks %lld < required %lld", (long long)a.max_blocks,
+                (long long)need);
+  if (a.max_blocks * a.block_m >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks too large");
+  if (a.rows > 0 && (a.a == nullptr || a.a_scale == nullptr || a.w == nullptr || a.w_scale == nullptr ||
+                     a.c == nullptr || a.block_expert_ids == nullptr || a.block_token_offsets == nullptr ||
+                     a.block_token_ends == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (((uintptr_t)a.a | (uintptr_t)a.w) % 16 != 0 || (uintptr_t)a.c % 2 != 0 ||
+      ((uintptr_t)a.a_scale | (uintptr_t)a.w_scale) % 4 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "a and w must be 16-byte aligned, c 2-byte, the scales 4-byte");
+  constexpr int64_t kBufMax = (int64_t)0x80000000;
+  const int64_t w_span = (kblock ? nblk : a.n) * a.w_ld;
+  if (a.rows * a.a_ld >= kBufMax || w_span >= kBufMax)
+    return fail(MOE_ERR_UNSUPPORTED, "A or one expert's weights span 2 GB or more");
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  if (a.rows == 0 || a.max_blocks == 0) return ok();
+  if (a.max_blocks * ((a.n + 511) / 512) >= (int64_t)UINT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
+
+  moe::GemmParams p{};
+  p.a = static_cast<const uint16_t*>(static_cast<const void*>(a.a));
+  p.a_ld = a.a_ld;
+  p.a_rows = a.rows;
+  p.a_row_div = 1;
+  p.w = a.w;
+  p.w_stride_e = a.w_stride_e;
+  p.w_row = kblock ? 64 : a.w_ld;
+  p.w_blk = kblock ? a.w_ld : 64;
+  p.w_span = w_span;
+  p.bias = static_cast<const uint16_t*>(a.bias);
+  p.bias_se = a.bias_stride_e;
+  p.bias_sn = a.bias_stride_n;
+  p.c = static_cast<uint16_t*>(a.c);
+  p.c_ld = a.c_ld;
+  p.expert_ids = a.block_expert_ids;
+  p.blk_off = a.block_token_offsets;
+  p.blk_end = a.block_token_ends;
+  p.tok_scale = a.a_scale;
+  p.exp_scale = a.w_scale;
+  p.S = (int32_t)a.rows;
+  p.N = (int32_t)a.n;
+  p.K = (int32_t)a.k;
+  p.E = a.num_experts;
+  p.max_blocks = (int32_t)a.max_blocks;
+  return hip_status(moe::launch_gemm_per_token(p, a.bias != nullptr, (hipStream_t)stream),
+                    "moe_grouped_gemm_per_token launch");
 }
 
 }  // extern "C"

@@ -22,6 +22,15 @@
 //    0-15 of both lane halves (h = 0) or bytes 16-31 (h = 1). So a lane reads
 //    16-byte units h and 2 + h of its row's 64-byte step piece.
 //  * fp32 accumulators, bias and SwiGLU in the epilogue, one bf16 rounding.
+//
+// The same kernel in per-token mode is moe_gemm_per_token of that PR
+// (Summary: E4M3 operands with one fp32 scale per activation row and one per
+// expert, both applied after the fp8 dot product; a group_sizes interface):
+// the routing block is a run of consecutive rows of one expert taken from the
+// block mapping (block_expert_ids / block_token_offsets / block_token_ends of
+// the second review), the MFMA's scale bytes are the constant 127 (2^0), no
+// scale bytes are loaded, and the epilogue multiplies the fp32 accumulator by
+// a_scale[row] * w_scale[e] before the bias.
 #include "gemm_util.h"
 
 namespace moe {
@@ -32,7 +41,9 @@ constexpr int kF8RowBytes = 64;                 // one row's codes per K step
 
 typedef int f8_v8i __attribute__((ext_vector_type(8)));
 
-template <bool SWIGLU, bool BIAS>
+constexpr int kE8M0One = 127;                   // E8M0 code of 2^0
+
+template <bool SWIGLU, bool BIAS, bool PT>
 __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmParams p) {
   constexpr int NT = kF8NT, STAGES = kF8Stages, RB = kF8RowBytes;
   constexpr int WN = NT * 32, BN = kWavesN * WN;
@@ -42,7 +53,8 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
   constexpr int W_BYTES = BN * RB;                  // 32 KB
   constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // 1
   constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;  // 8
-  constexpr int LOADS = A_LOADS + W_LOADS + NT + 2; // + weight and activation scale bytes
+  constexpr int SC = PT ? 1 : NT + 2;               // scale-byte registers per stage (PT: none used)
+  constexpr int LOADS = A_LOADS + W_LOADS + (PT ? 0 : NT + 2); // + weight and activation scale bytes
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
   static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
   constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
@@ -53,7 +65,14 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
   const int b = L % p.max_blocks;
   const int tile_n = L / p.max_blocks;
   const int e = p.expert_ids[b];
-  if (e < 0) return;  // sentinel block
+  if (e < 0 || e >= p.E) return;  // sentinel block
+
+  // PT: rows row0 .. row_end - 1 of A and C (at most 64, clipped to S)
+  int row0 = 0, row_end = 0;
+  if constexpr (PT) {
+    row0 = max(p.blk_off[b], 0);
+    row_end = min(min(p.blk_end[b], p.S), row0 + min(p.S - row0, kBM));
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -61,10 +80,20 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
   const int wn = wave % kWavesN;
   const int l32 = lane % 32, h = lane / 32;
   const int32_t* blk_slots = p.sorted + (int64_t)b * kBM;
+  // slot (output row) of block row r: S (= PAD) for none
+  auto slot_of = [&](int r) -> int {
+    if constexpr (PT) return row0 + r < row_end ? row0 + r : p.S;
+    else return blk_slots[r];
+  };
+  // A row of slot s
+  auto a_row = [&](int s) -> int64_t {
+    if constexpr (PT) return s;
+    else return s / p.a_row_div;
+  };
 
   // a wave with only PAD rows or only columns past N computes nothing (it
   // still loads its share and joins every barrier)
-  const bool rows_live = __ballot(blk_slots[lane] < p.S) != 0;
+  const bool rows_live = __ballot(slot_of(lane) < p.S) != 0;
   const bool cols_live = tile_w_row<NT, SWIGLU>(wn * WN, tile_n, p.N) >= 0;
   const bool wave_live = rows_live && cols_live;
 
@@ -86,9 +115,9 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
   for (int i = 0; i < A_LOADS; ++i) {
     const int q = (wave * A_LOADS + i) * 64 + lane;
     const int row = q / U, u = swz<U>(row, q % U);
-    const int s = blk_slots[row];
+    const int s = slot_of(row);
     a_k[i] = u * 16;
-    a_off[i] = s < p.S ? (uint32_t)((int64_t)(s / p.a_row_div) * p.a_ld + u * 16) : kOOB;
+    a_off[i] = s < p.S ? (uint32_t)(a_row(s) * p.a_ld + u * 16) : kOOB;
   }
   uint32_t w_off[W_LOADS];
   int w_k[W_LOADS];
@@ -111,15 +140,15 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
   }
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const int s = blk_slots[mt * 32 + l32];
-    as_off[mt] = s < p.S ? (uint32_t)((int64_t)(s / p.a_row_div) * p.as_ld + h) : kOOB;
+    const int s = slot_of(mt * 32 + l32);
+    as_off[mt] = !PT && s < p.S ? (uint32_t)(a_row(s) * p.as_ld + h) : kOOB;
   }
   const uint32_t w_blk = (uint32_t)p.w_blk, ws_blk = (uint32_t)p.ws_blk;
 
   const int nsteps = (p.K + kBK - 1) / kBK;
   const int nsteps_pad = ((nsteps + STAGES - 1) / STAGES) * STAGES;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)&lds[0][0];
-  uint32_t sc[STAGES][NT + 2];  // the step's scale bytes: weights (NT), then activations (2)
+  uint32_t sc[STAGES][SC];  // the step's scale bytes: weights (NT), then activations (2)
 
   // Issue the loads of K step `step` into stage ST; the K tail and the
   // look-ahead steps past the last one take the checked path (lanes past K
@@ -141,10 +170,12 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
     for (int i = 0; i < W_LOADS; ++i)
       dma16(w_rsrc, (full || (live && k0 + w_k[i] < p.K)) ? w_off[i] : kOOB, sw,
             base + A_BYTES + (wave * W_LOADS + i) * 1024);
+    if constexpr (!PT) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sc[ST][nt] = load_byte(s_rsrc, h_live ? ws_off[nt] : kOOB, ss);
+      for (int nt = 0; nt < NT; ++nt) sc[ST][nt] = load_byte(s_rsrc, h_live ? ws_off[nt] : kOOB, ss);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) sc[ST][NT + mt] = load_byte(as_rsrc, h_live ? as_off[mt] : kOOB, sas);
+      for (int mt = 0; mt < 2; ++mt) sc[ST][NT + mt] = load_byte(as_rsrc, h_live ? as_off[mt] : kOOB, sas);
+    }
   };
 
   f32x16_t acc[2][NT];
@@ -178,7 +209,8 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            af[mt], bf, acc[mt][nt], 0, 0, 0, (int)sc[ST][NT + mt], 0, (int)sc[ST][nt]);
+            af[mt], bf, acc[mt][nt], 0, 0, 0, PT ? kE8M0One : (int)sc[ST][NT + mt], 0,
+            PT ? kE8M0One : (int)sc[ST][nt]);
     }
   };
 
@@ -194,11 +226,17 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
       if (wave_live) compute(st);
     });
   }
-  // drain the look-ahead loads, then keep the slot list in stage 0
+  // drain the look-ahead loads, then keep the slot list (PT: each row's
+  // combined scale) in stage 0
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int32_t* s_slot = reinterpret_cast<int32_t*>(&lds[0][0]);
-  if (tid < kBM) s_slot[tid] = blk_slots[tid];
+  float* s_scale = reinterpret_cast<float*>(&lds[0][0]) + kBM;
+  if (tid < kBM) {
+    const int s = slot_of(tid);
+    s_slot[tid] = s;
+    if constexpr (PT) s_scale[tid] = s < p.S ? p.tok_scale[s] * p.exp_scale[e] : 0.0f;
+  }
   __syncthreads();
 
   // ---- epilogue: bias, SwiGLU, one bf16 rounding, store real rows only
@@ -217,11 +255,12 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
       const int s = s_slot[row];
       if (s >= p.S) continue;
       uint16_t* crow = p.c + (int64_t)s * p.c_ld;
+      const float rs = PT ? s_scale[row] : 1.0f;
       if constexpr (!SWIGLU) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           if (my_wrow[nt] >= 0) {
-            const float v = acc[mt][nt][i] + bv[nt];
+            const float v = (PT ? acc[mt][nt][i] * rs : acc[mt][nt][i]) + bv[nt];
             crow[my_wrow[nt]] = (uint16_t)f32_to_bf16_bits(p.relu2 ? relu2_f32(v) : v);
           }
         }
@@ -245,12 +284,21 @@ hipError_t launch_gemm_f8(const GemmParams& p, bool swiglu, bool bias, hipStream
   const int64_t tiles = swiglu ? (p.N / 2 + bn / 2 - 1) / (bn / 2) : (p.N + bn - 1) / bn;
   const dim3 grid((uint32_t)(tiles * p.max_blocks));
   if (swiglu) {
-    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<true, true>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((moe_gemm_f8_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
+    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<true, true, false>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((moe_gemm_f8_kernel<true, false, false>), grid, dim3(kThreads), 0, stream, p);
   } else {
-    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
+    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, false>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, false>), grid, dim3(kThreads), 0, stream, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_per_token(const GemmParams& p, bool bias, hipStream_t stream) {
+  if (p.max_blocks <= 0) return hipSuccess;
+  const int bn = kWavesN * 32 * kF8NT;
+  const dim3 grid((uint32_t)((p.N + bn - 1) / bn * (int64_t)p.max_blocks));
+  if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, true>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, true>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -36,6 +36,14 @@ struct GemmParams {
   int32_t N, K;
   int32_t max_blocks;
   int32_t relu2;       // non-SwiGLU epilogue: store max(pre, 0)^2 instead of pre
+  int32_t E;           // experts: a block naming another expert is skipped
+  // Per-token mode of the fp8 kernel (group_sizes interface): block b covers
+  // rows [blk_off[b], min(blk_off[b] + 64, blk_end[b], S)) of A and C, and
+  // the accumulator is scaled by tok_scale[row] * exp_scale[e].
+  const int32_t* blk_off;
+  const int32_t* blk_end;
+  const float* tok_scale;
+  const float* exp_scale;
 };
 
 struct WgradParams {
@@ -56,10 +64,15 @@ struct WgradParams {
 
 hipError_t launch_align(const int32_t* ids, int32_t S, int32_t E, int32_t B, int32_t* sorted_ids,
                         int32_t* expert_ids, int32_t* post_pad, int32_t max_blocks, hipStream_t stream);
+hipError_t launch_block_map(const int32_t* group_sizes, int32_t E, int32_t B, int32_t rows, int32_t* expert_ids,
+                            int32_t* offsets, int32_t* ends, int32_t max_blocks, int32_t* total_out,
+                            hipStream_t stream);
 hipError_t launch_gemm_large(const GemmParams& p, int wdt, bool swiglu, bool bias, hipStream_t stream);
 hipError_t launch_gemm_decode(const GemmParams& p, int wdt, bool swiglu, bool bias, hipStream_t stream);
 // MXFP8 activations x MXFP8 (E4M3) weights on the scaled fp8 MFMA
 hipError_t launch_gemm_f8(const GemmParams& p, bool swiglu, bool bias, hipStream_t stream);
+// E4M3 x E4M3 with per-token and per-expert fp32 scales over a block mapping
+hipError_t launch_gemm_per_token(const GemmParams& p, bool bias, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* c, int64_t c_ld, const float* w, int64_t T, int32_t top_k,
                           int64_t N, uint16_t* y, int64_t y_ld, hipStream_t stream);
 hipError_t launch_wgrad(const WgradParams& p, hipStream_t stream);

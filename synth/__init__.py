@@ -24,7 +24,7 @@ __all__ = [
     "gen", "bf16_normal", "e4m3_normal", "e2m1_uniform", "e8m0_uniform",
     "softmax_topk_routing", "zipf_topk_routing", "uniform_topk_routing",
     "gemm_case", "config1", "config2", "config3", "config4", "config5", "nemotron_layer",
-    "bits", "draw_token_counts",
+    "bits", "draw_token_counts", "f32_uniform", "zipf_group_sizes", "per_token_case", "config_per_token",
 ]
 
 
@@ -213,6 +213,44 @@ def config5(seed=1005, device="cpu", T=16384, E=256, N=2048, K=7168, k=8):
     d["grad"] = bf16_normal((T * k, N), 1.0, seed, "grad", device)
     d["ids"], d["topk_w"] = uniform_topk_routing(T, E, k, seed, "route", device)
     return d
+
+
+def f32_uniform(shape, lo, hi, seed, tag, device="cpu"):
+    """float32 uniform in [lo, hi)."""
+    g = gen(seed, tag, device)
+    return torch.rand(shape, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
+
+
+def zipf_group_sizes(T, E, k, s, n_empty, seed, tag="route", device="cpu"):
+    """Per-expert row counts (int32 [E], summing to T * k) of the slots of
+    zipf_topk_routing(T, E, k, s, n_empty): the rows of a grouped GEMM over
+    T tokens' k distinct experts, grouped by expert."""
+    ids, _ = zipf_topk_routing(T, E, k, s, n_empty, seed, tag, device)
+    return torch.bincount(ids.reshape(-1).to(torch.int64), minlength=E).to(torch.int32)
+
+
+def per_token_case(group_sizes, N, K, seed, bias=False, device="cpu"):
+    """Inputs of the per-token-scaled FP8 grouped GEMM: A E4M3 codes of
+    N(0, 1) [R, K] with R = sum(group_sizes), per-row scales uniform in
+    [0.5, 2), W E4M3 codes of N(0, 1) [E, N, K], per-expert scales uniform
+    in [0.5, 2), optional bias bf16 N(0, 1) [E, N]."""
+    gs = torch.as_tensor(group_sizes, dtype=torch.int32).to(device)
+    E, R = gs.numel(), int(gs.sum())
+    d = {"E": E, "N": N, "K": K, "R": R, "group_sizes": gs}
+    d["a"] = e4m3_normal((R, K), 1.0, seed, "a", device, chunk_dim0=False)
+    d["a_scale"] = f32_uniform((R,), 0.5, 2.0, seed, "as", device)
+    d["w"] = e4m3_normal((E, N, K), 1.0, seed, "w", device)
+    d["w_scale"] = f32_uniform((E,), 0.5, 2.0, seed, "wsc", device)
+    d["bias"] = bf16_normal((E, N), 1.0, seed, "bias", device) if bias else None
+    return d
+
+
+def config_per_token(seed=1007, bias=False, device="cpu", T=4096, E=256, N=4096, K=7168, n_empty=16):
+    """Per-token FP8 grouped GEMM, DSv4-shaped like the MXFP8 workload: E=256,
+    K=7168, N=4096, R = 4096 tokens x top-8 = 32768 rows grouped by expert,
+    the group sizes those of Zipf(1.1) top-8 routing (the n_empty
+    lowest-ranked experts empty)."""
+    return per_token_case(zipf_group_sizes(T, E, 8, 1.1, n_empty, seed, device=device), N, K, seed, bias, device)
 
 
 def bits(t):

@@ -39,7 +39,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol():
     syms = _declared_symbols()
-    assert len(syms) == 16, syms
+    assert len(syms) == 18, syms
     for name in syms:
         assert hasattr(L, name), name
 
@@ -225,6 +225,63 @@ def test_pack_weights_rejects(no_device):
     assert call(wo=FAKE) == INVALID            # output overlaps the input
     assert call(w=ctypes.c_void_p(0x100008)) == INVALID
     assert call(wd=moe.MOE_FP32) == INVALID
+
+
+def test_block_mapping_rejects(no_device):
+    def call(gs=FAKE, E=8, rows=100, bm=64, e=FAKE, o=FAKE, en=FAKE, mb=None, tot=None):
+        if mb is None:
+            mb = moe.moe_align_max_blocks(rows, E, bm) if rows >= 0 and 1 <= bm <= 256 else 1
+        return L.moe_block_mapping(gs, E, rows, bm, e, o, en, mb, tot, None)
+
+    assert call(E=0) == INVALID
+    assert call(E=1025) == INVALID
+    assert call(rows=-1) == INVALID
+    assert call(rows=1 << 31) == INVALID
+    assert call(bm=0) == INVALID
+    assert call(bm=257) == INVALID
+    assert call(mb=2) == INVALID               # fewer than the bound
+    assert call(gs=None) == INVALID
+    assert call(e=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(en=None) == INVALID
+
+
+def _per_token(**kw):
+    g = moe.MoePerTokenArgs()
+    R, E, N, K = 300, 8, 256, 128
+    g.rows, g.num_experts, g.n, g.k = R, E, N, K
+    g.a, g.a_ld, g.a_scale = 0x100000, K, 0x100000
+    g.w_layout, g.w, g.w_stride_e, g.w_ld, g.w_scale = moe.MOE_LAYOUT_ROWS, 0x100000, N * K, K, 0x100000
+    g.c, g.c_ld = 0x100000, N
+    g.block_expert_ids = g.block_token_offsets = g.block_token_ends = 0x100000
+    g.block_m = L.moe_gemm_block_m(moe.MOE_E4M3, moe.MOE_E4M3, R)
+    g.max_blocks = moe.moe_align_max_blocks(R, E, g.block_m)
+    for key, v in kw.items():
+        setattr(g, key, v)
+    return L.moe_grouped_gemm_per_token(ctypes.byref(g), None)
+
+
+def test_grouped_gemm_per_token_rejects(no_device):
+    assert L.moe_grouped_gemm_per_token(None, None) == INVALID
+    assert _per_token(rows=-1) == INVALID
+    assert _per_token(num_experts=0) == INVALID
+    assert _per_token(k=24, a_ld=32, w_ld=32, w_stride_e=256 * 32) == INVALID   # k % 16
+    assert _per_token(a_ld=136) == INVALID             # not a multiple of 16 bytes
+    assert _per_token(a_ld=64) == INVALID              # shorter than k
+    assert _per_token(w_ld=120) == INVALID
+    assert _per_token(w_stride_e=100) == INVALID
+    assert _per_token(w_layout=7) == INVALID
+    assert _per_token(k=48, a_ld=48, w_ld=48, w_stride_e=256 * 48, w_layout=moe.MOE_LAYOUT_KBLOCK) == INVALID
+    assert _per_token(w_layout=moe.MOE_LAYOUT_KBLOCK, w_ld=256 * 64 - 16) == INVALID
+    assert _per_token(c_ld=255) == INVALID
+    assert _per_token(bias=0x100000, bias_stride_e=-1) == INVALID
+    assert _per_token(block_m=32) == INVALID
+    assert _per_token(max_blocks=3) == INVALID
+    assert _per_token(a_scale=None) == INVALID
+    assert _per_token(w_scale=None) == INVALID
+    assert _per_token(block_token_ends=None) == INVALID
+    assert _per_token(a_scale=0x100002) == INVALID     # not 4-byte aligned
+    assert _per_token(a=0x100008) == INVALID           # not 16-byte aligned
 
 
 def test_quantize_mxfp8_rejects(no_device):
