@@ -1,6 +1,7 @@
 """Benchmark of the MoE expert-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|w4a16|mxfp8|mxfp8a|wgrad]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload decode|nemotron|w4a16|mxfp8|mxfp8a|pertoken|wgrad|copy]
 
 Prints one JSON line. The default workload is the bf16 decode MoE
 (E=128, N=1856, K=2048, top-6) at the MTP6 verify token counts
@@ -9,8 +10,9 @@ GEMM -> moe_combine on a fresh routing (a seeded set of routings is cycled).
 `value` is the step's algorithmic HBM bytes over its time (GB/s); the
 per-call microseconds are reported beside it. The other workloads (the
 gpt-oss-shaped W4A16 MXFP4 layer, the 256-expert MXFP8 grouped GEMM with
-bf16 or MXFP8 activations, the weight gradient) are selected with --workload
-and report TFLOP/s.
+bf16 or MXFP8 activations, the per-token-scaled FP8 grouped GEMM over
+group_sizes, the weight gradient) are selected with --workload and report
+TFLOP/s.
 
 Inputs are synthetic (seeded), generated on the device before the timed
 region. Steps are replayed from HIP graphs captured once per routing variant.
@@ -42,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "nemotron", "w4a16", "mxfp8", "mxfp8a", "wgrad", "copy"])
+                    choices=["decode", "nemotron", "w4a16", "mxfp8", "mxfp8a", "pertoken", "wgrad", "copy"])
     ap.add_argument("--variants", type=int, default=4, help="routing variants cycled across steps")
     ap.add_argument("--launch-reps", type=int, default=10,
                     help="back-to-back launches per event pair when timing the dominant kernel")
@@ -60,6 +62,7 @@ def parse():
 # sources whose change can change a workload's dominant kernel
 KERNEL_SOURCES = {"decode": ["decode.hip"], "nemotron": ["decode.hip"], "w4a16": ["gemm.hip", "gemm_util.h"],
                   "mxfp8": ["gemm.hip", "gemm_util.h"], "mxfp8a": ["gemm_f8.hip", "gemm_util.h"],
+                  "pertoken": ["gemm_f8.hip", "gemm_util.h"],
                   "wgrad": ["wgrad.hip"], "copy": []}
 
 
@@ -162,7 +165,8 @@ class Workload:
         raise NotImplementedError
 
 
-LAYOUT = {"decode": "rows", "nemotron": "rows", "w4a16": "kblock", "mxfp8": "kblock", "mxfp8a": "kblock"}  # resolved --layout per workload
+LAYOUT = {"decode": "rows", "nemotron": "rows", "w4a16": "kblock", "mxfp8": "kblock", "mxfp8a": "kblock",
+          "pertoken": "kblock"}  # resolved --layout per workload
 
 
 def _gemm_weights(moe, name, w, w_dtype, w_scale):
@@ -583,6 +587,82 @@ class MXFP8A(MXFP8):
         return items, run, "TFLOP/s"
 
 
+class PerToken(Workload):
+    """Per-token-scaled FP8 grouped GEMM over the group_sizes interface at the
+    MXFP8 workload's shape: each step builds the block mapping from the group
+    sizes on the device and runs the GEMM (E4M3 x E4M3, per-row and
+    per-expert fp32 scales after the fp8 dot product)."""
+    name = "pertoken"
+    cpu_sample_desc = "per-token GEMM over all rows of the median-load and the top-load expert"
+    dominant = "moe_gemm_f8_kernel"
+    bound = "hbm"
+
+    def __init__(self, torch, dev, variants, bias=False):
+        import mixture_experts_grouped_moe_amd as moe
+        import synth
+        self.torch, self.moe = torch, moe
+        d = synth.config_per_token(device=dev, bias=bias)
+        self.d = d
+        self.E, self.N, self.K, self.R = d["E"], d["N"], d["K"], d["R"]
+        self.wg = moe.moe_pack_weights(d["w"], "e4m3") if LAYOUT[self.name] == "kblock" else d["w"]
+        self.mapping = moe.moe_block_mapping(d["group_sizes"], self.R)
+        self.C = torch.empty((self.R, self.N), dtype=torch.bfloat16, device=dev)
+        gs = synth.bits(d["group_sizes"])
+        self.gs = gs
+        self.touched = int((gs > 0).sum())
+        self.empty = int((gs == 0).sum())
+
+    def step_flops(self, v):
+        return 2 * self.R * self.N * self.K
+
+    def gemm_bytes(self):
+        w = self.touched * self.N * self.K + self.E * 4
+        return int(w + self.R * (self.K + 4) + self.R * self.N * 2)
+
+    def step_bytes(self, v):
+        return self.gemm_bytes()
+
+    def _gemm(self):
+        d = self.d
+        return self.moe.moe_grouped_gemm_per_token(d["a"], d["a_scale"], self.wg, d["w_scale"], self.mapping,
+                                                   bias=d["bias"], out=self.C)
+
+    def step(self, v):
+        self.moe.moe_block_mapping(self.d["group_sizes"], self.R, out=self.mapping)
+        self._gemm()
+
+    def dominant_launches(self, v):
+        return [(self._gemm, self.gemm_bytes())]
+
+    def extra(self, per_call_us):
+        return {"touched_experts": self.touched, "empty_experts": self.empty}
+
+    def cpu_sample(self):
+        import numpy as np
+        import synth
+        from oracle import gemm as ogemm
+        d = self.d
+        gs = self.gs.astype(np.int64)
+        offs = np.concatenate([[0], np.cumsum(gs)])
+        order = np.argsort(gs)
+        experts = [int(order[len(order) // 2]), int(order[-1])]
+        w = LazyRows(d["w"])
+        w_s = synth.bits(d["w_scale"])
+        items = []
+        for e in experts:
+            rows = torch_index(np.arange(offs[e], offs[e + 1]))
+            sub = np.zeros_like(gs)
+            sub[e] = gs[e]
+            items.append((synth.bits(d["a"][rows.to(d["a"].device)]),
+                          synth.bits(d["a_scale"][rows.to(d["a"].device)]), sub))
+
+        def run(item):
+            a, a_s, sub = item
+            ogemm.grouped_gemm_per_token(a, a_s, w, w_s, sub)
+            return 2 * a.shape[0] * self.N * self.K
+        return items, run, "TFLOP/s"
+
+
 def torch_index(rows):
     import torch
     return torch.from_numpy(rows.astype("int64"))
@@ -686,7 +766,8 @@ class Copy(Workload):
         return [0], run, "GB/s"
 
 
-WORKLOADS = {"decode": Decode, "nemotron": Nemotron, "w4a16": W4A16, "mxfp8": MXFP8, "mxfp8a": MXFP8A, "wgrad": Wgrad, "copy": Copy}
+WORKLOADS = {"decode": Decode, "nemotron": Nemotron, "w4a16": W4A16, "mxfp8": MXFP8, "mxfp8a": MXFP8A,
+             "pertoken": PerToken, "wgrad": Wgrad, "copy": Copy}
 CONFIG_NAMES = {
     "decode": "decode bf16 MoE, E=128 N=1856 K=2048 top-6, M in {1,7,14,21,28}",
     "nemotron": "Nemotron-shaped relu2 decode MoE layer, E=128 top-6 hidden=2688 N=1856, bf16, M in {1,7,14,21,28}",
@@ -694,6 +775,8 @@ CONFIG_NAMES = {
     "mxfp8": "MXFP8 grouped GEMM, E=256 top-8 K=7168 N=4096 T=4096, Zipf(1.1) routing with 16 empty experts",
     "mxfp8a": "MXFP8 grouped GEMM with MXFP8 activations (bf16 converted each step), E=256 top-8 K=7168 N=4096 "
               "T=4096, Zipf(1.1) routing with 16 empty experts",
+    "pertoken": "per-token-scaled FP8 grouped GEMM over group_sizes, E=256 K=7168 N=4096, 32768 rows "
+                "(4096 tokens x top-8) grouped by Zipf(1.1) top-8 counts with 16 empty experts",
     "wgrad": "moe_wgrad, E=256 top-8 T=16384, x [T,7168], grad [8T,2048], fp32 dW [256,2048,7168]",
     "copy": "device-to-device copy of 1 GiB (counter calibration)",
 }
@@ -820,11 +903,12 @@ def main():
         unit_v = "TFLOP/s"
         extra = wl.extra(None)
         extra["mfma_frac_step_bf16"] = round(value / PEAK_BF16_TFLOPS, 4)
-        if args.workload == "mxfp8a":
+        if args.workload in ("mxfp8a", "pertoken"):
             extra["mfma_frac_step_fp8"] = round(value / (2 * PEAK_BF16_TFLOPS), 4)
         extra["hbm_GBps_step"] = round(step_bytes / dt / 1e9, 1)
         dtype = {"w4a16": "bf16 x e2m1 (bf16 MFMA)", "mxfp8": "bf16 x e4m3 (bf16 MFMA)",
                  "mxfp8a": "e4m3 x e4m3, E8M0 per 32 (scaled fp8 MFMA)",
+                 "pertoken": "e4m3 x e4m3, fp32 per-row and per-expert scales (fp8 MFMA)",
                  "wgrad": "bf16 (bf16 MFMA, fp32 out)"}[args.workload]
 
     cpu = None

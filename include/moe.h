@@ -229,8 +229,9 @@ typedef struct {
  * expert's weights and one expert's scales each span less than 2 GB.
  * MOE_E4M3 activations: w_dtype MOE_E4M3, a_ld a multiple of 16, a_scale
  * non-null with a_scale_ld >= k / 32, the scales under 2 GB; every token
- * count runs the large-M kernel (no decode variant), so block_m is the
- * large-M one for every num_tokens. Other combinations: MOE_ERR_UNSUPPORTED.
+ * count runs the one scaled-fp8 kernel (no decode variant), whose block_m
+ * (128 rows) is the same for every num_tokens. Other combinations:
+ * MOE_ERR_UNSUPPORTED.
  * No workspace. */
 moe_status moe_grouped_gemm(const moe_gemm_args* args, moe_stream_t stream);
 

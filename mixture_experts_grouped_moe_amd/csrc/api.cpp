@@ -103,7 +103,7 @@ int64_t moe_align_max_blocks(int64_t num_slots, int32_t num_experts, int32_t blo
 
 int32_t moe_gemm_block_m(int32_t a_dtype, int32_t w_dtype, int64_t num_tokens) {
   if (num_tokens < 0) return -1;
-  if (a_dtype == MOE_E4M3 && w_dtype == MOE_E4M3) return moe::gemm_block_m_large();  // no decode variant
+  if (a_dtype == MOE_E4M3 && w_dtype == MOE_E4M3) return moe::gemm_block_m_f8();  // one kernel for every T
   if (a_dtype != MOE_BF16 || !valid_w_dtype(w_dtype)) return -1;
   return num_tokens <= kDecodeMaxTokens ? moe::gemm_block_m_decode() : moe::gemm_block_m_large();
 }
@@ -455,8 +455,8 @@ moe_status moe_grouped_gemm_per_token(const moe_per_token_args* g, moe_stream_t 
   if (a.bias != nullptr && (a.bias_stride_e < 0 || a.bias_stride_n < 0))
     return fail(MOE_ERR_INVALID_ARGUMENT, "negative bias stride");
   if (a.c_ld < a.n) return fail(MOE_ERR_INVALID_ARGUMENT, "c_ld must be >= n");
-  if (a.block_m != moe::gemm_block_m_large())
-    return fail(MOE_ERR_INVALID_ARGUMENT, "block_m %d, expected %d", a.block_m, moe::gemm_block_m_large());
+  if (a.block_m != moe::gemm_block_m_f8())
+    return fail(MOE_ERR_INVALID_ARGUMENT, "block_m %d, expected %d", a.block_m, moe::gemm_block_m_f8());
   const int64_t need = moe_align_max_blocks(a.rows, a.num_experts, a.block_m);
   if (a.max_blocks < need)
     return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks %lld < required %lld", (long long)a.max_blocks,

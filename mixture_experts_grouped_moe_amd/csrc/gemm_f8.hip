@@ -6,13 +6,17 @@
 // decodes an a_scale and a b_scale byte per K block, sentinel blocks return at
 // once, E8M0 0x00 is 2^-127 and 0xFF NaN, bias through explicit strides).
 //
-// Design for gfx950 (the same routing, tiling and load pipeline as the bf16
-// large-M kernel in gemm.hip):
-//  * One workgroup of 4 waves (each 64 rows x 128 columns) per (routing block
-//    of 64 rows, N tile of 512 weight rows); two workgroups per CU.
-//  * Each 64-wide K step moves 4 KB of activation codes and 32 KB of weight
-//    codes straight into LDS with buffer_load ... lds, two stages deep, and
-//    the step's E8M0 bytes into the lanes that use them with byte loads.
+// Design for gfx950 (the routing and load pipeline of the bf16 large-M kernel
+// in gemm.hip, on a taller tile):
+//  * One workgroup of 8 waves (2 along M x 4 along N, each 64 rows x 128
+//    columns) per (routing block of 128 rows, N tile of 512 weight rows); one
+//    workgroup per CU. The kernel is bound by the bytes moved from L2 into
+//    LDS: a 128-row block reads each weight tile once for twice the rows of a
+//    64-row block, which took the MXFP8 workload from 2.24 to 2.05 ms.
+//  * Each 64-wide K step moves 8 KB of activation codes and 32 KB of weight
+//    codes straight into LDS with buffer_load ... lds, three stages deep (two
+//    steps in flight), and the step's E8M0 bytes into the lanes that use them
+//    with byte loads.
 //  * The contraction is v_mfma_scale_f32_32x32x64_f8f6f4: one instruction
 //    per 32 x 32 output tile and K step, with the E8M0 bytes fed to it as they
 //    are (no dequantisation). Its operand layout (measured on gfx950): lane l
@@ -36,29 +40,33 @@
 namespace moe {
 
 constexpr int kF8NT = 4;                        // 32-column MFMA tiles per wave
-constexpr int kF8Stages = 2;
+constexpr int kF8WavesM = 2;                    // waves along M (64 rows each)
+constexpr int kF8Stages = 3;
 constexpr int kF8RowBytes = 64;                 // one row's codes per K step
+constexpr int kF8BM = 64 * kF8WavesM;           // the routing block
+constexpr int kF8Threads = kWave * kF8WavesM * kWavesN;
+constexpr int kF8MinBlocks = kF8WavesM == 1 ? 2 : 1;  // workgroups per CU
 
 typedef int f8_v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kE8M0One = 127;                   // E8M0 code of 2^0
 
 template <bool SWIGLU, bool BIAS, bool PT>
-__global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmParams p) {
-  constexpr int NT = kF8NT, STAGES = kF8Stages, RB = kF8RowBytes;
+__global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(GemmParams p) {
+  constexpr int NT = kF8NT, STAGES = kF8Stages, RB = kF8RowBytes, BM = kF8BM;
   constexpr int WN = NT * 32, BN = kWavesN * WN;
-  constexpr int NWAVES = kWavesM * kWavesN;
+  constexpr int NWAVES = kF8WavesM * kWavesN;
   constexpr int U = RB / 16;                        // 16-byte units per row per step
-  constexpr int A_BYTES = kBM * RB;                 // 4 KB
+  constexpr int A_BYTES = BM * RB;                  // 4 KB per 64 rows
   constexpr int W_BYTES = BN * RB;                  // 32 KB
   constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // 1
-  constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;  // 8
+  constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;  // 4
   constexpr int SC = PT ? 1 : NT + 2;               // scale-byte registers per stage (PT: none used)
   constexpr int LOADS = A_LOADS + W_LOADS + (PT ? 0 : NT + 2); // + weight and activation scale bytes
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
   static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
   constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
-  static_assert(kMinBlocks * STAGES * STAGE_BYTES <= 160 * 1024, "two workgroups per CU");
+  static_assert(kF8MinBlocks * STAGES * STAGE_BYTES <= 160 * 1024, "LDS of the workgroups of one CU");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][STAGE_BYTES];
 
   const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
@@ -71,15 +79,16 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
   int row0 = 0, row_end = 0;
   if constexpr (PT) {
     row0 = max(p.blk_off[b], 0);
-    row_end = min(min(p.blk_end[b], p.S), row0 + min(p.S - row0, kBM));
+    row_end = min(min(p.blk_end[b], p.S), row0 + min(p.S - row0, BM));
   }
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wn = wave % kWavesN;
+  const int wm = wave / kWavesN;                   // the wave's 64 rows: wm * 64 ..
   const int l32 = lane % 32, h = lane / 32;
-  const int32_t* blk_slots = p.sorted + (int64_t)b * kBM;
+  const int32_t* blk_slots = p.sorted + (int64_t)b * BM;
   // slot (output row) of block row r: S (= PAD) for none
   auto slot_of = [&](int r) -> int {
     if constexpr (PT) return row0 + r < row_end ? row0 + r : p.S;
@@ -93,7 +102,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
 
   // a wave with only PAD rows or only columns past N computes nothing (it
   // still loads its share and joins every barrier)
-  const bool rows_live = __ballot(slot_of(lane) < p.S) != 0;
+  const bool rows_live = __ballot(slot_of(wm * 64 + lane) < p.S) != 0;
   const bool cols_live = tile_w_row<NT, SWIGLU>(wn * WN, tile_n, p.N) >= 0;
   const bool wave_live = rows_live && cols_live;
 
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
   }
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const int s = slot_of(mt * 32 + l32);
+    const int s = slot_of(wm * 64 + mt * 32 + l32);
     as_off[mt] = !PT && s < p.S ? (uint32_t)(a_row(s) * p.as_ld + h) : kOOB;
   }
   const uint32_t w_blk = (uint32_t)p.w_blk, ws_blk = (uint32_t)p.ws_blk;
@@ -202,7 +211,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
     const lds_u8_t* Ws = As + A_BYTES;
     f8_v8i af[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) af[mt] = operand(As, mt * 32 + l32);
+    for (int mt = 0; mt < 2; ++mt) af[mt] = operand(As, wm * 64 + mt * 32 + l32);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const f8_v8i bf = operand(Ws, wn * WN + nt * 32 + l32);
@@ -214,9 +223,9 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
     }
   };
 
-  // two stages: wait for this step's loads (none are younger), barrier, load
-  // the next step into the other stage (every wave is past its compute),
-  // compute this one
+  // STAGES - 1 steps in flight: wait for this step's loads (the younger
+  // look-ahead ones may still run), barrier, load step + STAGES - 1 into the
+  // stage every wave has finished computing on, compute this one
   static_for<0, STAGES - 1>([&](auto st) { issue(decltype(st)::value, st); });
   for (int step = 0; step < nsteps_pad; step += STAGES) {
     static_for<0, STAGES>([&](auto st) {
@@ -231,8 +240,8 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int32_t* s_slot = reinterpret_cast<int32_t*>(&lds[0][0]);
-  float* s_scale = reinterpret_cast<float*>(&lds[0][0]) + kBM;
-  if (tid < kBM) {
+  float* s_scale = reinterpret_cast<float*>(&lds[0][0]) + BM;
+  if (tid < BM) {
     const int s = slot_of(tid);
     s_slot[tid] = s;
     if constexpr (PT) s_scale[tid] = s < p.S ? p.tok_scale[s] * p.exp_scale[e] : 0.0f;
@@ -251,7 +260,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_f8_kernel(GemmP
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = mt * 32 + (i / 4) * 8 + h * 4 + (i % 4);
+      const int row = wm * 64 + mt * 32 + (i / 4) * 8 + h * 4 + (i % 4);
       const int s = s_slot[row];
       if (s >= p.S) continue;
       uint16_t* crow = p.c + (int64_t)s * p.c_ld;
@@ -284,11 +293,11 @@ hipError_t launch_gemm_f8(const GemmParams& p, bool swiglu, bool bias, hipStream
   const int64_t tiles = swiglu ? (p.N / 2 + bn / 2 - 1) / (bn / 2) : (p.N + bn - 1) / bn;
   const dim3 grid((uint32_t)(tiles * p.max_blocks));
   if (swiglu) {
-    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<true, true, false>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((moe_gemm_f8_kernel<true, false, false>), grid, dim3(kThreads), 0, stream, p);
+    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<true, true, false>), grid, dim3(kF8Threads), 0, stream, p);
+    else hipLaunchKernelGGL((moe_gemm_f8_kernel<true, false, false>), grid, dim3(kF8Threads), 0, stream, p);
   } else {
-    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, false>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, false>), grid, dim3(kThreads), 0, stream, p);
+    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, false>), grid, dim3(kF8Threads), 0, stream, p);
+    else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, false>), grid, dim3(kF8Threads), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -297,9 +306,11 @@ hipError_t launch_gemm_per_token(const GemmParams& p, bool bias, hipStream_t str
   if (p.max_blocks <= 0) return hipSuccess;
   const int bn = kWavesN * 32 * kF8NT;
   const dim3 grid((uint32_t)((p.N + bn - 1) / bn * (int64_t)p.max_blocks));
-  if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, true>), grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, true>), grid, dim3(kThreads), 0, stream, p);
+  if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, true>), grid, dim3(kF8Threads), 0, stream, p);
+  else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, true>), grid, dim3(kF8Threads), 0, stream, p);
   return hipGetLastError();
 }
+
+int gemm_block_m_f8() { return kF8BM; }
 
 }  // namespace moe

@@ -83,6 +83,7 @@ hipError_t launch_pack(const uint8_t* w, int64_t w_stride_e, int64_t w_ld, const
 hipError_t launch_quant_mxfp8(const uint16_t* x, int64_t x_ld, int64_t rows, int64_t k, uint8_t* q, int64_t q_ld,
                               uint8_t* s, int64_t s_ld, hipStream_t stream);
 int gemm_block_m_large();
+int gemm_block_m_f8();
 int gemm_block_m_decode();
 int wgrad_block_m();
 
