@@ -97,8 +97,11 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   // moe_align's routing the real rows of a block come first, so this skips
   // the padding past the last real row in 64-row steps) or when all its
   // columns lie past N; it still loads its share of the tiles and joins
-  // every barrier.
-  const bool rows_live = __ballot(blk_slots[wm * 64 + lane] < p.S) != 0;
+  // every barrier. When its upper 32 rows are all PAD (an expert's last,
+  // short block) it runs the MFMAs of the lower 32 only.
+  const uint64_t live_rows = __ballot(blk_slots[wm * 64 + lane] < p.S);
+  const bool rows_live = live_rows != 0;
+  const bool upper_live = (live_rows >> 32) != 0;
   const bool cols_live = tile_w_row<NT, SWIGLU>(wn * WN, tile_n, p.N) >= 0;
   const bool wave_live = rows_live && cols_live;
 
@@ -273,6 +276,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
     }
   };
 
+  using One = std::integral_constant<int, 1>;
   using Two = std::integral_constant<int, 2>;
 
   // Stage s holds steps s, s + STAGES, ... Before computing a step, the wave
@@ -280,15 +284,23 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   // outstanding, so this step's loads are done; the barrier then makes every
   // wave's loads visible and guarantees all waves finished the previous step,
   // whose stage the loads issued next overwrite.
-  static_for<0, STAGES - 1>([&](auto st) { issue(decltype(st)::value, st); });
-  for (int step = 0; step < nsteps_pad; step += STAGES) {
-    static_for<0, STAGES>([&](auto st) {
-      constexpr int ST = decltype(st)::value;
-      wait_loads_barrier<LOADS * (STAGES - 2)>(sc[ST]);
-      issue(step + ST + STAGES - 1, std::integral_constant<int, (ST + STAGES - 1) % STAGES>{});
-      if (wave_live) compute(st, Two{});
-    });
-  }
+  // (the loop, with its first loads, is instantiated once per row count and
+  // chosen before any load is issued: the scale bytes arrive by loads the
+  // compiler does not track, so no register they write may be live across
+  // the choice, where the compiler could copy it before the data lands)
+  auto k_loop = [&](auto nmt_tag) {
+    static_for<0, STAGES - 1>([&](auto st) { issue(decltype(st)::value, st); });
+    for (int step = 0; step < nsteps_pad; step += STAGES) {
+      static_for<0, STAGES>([&](auto st) {
+        constexpr int ST = decltype(st)::value;
+        wait_loads_barrier<LOADS * (STAGES - 2)>(sc[ST]);
+        issue(step + ST + STAGES - 1, std::integral_constant<int, (ST + STAGES - 1) % STAGES>{});
+        if (wave_live) compute(st, nmt_tag);
+      });
+    }
+  };
+  if (upper_live) k_loop(Two{});
+  else k_loop(One{});
   // drain the look-ahead loads (all of them read as zeros past the last step),
   // then keep the slot list in stage 0 once every wave is done with it
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
