@@ -61,11 +61,16 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   constexpr int W_BYTES = BN * RB;                  // 32 KB
   constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // 1
   constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;  // 4
-  constexpr int SC = PT ? 1 : NT + 2;               // scale-byte registers per stage (PT: none used)
-  constexpr int LOADS = A_LOADS + W_LOADS + (PT ? 0 : NT + 2); // + weight and activation scale bytes
+  constexpr int AS_BYTES = PT ? 0 : BM * 2 * 4;     // the step's activation scale bytes, one dword each
+  constexpr int WS_BYTES = PT ? 0 : BN * 2 * 4;     // the step's weight scale bytes, one dword each
+  constexpr int AS_GROUPS = BM / 32;                // 32-row groups, one scale DMA each
+  constexpr int WS_DMAS = BN / 32 / NWAVES;         // weight-scale DMAs per wave (32 rows each)
+  static_assert(NWAVES % AS_GROUPS == 0, "every wave issues one activation-scale DMA");
+  static_assert(WS_DMAS * NWAVES * 32 == BN, "weight-scale split");
+  constexpr int LOADS = A_LOADS + W_LOADS + (PT ? 0 : WS_DMAS + 1);  // + the scale DMAs
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
   static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
-  constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
+  constexpr int STAGE_BYTES = A_BYTES + W_BYTES + AS_BYTES + WS_BYTES;
   static_assert(kF8MinBlocks * STAGES * STAGE_BYTES <= 160 * 1024, "LDS of the workgroups of one CU");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][STAGE_BYTES];
 
@@ -138,26 +143,34 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
     w_k[i] = u * 16;
     w_off[i] = wr >= 0 ? (uint32_t)((int64_t)wr * p.w_row + u * 16) : kOOB;
   }
-  // scale bytes of K block 2 * step + h: the lane's weight rows (one per
-  // N sub-tile) and activation rows (one per M sub-tile)
+  // Scale bytes of K block 2 * step + h go by DMA into the stage (one zero-
+  // extended dword per byte, lane order: 32-row group, then h, then the
+  // row's place in the group), where each wave reads those of its own rows
+  // and columns: the waves of a row group or of a column group would
+  // otherwise each load the same bytes. Activation rows: group
+  // wave % AS_GROUPS (two waves write each group alike); weight rows: groups
+  // WS_DMAS * wave + i.
   int32_t my_wrow[NT];
-  uint32_t ws_off[NT], as_off[2];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    my_wrow[nt] = tile_w_row<NT, SWIGLU>(wn * WN + nt * 32 + l32, tile_n, p.N);
-    ws_off[nt] = my_wrow[nt] >= 0 ? (uint32_t)((int64_t)my_wrow[nt] * p.ws_row + h) : kOOB;
+  for (int nt = 0; nt < NT; ++nt) my_wrow[nt] = tile_w_row<NT, SWIGLU>(wn * WN + nt * 32 + l32, tile_n, p.N);
+  uint32_t ws_off[WS_DMAS];
+#pragma unroll
+  for (int i = 0; i < WS_DMAS; ++i) {
+    const int32_t wr = tile_w_row<NT, SWIGLU>((WS_DMAS * wave + i) * 32 + l32, tile_n, p.N);
+    ws_off[i] = !PT && wr >= 0 ? (uint32_t)((int64_t)wr * p.ws_row + h) : kOOB;
   }
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int s = slot_of(wm * 64 + mt * 32 + l32);
-    as_off[mt] = !PT && s < p.S ? (uint32_t)(a_row(s) * p.as_ld + h) : kOOB;
+  const int as_group = wave % AS_GROUPS;
+  uint32_t as_off;
+  {
+    const int s = slot_of(as_group * 32 + l32);
+    as_off = !PT && s < p.S ? (uint32_t)(a_row(s) * p.as_ld + h) : kOOB;
   }
   const uint32_t w_blk = (uint32_t)p.w_blk, ws_blk = (uint32_t)p.ws_blk;
 
   const int nsteps = (p.K + kBK - 1) / kBK;
   const int nsteps_pad = ((nsteps + STAGES - 1) / STAGES) * STAGES;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)&lds[0][0];
-  uint32_t sc[STAGES][SC];  // the step's scale bytes: weights (NT), then activations (2)
+  uint32_t no_regs[1];      // the loads below write no registers the waits must hold
 
   // Issue the loads of K step `step` into stage ST; the K tail and the
   // look-ahead steps past the last one take the checked path (lanes past K
@@ -181,9 +194,10 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
             base + A_BYTES + (wave * W_LOADS + i) * 1024);
     if constexpr (!PT) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sc[ST][nt] = load_byte(s_rsrc, h_live ? ws_off[nt] : kOOB, ss);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) sc[ST][NT + mt] = load_byte(as_rsrc, h_live ? as_off[mt] : kOOB, sas);
+      for (int i = 0; i < WS_DMAS; ++i)
+        dma_byte(s_rsrc, h_live ? ws_off[i] : kOOB, ss,
+                 base + A_BYTES + W_BYTES + AS_BYTES + (WS_DMAS * wave + i) * 256);
+      dma_byte(as_rsrc, h_live ? as_off : kOOB, sas, base + A_BYTES + W_BYTES + as_group * 256);
     }
   };
 
@@ -210,16 +224,21 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
     const lds_u8_t* As = (const lds_u8_t*)&lds[ST][0];
     const lds_u8_t* Ws = As + A_BYTES;
     f8_v8i af[2];
+    int sa[2] = {kE8M0One, kE8M0One};
+    const lds_u8_t* Ss = Ws + W_BYTES + AS_BYTES;  // weight scale dwords
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) af[mt] = operand(As, wm * 64 + mt * 32 + l32);
+    for (int mt = 0; mt < 2; ++mt) {
+      af[mt] = operand(As, wm * 64 + mt * 32 + l32);
+      if constexpr (!PT) sa[mt] = (int)lds_read<uint32_t>(Ws + W_BYTES + ((2 * wm + mt) * 64 + lane) * 4);
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const f8_v8i bf = operand(Ws, wn * WN + nt * 32 + l32);
+      const int sw = PT ? kE8M0One : (int)lds_read<uint32_t>(Ss + ((wn * NT + nt) * 64 + lane) * 4);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            af[mt], bf, acc[mt][nt], 0, 0, 0, PT ? kE8M0One : (int)sc[ST][NT + mt], 0,
-            PT ? kE8M0One : (int)sc[ST][nt]);
+            af[mt], bf, acc[mt][nt], 0, 0, 0, sa[mt], 0, sw);
     }
   };
 
@@ -230,7 +249,7 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   for (int step = 0; step < nsteps_pad; step += STAGES) {
     static_for<0, STAGES>([&](auto st) {
       constexpr int ST = decltype(st)::value;
-      wait_loads_barrier<LOADS * (STAGES - 2)>(sc[ST]);
+      wait_loads_barrier<LOADS * (STAGES - 2)>(no_regs);
       issue(step + ST + STAGES - 1, std::integral_constant<int, (ST + STAGES - 1) % STAGES>{});
       if (wave_live) compute(st);
     });

@@ -46,6 +46,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff
                   "s"(__builtin_amdgcn_readfirstlane(soff)) : "m0");
 }
 
+// One byte per lane from buffer `rsrc` at `voff` + `soff` into LDS, written
+// zero-extended as the dword at `lds_base` + 4 * lane (measured on gfx950); a
+// lane whose `voff` is kOOB writes 0.
+__device__ __forceinline__ void dma_byte(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_ubyte %0, %2, %3 offen lds"
+               :: "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "m0");
+}
+
 // One byte from buffer `rsrc` at `voff` + `soff` into a register (zero for a
 // lane whose `voff` is kOOB).
 __device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
