@@ -22,8 +22,11 @@
 //    global memory into LDS with buffer_load ... lds (no registers; rows past
 //    N, PAD rows and the K tail read as zeros through the buffer bounds),
 //    three stages deep, one barrier per step. The E8M0 bytes of a lane's
-//    weight rows arrive in registers with byte loads of the same step (a
-//    variant that brought them by DMA into LDS measured no faster).
+//    weight rows arrive in registers with byte loads issued one step ahead
+//    of their step's tiles, right after the compute that frees their
+//    registers (issued with the tiles, last, they held up each step's wait:
+//    3% on the MXFP8 workload; a variant that brought them by DMA into LDS
+//    measured no faster).
 //  * K order inside a step: lane half h of a wave handles K elements
 //    [32h, 32h + 32) and MFMA substep ks takes [32h + 8ks, 32h + 8ks + 8).
 //    Any order common to both operands gives the same dot product; this one
@@ -67,10 +70,14 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;
   constexpr int S_LOADS = (WDT == W_BF16) ? 0 : NT;  // scale bytes per lane per step
   constexpr int SC_REGS = (WDT == W_BF16) ? 1 : NT;
-  constexpr int LOADS = A_LOADS + W_LOADS + S_LOADS;  // loads per step per wave
+  constexpr int LOADS = A_LOADS + W_LOADS;            // DMA loads per step per wave
+  // Before computing a step a wave may leave in flight the DMA loads of the
+  // next STAGES - 2 steps and the scale loads of the next STAGES - 1 (the
+  // scale bytes of a step are loaded one step earlier than its tiles).
+  constexpr int WAIT_N = LOADS * (STAGES - 2) + S_LOADS * (STAGES - 1);
   constexpr int PIECES = (WDT == W_BF16) ? 4 : (WDT == W_E4M3 ? 2 : 1);  // 16-byte code pieces per lane-row
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
-  static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(WAIT_N < 64, "vmcnt range");
 
   // LDS: STAGES x [A tile | weight tile] (E4M3: two 40 KB stages, so two
   // workgroups fill a CU's 160 KB exactly; the block's slot list is read from
@@ -156,8 +163,8 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   // scale bytes of this lane's weight rows (one per N sub-tile), per stage
   uint32_t sc[STAGES][SC_REGS];
 
-  // Issue the loads of K step `step` into stage ST. A step wholly inside K
-  // uses the per-lane offsets as they are, advanced by a scalar offset; the
+  // Issue the DMA loads of K step `step` into stage ST. A step wholly inside
+  // K uses the per-lane offsets as they are, advanced by a scalar offset; the
   // K tail and the look-ahead steps past the last one (every step issues the
   // same number of loads) take the checked path, whose lanes past K read
   // zeros.
@@ -166,19 +173,14 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
     const int k0 = step * kBK;
     const uint32_t base = lds_base + ST * STAGE_BYTES;
     if (k0 + kBK <= p.K) {
-      const uint32_t sa = (uint32_t)k0 * 2, sw = (uint32_t)step * w_blk, ss = (uint32_t)step * ws_blk;
+      const uint32_t sa = (uint32_t)k0 * 2, sw = (uint32_t)step * w_blk;
 #pragma unroll
       for (int i = 0; i < A_LOADS; ++i) dma16(a_rsrc, a_off[i], sa, base + (wave * A_LOADS + i) * 1024);
 #pragma unroll
       for (int i = 0; i < W_LOADS; ++i) dma16(w_rsrc, w_off[i], sw, base + A_BYTES + (wave * W_LOADS + i) * 1024);
-      if constexpr (WDT != W_BF16) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sc[ST][nt] = load_byte(s_rsrc, s_off[nt], ss);
-      }
     } else {
       const bool live = k0 < p.K;
-      const uint32_t sa = live ? (uint32_t)k0 * 2 : 0u, sw = live ? (uint32_t)step * w_blk : 0u,
-                     ss = live ? (uint32_t)step * ws_blk : 0u;
+      const uint32_t sa = live ? (uint32_t)k0 * 2 : 0u, sw = live ? (uint32_t)step * w_blk : 0u;
 #pragma unroll
       for (int i = 0; i < A_LOADS; ++i)
         dma16(a_rsrc, (live && k0 + a_k[i] < p.K) ? a_off[i] : kOOB, sa, base + (wave * A_LOADS + i) * 1024);
@@ -186,11 +188,18 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
       for (int i = 0; i < W_LOADS; ++i)
         dma16(w_rsrc, (live && k0 + w_k[i] < p.K) ? w_off[i] : kOOB, sw,
               base + A_BYTES + (wave * W_LOADS + i) * 1024);
-      if constexpr (WDT != W_BF16) {
+    }
+  };
+  // The scale bytes of K step `step` into register set ST (the set of the
+  // step just computed, step - STAGES); a block past K reads 0.
+  auto issue_scales = [&](int step, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
+    if constexpr (WDT != W_BF16) {
+      const int k0 = step * kBK;
+      const bool hl = k0 + 32 * h < p.K;
+      const uint32_t ss = k0 < p.K ? (uint32_t)step * ws_blk : 0u;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          sc[ST][nt] = load_byte(s_rsrc, (live && k0 + 32 * h < p.K) ? s_off[nt] : kOOB, ss);
-      }
+      for (int nt = 0; nt < NT; ++nt) sc[ST][nt] = load_byte(s_rsrc, hl ? s_off[nt] : kOOB, ss);
     }
   };
 
@@ -280,22 +289,31 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   using Two = std::integral_constant<int, 2>;
 
   // Stage s holds steps s, s + STAGES, ... Before computing a step, the wave
-  // waits until only the loads of the STAGES - 2 steps after it are
-  // outstanding, so this step's loads are done; the barrier then makes every
-  // wave's loads visible and guarantees all waves finished the previous step,
-  // whose stage the loads issued next overwrite.
+  // waits until only the loads issued after this step's tiles are
+  // outstanding (WAIT_N), so this step's tiles and scale bytes are done; the
+  // barrier then makes every wave's loads visible and guarantees all waves
+  // finished the previous step, whose stage the loads issued next overwrite.
+  // Issue order: scales(0), then per step t < STAGES - 1 tiles(t) and
+  // scales(t + 1); in the loop, tiles(step + STAGES - 1) before the compute
+  // and scales(step + STAGES) after it, into the register set just read.
   // (the loop, with its first loads, is instantiated once per row count and
   // chosen before any load is issued: the scale bytes arrive by loads the
   // compiler does not track, so no register they write may be live across
   // the choice, where the compiler could copy it before the data lands)
   auto k_loop = [&](auto nmt_tag) {
-    static_for<0, STAGES - 1>([&](auto st) { issue(decltype(st)::value, st); });
+    issue_scales(0, std::integral_constant<int, 0>{});
+    static_for<0, STAGES - 1>([&](auto st) {
+      constexpr int ST = decltype(st)::value;
+      issue(ST, st);
+      issue_scales(ST + 1, std::integral_constant<int, ST + 1>{});
+    });
     for (int step = 0; step < nsteps_pad; step += STAGES) {
       static_for<0, STAGES>([&](auto st) {
         constexpr int ST = decltype(st)::value;
-        wait_loads_barrier<LOADS * (STAGES - 2)>(sc[ST]);
+        wait_loads_barrier<WAIT_N>(sc[ST]);
         issue(step + ST + STAGES - 1, std::integral_constant<int, (ST + STAGES - 1) % STAGES>{});
         if (wave_live) compute(st, nmt_tag);
+        issue_scales(step + ST + STAGES, st);
       });
     }
   };
