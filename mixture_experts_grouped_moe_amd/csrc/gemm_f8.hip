@@ -67,12 +67,21 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   constexpr int WS_DMAS = BN / 32 / NWAVES;         // weight-scale DMAs per wave (32 rows each)
   static_assert(NWAVES % AS_GROUPS == 0, "every wave issues one activation-scale DMA");
   static_assert(WS_DMAS * NWAVES * 32 == BN, "weight-scale split");
-  constexpr int LOADS = A_LOADS + W_LOADS + (PT ? 0 : WS_DMAS + 1);  // + the scale DMAs
+  constexpr int T_LOADS = A_LOADS + W_LOADS;        // tile DMAs per step per wave
+  constexpr int S_DMAS = PT ? 0 : WS_DMAS + 1;      // scale DMAs per step per wave
+  // A step's scale bytes are loaded one step before its tiles, into their
+  // own ring of SR sets; before computing a step a wave may leave in flight
+  // the tiles of the next STAGES - 2 steps and the scales of the next
+  // STAGES - 1.
+  constexpr int SR = STAGES + 1;
+  constexpr int SC_BYTES = AS_BYTES + WS_BYTES;
+  constexpr int WAIT_N = T_LOADS * (STAGES - 2) + S_DMAS * (STAGES - 1);
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
-  static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
-  constexpr int STAGE_BYTES = A_BYTES + W_BYTES + AS_BYTES + WS_BYTES;
-  static_assert(kF8MinBlocks * STAGES * STAGE_BYTES <= 160 * 1024, "LDS of the workgroups of one CU");
+  static_assert(WAIT_N < 64, "vmcnt range");
+  constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
+  static_assert(kF8MinBlocks * (STAGES * STAGE_BYTES + SR * SC_BYTES) <= 160 * 1024, "LDS of the workgroups of one CU");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_sc[PT ? 1 : SR][PT ? 16 : SC_BYTES];
 
   const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
   const int b = L % p.max_blocks;
@@ -170,20 +179,19 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   const int nsteps = (p.K + kBK - 1) / kBK;
   const int nsteps_pad = ((nsteps + STAGES - 1) / STAGES) * STAGES;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)&lds[0][0];
+  const uint32_t lds_sc_base = (uint32_t)(uintptr_t)(lds_u8_t*)&lds_sc[0][0];
   uint32_t no_regs[1];      // the loads below write no registers the waits must hold
 
-  // Issue the loads of K step `step` into stage ST; the K tail and the
+  // Issue the tile loads of K step `step` into stage ST; the K tail and the
   // look-ahead steps past the last one take the checked path (lanes past K
-  // read zeros, so do the scale bytes of a missing second block).
+  // read zeros).
   auto issue = [&](int step, auto stage_tag) {
     constexpr int ST = decltype(stage_tag)::value;
     const int k0 = step * kBK;
     const uint32_t base = lds_base + ST * STAGE_BYTES;
     const bool full = k0 + kBK <= p.K;
     const bool live = k0 < p.K;
-    const uint32_t sa = live ? (uint32_t)k0 : 0u, sw = live ? (uint32_t)step * w_blk : 0u,
-                   ss = live ? (uint32_t)step * ws_blk : 0u, sas = live ? (uint32_t)step * 2 : 0u;
-    const bool h_live = live && k0 + 32 * h < p.K;
+    const uint32_t sa = live ? (uint32_t)k0 : 0u, sw = live ? (uint32_t)step * w_blk : 0u;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
       dma16(a_rsrc, (full || (live && k0 + a_k[i] < p.K)) ? a_off[i] : kOOB, sa,
@@ -192,12 +200,20 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
     for (int i = 0; i < W_LOADS; ++i)
       dma16(w_rsrc, (full || (live && k0 + w_k[i] < p.K)) ? w_off[i] : kOOB, sw,
             base + A_BYTES + (wave * W_LOADS + i) * 1024);
+  };
+  // The scale bytes of K step `step` into scale set step % SR (a block past
+  // K reads 0).
+  auto issue_scales = [&](int step) {
     if constexpr (!PT) {
+      const int k0 = step * kBK;
+      const bool live = k0 < p.K;
+      const uint32_t ss = live ? (uint32_t)step * ws_blk : 0u, sas = live ? (uint32_t)step * 2 : 0u;
+      const bool h_live = live && k0 + 32 * h < p.K;
+      const uint32_t base = lds_sc_base + (uint32_t)(step % SR) * SC_BYTES;
 #pragma unroll
       for (int i = 0; i < WS_DMAS; ++i)
-        dma_byte(s_rsrc, h_live ? ws_off[i] : kOOB, ss,
-                 base + A_BYTES + W_BYTES + AS_BYTES + (WS_DMAS * wave + i) * 256);
-      dma_byte(as_rsrc, h_live ? as_off : kOOB, sas, base + A_BYTES + W_BYTES + as_group * 256);
+        dma_byte(s_rsrc, h_live ? ws_off[i] : kOOB, ss, base + AS_BYTES + (WS_DMAS * wave + i) * 256);
+      dma_byte(as_rsrc, h_live ? as_off : kOOB, sas, base + as_group * 256);
     }
   };
 
@@ -219,17 +235,18 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
     return r;
   };
 
-  auto compute = [&](auto stage_tag) {
+  auto compute = [&](auto stage_tag, int step) {
     constexpr int ST = decltype(stage_tag)::value;
     const lds_u8_t* As = (const lds_u8_t*)&lds[ST][0];
     const lds_u8_t* Ws = As + A_BYTES;
     f8_v8i af[2];
     int sa[2] = {kE8M0One, kE8M0One};
-    const lds_u8_t* Ss = Ws + W_BYTES + AS_BYTES;  // weight scale dwords
+    const lds_u8_t* Sa = (const lds_u8_t*)&lds_sc[0][0] + (step % SR) * SC_BYTES;  // activation scale dwords
+    const lds_u8_t* Ss = Sa + AS_BYTES;                                              // weight scale dwords
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       af[mt] = operand(As, wm * 64 + mt * 32 + l32);
-      if constexpr (!PT) sa[mt] = (int)lds_read<uint32_t>(Ws + W_BYTES + ((2 * wm + mt) * 64 + lane) * 4);
+      if constexpr (!PT) sa[mt] = (int)lds_read<uint32_t>(Sa + ((2 * wm + mt) * 64 + lane) * 4);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -243,15 +260,25 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   };
 
   // STAGES - 1 steps in flight: wait for this step's loads (the younger
-  // look-ahead ones may still run), barrier, load step + STAGES - 1 into the
-  // stage every wave has finished computing on, compute this one
-  static_for<0, STAGES - 1>([&](auto st) { issue(decltype(st)::value, st); });
+  // look-ahead ones may still run), barrier, load the tiles of step +
+  // STAGES - 1 into the stage every wave has finished computing on, compute
+  // this one, then load the scales of step + STAGES into the set of the step
+  // before this one (every wave is past it: it computed before the barrier).
+  // Issue order: scales(0), then per step t < STAGES - 1 tiles(t) and
+  // scales(t + 1).
+  issue_scales(0);
+  static_for<0, STAGES - 1>([&](auto st) {
+    constexpr int ST = decltype(st)::value;
+    issue(ST, st);
+    issue_scales(ST + 1);
+  });
   for (int step = 0; step < nsteps_pad; step += STAGES) {
     static_for<0, STAGES>([&](auto st) {
       constexpr int ST = decltype(st)::value;
-      wait_loads_barrier<LOADS * (STAGES - 2)>(no_regs);
+      wait_loads_barrier<WAIT_N>(no_regs);
       issue(step + ST + STAGES - 1, std::integral_constant<int, (ST + STAGES - 1) % STAGES>{});
-      if (wave_live) compute(st);
+      if (wave_live) compute(st, step + ST);
+      issue_scales(step + ST + STAGES);
     });
   }
   // drain the look-ahead loads, then keep the slot list (PT: each row's
