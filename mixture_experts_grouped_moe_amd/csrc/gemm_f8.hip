@@ -49,9 +49,21 @@ constexpr int kF8MinBlocks = kF8WavesM == 1 ? 2 : 1;  // workgroups per CU
 
 typedef int f8_v8i __attribute__((ext_vector_type(8)));
 
+// Two bytes per lane from buffer `rsrc` at `voff` + `soff` into LDS, written
+// zero-extended as the dword at `lds_base` + 4 * lane (the byte at `voff` in
+// bits 0-7); a lane whose `voff` is kOOB writes 0. `voff` + `soff` is even.
+__device__ __forceinline__ void dma_ushort(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_ushort %0, %2, %3 offen lds"
+               :: "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "m0");
+}
+
 constexpr int kE8M0One = 127;                   // E8M0 code of 2^0
 
-template <bool SWIGLU, bool BIAS, bool PT>
+// WS2: a weight row's two scale bytes of a step are adjacent and 2-byte
+// aligned (even scale strides), so one 2-byte DMA per lane fetches both and
+// one DMA covers 64 rows; otherwise one byte per lane and 32 rows per DMA.
+template <bool SWIGLU, bool BIAS, bool PT, bool WS2>
 __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(GemmParams p) {
   constexpr int NT = kF8NT, STAGES = kF8Stages, RB = kF8RowBytes, BM = kF8BM;
   constexpr int WN = NT * 32, BN = kWavesN * WN;
@@ -62,11 +74,12 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // 1
   constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;  // 4
   constexpr int AS_BYTES = PT ? 0 : BM * 2 * 4;     // the step's activation scale bytes, one dword each
-  constexpr int WS_BYTES = PT ? 0 : BN * 2 * 4;     // the step's weight scale bytes, one dword each
+  constexpr int WS_BYTES = PT ? 0 : BN * (WS2 ? 1 : 2) * 4;  // the step's weight scale bytes, one dword per row (WS2) or byte
   constexpr int AS_GROUPS = BM / 32;                // 32-row groups, one scale DMA each
-  constexpr int WS_DMAS = BN / 32 / NWAVES;         // weight-scale DMAs per wave (32 rows each)
+  constexpr int WS_ROWS = WS2 ? 64 : 32;            // weight rows per scale DMA
+  constexpr int WS_DMAS = BN / WS_ROWS / NWAVES;    // weight-scale DMAs per wave
   static_assert(NWAVES % AS_GROUPS == 0, "every wave issues one activation-scale DMA");
-  static_assert(WS_DMAS * NWAVES * 32 == BN, "weight-scale split");
+  static_assert(WS_DMAS * NWAVES * WS_ROWS == BN, "weight-scale split");
   constexpr int T_LOADS = A_LOADS + W_LOADS;        // tile DMAs per step per wave
   constexpr int S_DMAS = PT ? 0 : WS_DMAS + 1;      // scale DMAs per step per wave
   // A step's scale bytes are loaded one step before its tiles, into their
@@ -158,15 +171,17 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   // and columns: the waves of a row group or of a column group would
   // otherwise each load the same bytes. Activation rows: group
   // wave % AS_GROUPS (two waves write each group alike); weight rows: groups
-  // WS_DMAS * wave + i.
+  // WS_DMAS * wave + i (WS2: 64-row groups, one dword per row holding
+  // both bytes).
   int32_t my_wrow[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) my_wrow[nt] = tile_w_row<NT, SWIGLU>(wn * WN + nt * 32 + l32, tile_n, p.N);
   uint32_t ws_off[WS_DMAS];
 #pragma unroll
   for (int i = 0; i < WS_DMAS; ++i) {
-    const int32_t wr = tile_w_row<NT, SWIGLU>((WS_DMAS * wave + i) * 32 + l32, tile_n, p.N);
-    ws_off[i] = !PT && wr >= 0 ? (uint32_t)((int64_t)wr * p.ws_row + h) : kOOB;
+    const int r = WS2 ? (WS_DMAS * wave + i) * 64 + lane : (WS_DMAS * wave + i) * 32 + l32;
+    const int32_t wr = tile_w_row<NT, SWIGLU>(r, tile_n, p.N);
+    ws_off[i] = !PT && wr >= 0 ? (uint32_t)((int64_t)wr * p.ws_row + (WS2 ? 0 : h)) : kOOB;
   }
   const int as_group = wave % AS_GROUPS;
   uint32_t as_off;
@@ -211,8 +226,10 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
       const bool h_live = live && k0 + 32 * h < p.K;
       const uint32_t base = lds_sc_base + (uint32_t)(step % SR) * SC_BYTES;
 #pragma unroll
-      for (int i = 0; i < WS_DMAS; ++i)
-        dma_byte(s_rsrc, h_live ? ws_off[i] : kOOB, ss, base + AS_BYTES + (WS_DMAS * wave + i) * 256);
+      for (int i = 0; i < WS_DMAS; ++i) {
+        if constexpr (WS2) dma_ushort(s_rsrc, live ? ws_off[i] : kOOB, ss, base + AS_BYTES + (WS_DMAS * wave + i) * 256);
+        else dma_byte(s_rsrc, h_live ? ws_off[i] : kOOB, ss, base + AS_BYTES + (WS_DMAS * wave + i) * 256);
+      }
       dma_byte(as_rsrc, h_live ? as_off : kOOB, sas, base + as_group * 256);
     }
   };
@@ -251,7 +268,14 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const f8_v8i bf = operand(Ws, wn * WN + nt * 32 + l32);
-      const int sw = PT ? kE8M0One : (int)lds_read<uint32_t>(Ss + ((wn * NT + nt) * 64 + lane) * 4);
+      int sw = kE8M0One;
+      if constexpr (!PT && WS2) {
+        // both bytes of the row; the second block of a half K step lies past K
+        const uint32_t d = lds_read<uint32_t>(Ss + (wn * WN + nt * 32 + l32) * 4);
+        sw = (h && step * kBK + 32 >= p.K) ? 0 : (int)((d >> (8 * h)) & 0xffu);
+      } else if constexpr (!PT) {
+        sw = (int)lds_read<uint32_t>(Ss + ((wn * NT + nt) * 64 + lane) * 4);
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -338,13 +362,18 @@ hipError_t launch_gemm_f8(const GemmParams& p, bool swiglu, bool bias, hipStream
   const int bn = kWavesN * 32 * kF8NT;
   const int64_t tiles = swiglu ? (p.N / 2 + bn / 2 - 1) / (bn / 2) : (p.N + bn - 1) / bn;
   const dim3 grid((uint32_t)(tiles * p.max_blocks));
+  // both scale bytes of a row's step in one aligned 2-byte load?
+  const bool ws2 = p.ws_row % 2 == 0 && p.ws_blk % 2 == 0 && p.ws_stride_e % 2 == 0 && (uintptr_t)p.ws % 2 == 0;
+#define MOE_LAUNCH_F8(SW, BI, W2) \
+  hipLaunchKernelGGL((moe_gemm_f8_kernel<SW, BI, false, W2>), grid, dim3(kF8Threads), 0, stream, p)
   if (swiglu) {
-    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<true, true, false>), grid, dim3(kF8Threads), 0, stream, p);
-    else hipLaunchKernelGGL((moe_gemm_f8_kernel<true, false, false>), grid, dim3(kF8Threads), 0, stream, p);
+    if (bias) { if (ws2) MOE_LAUNCH_F8(true, true, true); else MOE_LAUNCH_F8(true, true, false); }
+    else { if (ws2) MOE_LAUNCH_F8(true, false, true); else MOE_LAUNCH_F8(true, false, false); }
   } else {
-    if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, false>), grid, dim3(kF8Threads), 0, stream, p);
-    else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, false>), grid, dim3(kF8Threads), 0, stream, p);
+    if (bias) { if (ws2) MOE_LAUNCH_F8(false, true, true); else MOE_LAUNCH_F8(false, true, false); }
+    else { if (ws2) MOE_LAUNCH_F8(false, false, true); else MOE_LAUNCH_F8(false, false, false); }
   }
+#undef MOE_LAUNCH_F8
   return hipGetLastError();
 }
 
@@ -352,8 +381,8 @@ hipError_t launch_gemm_per_token(const GemmParams& p, bool bias, hipStream_t str
   if (p.max_blocks <= 0) return hipSuccess;
   const int bn = kWavesN * 32 * kF8NT;
   const dim3 grid((uint32_t)((p.N + bn - 1) / bn * (int64_t)p.max_blocks));
-  if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, true>), grid, dim3(kF8Threads), 0, stream, p);
-  else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, true>), grid, dim3(kF8Threads), 0, stream, p);
+  if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, true, false>), grid, dim3(kF8Threads), 0, stream, p);
+  else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, true, false>), grid, dim3(kF8Threads), 0, stream, p);
   return hipGetLastError();
 }
 
