@@ -306,7 +306,9 @@ moe_status moe_combine(const void* c, int64_t c_ld, const float* topk_w,
  * row stride grad_ld; dw (device) fp32 [E][N][K] contiguous.
  * Requirements: block_m == moe_wgrad_block_m(); num_experts <= 1024;
  * n % 32 == 0, k % 32 == 0; x_ld, grad_ld multiples of 8; x, grad and dw
- * 16-byte aligned; x and grad each span less than 2 GB.
+ * 16-byte aligned; x and grad each span less than 2 GB; the routing arrays
+ * non-null whenever max_blocks > 0 (also with no tokens: dW is then written
+ * as zeros); x and grad may be NULL when num_tokens = 0.
  * No workspace.
  * ---------------------------------------------------------------------- */
 moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad_ld,

@@ -375,8 +375,10 @@ moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad
     return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks %lld < required %lld", (long long)max_blocks,
                 (long long)need);
   if (max_blocks * block_m >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks too large");
-  if (dw == nullptr || (S > 0 && (x == nullptr || grad == nullptr || sorted_token_ids == nullptr ||
-                                  expert_ids == nullptr)))
+  // the kernel runs even with no slots (it writes dW as zeros) and reads the
+  // routing arrays whenever they have blocks
+  if (dw == nullptr || (S > 0 && (x == nullptr || grad == nullptr)) ||
+      (max_blocks > 0 && (sorted_token_ids == nullptr || expert_ids == nullptr)))
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (((uintptr_t)x | (uintptr_t)grad | (uintptr_t)dw) % 16 != 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "x, grad and dw must be 16-byte aligned");

@@ -86,3 +86,18 @@ def test_full_size_sampled_experts():
         assert_parity(got, ref, what=f"expert {e} ({counts[e]} slots)")
     # the last expert's output lives past INT32_MAX elements
     assert 255 * 2048 * 7168 > 2 ** 31 - 1
+
+
+def test_no_tokens_writes_zero_dw():
+    # with no routed token every expert is empty: dW is written as zeros
+    import mixture_experts_grouped_moe_amd as moe
+    E, N, K = 4, 64, 96
+    ids = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
+    routing = moe.moe_align(ids, E, moe.moe_wgrad_block_m())
+    x = torch.zeros((0, K), dtype=torch.bfloat16, device="cuda")
+    grad = torch.zeros((0, N), dtype=torch.bfloat16, device="cuda")
+    dw = torch.full((E, N, K), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_wgrad(x, grad, routing, 0, 2, E, out=dw)
+    torch.cuda.synchronize()
+    assert routing[1].numel() == 0 or (routing[1] == -1).all()
+    assert torch.equal(dw, torch.zeros_like(dw))

@@ -332,6 +332,9 @@ def test_wgrad_rejects(no_device):
     assert call(dw=None) == INVALID
     assert call(xld=100) == INVALID
     assert call(T=-1) == INVALID
+    # no tokens: the kernel still runs (dW = 0) and reads the routing arrays when they have blocks
+    assert call(T=0, x=None, g=None, e=None, mb=4) == INVALID
+    assert call(T=0, x=None, g=None, s=None, mb=4) == INVALID
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
