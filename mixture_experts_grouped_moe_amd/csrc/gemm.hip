@@ -17,11 +17,12 @@
 //    past N, or whose 64 rows hold only padding (real rows come first in a
 //    block), skips its MFMAs but still loads its share and joins every
 //    barrier.
-//  * Each 64-wide K step moves 8 KB of activations and 16 KB of weight codes
-//    (512 rows of E2M1, 256 of E4M3) or 32 KB of bf16 weights straight from
-//    global memory into LDS with buffer_load ... lds (no registers; rows past
-//    N, PAD rows and the K tail read as zeros through the buffer bounds),
-//    three stages deep, one barrier per step. The E8M0 bytes of a lane's
+//  * Each 64-wide K step moves 8 KB of activations and the weight codes of
+//    the N tile (512 rows: 16 KB of E2M1, 32 KB of E4M3; 256 rows: 32 KB of
+//    bf16) straight from global memory into LDS with buffer_load ... lds (no
+//    registers; rows past N, PAD rows and the K tail read as zeros through
+//    the buffer bounds), three stages deep (two for E4M3), one barrier per
+//    step. The E8M0 bytes of a lane's
 //    weight rows arrive in registers with byte loads issued one step ahead
 //    of their step's tiles, right after the compute that frees their
 //    registers (issued with the tiles, last, they held up each step's wait:
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   constexpr int UW = RB / 16;                       // 16-byte units per weight row per step
   constexpr int KPU = 64 / UW;                      // K elements per weight unit
   constexpr int A_BYTES = kBM * 128;                // 8 KB
-  constexpr int W_BYTES = BN * RB;                  // 16 KB (32 KB for bf16)
+  constexpr int W_BYTES = BN * RB;                  // 16 KB (E2M1), 32 KB (E4M3, bf16)
   constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // one 1 KB wave-wide load per instruction
   constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;
   constexpr int S_LOADS = (WDT == W_BF16) ? 0 : NT;  // scale bytes per lane per step

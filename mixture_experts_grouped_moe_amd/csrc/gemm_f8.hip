@@ -15,8 +15,8 @@
 //    64-row block, which took the MXFP8 workload from 2.24 to 2.05 ms.
 //  * Each 64-wide K step moves 8 KB of activation codes and 32 KB of weight
 //    codes straight into LDS with buffer_load ... lds, three stages deep (two
-//    steps in flight), and the step's E8M0 bytes into the lanes that use them
-//    with byte loads.
+//    steps in flight), and the step's E8M0 bytes by byte (or 2-byte) DMA
+//    into a ring of scale sets in LDS, one step ahead of the tiles.
 //  * The contraction is v_mfma_scale_f32_32x32x64_f8f6f4: one instruction
 //    per 32 x 32 output tile and K step, with the E8M0 bytes fed to it as they
 //    are (no dequantisation). Its operand layout (measured on gfx950): lane l
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
     w_k[i] = u * 16;
     w_off[i] = wr >= 0 ? (uint32_t)((int64_t)wr * p.w_row + u * 16) : kOOB;
   }
-  // Scale bytes of K block 2 * step + h go by DMA into the stage (one zero-
+  // Scale bytes of K block 2 * step + h go by DMA into a scale set (one zero-
   // extended dword per byte, lane order: 32-row group, then h, then the
   // row's place in the group), where each wave reads those of its own rows
   // and columns: the waves of a row group or of a column group would
