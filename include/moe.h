@@ -150,7 +150,7 @@ const char* moe_last_error(void);
  * The result is unique (a stable counting sort), and bit-identical run to run.
  * num_tokens = 0 is legal: writes 0 and max_blocks sentinel blocks.
  * Requirements: 1 <= top_k <= num_experts <= 1024, 1 <= block_m <= 256,
- * num_tokens * top_k < 2^31. No workspace. */
+ * num_tokens * top_k <= 2^31 - 2^16. No workspace. */
 moe_status moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t top_k,
                      int32_t num_experts, int32_t block_m,
                      int32_t* sorted_token_ids, int32_t* expert_ids,

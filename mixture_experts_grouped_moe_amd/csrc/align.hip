@@ -10,10 +10,14 @@
 // One workgroup of 1024 threads does the whole job: the sizes on this path
 // (at most a few hundred thousand slots, at most 1024 experts) keep it in the
 // microsecond range, and one workgroup needs no cross-workgroup
-// synchronisation and no workspace. The scatter walks the slots in order,
-// 1024 at a time; inside a chunk each wave ranks equal expert ids with
-// ballots, so the order within an expert is ascending slot order and the
-// result is unique and deterministic.
+// synchronisation and no workspace. Each of up to 16 waves owns a contiguous
+// run of slots: it counts its run's slots per expert, a scan in expert-major,
+// wave-minor order gives every wave its first position per expert, and each
+// wave then scatters its own run 64 slots at a time, ranking equal expert
+// ids with ballots and advancing its own per-expert counters. The order
+// within an expert is therefore ascending slot order (runs in slot order,
+// batches in order, lanes in order), the result unique and deterministic,
+// and the scatter needs no workgroup barrier.
 #include "common.h"
 #include "params.h"
 
@@ -22,7 +26,7 @@ namespace moe {
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 constexpr int kAlignMaxExperts = 1024;
-constexpr int kAlignBatch = 4;  // slots per thread per batch (loads issued together)
+constexpr int kAlignBatch = 8;  // 64-slot batches whose ids a wave loads together
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int32_t S, int32_t E, int32_t B,
@@ -30,30 +34,46 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     int32_t* __restrict__ post_pad, int32_t max_blocks) {
   __shared__ int32_t cnt[kAlignMaxExperts];
   __shared__ int32_t off[kAlignMaxExperts];   // exclusive scan of padded counts
-  __shared__ int32_t run[kAlignMaxExperts];   // next free position per expert
-  __shared__ int32_t wave_cnt[kAlignWaves][kAlignMaxExperts];
+  // per wave and expert: the count of the wave's run, then its next position
+  __shared__ int32_t wave_pos[kAlignWaves][kAlignMaxExperts];
   __shared__ int32_t wave_sum[kAlignWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
+  // this wave's run of slots: one run per 64 slots, at most one per wave, so
+  // small inputs leave most waves (and their counters) idle
+  const int runs = min(kAlignWaves, S / kWave + 1);
+  const int run_len = S / runs + (S % runs != 0);
+  const int r0 = min(wave * run_len, S), r1 = min(r0 + run_len, S);
 
-  for (int e = tid; e < kAlignMaxExperts; e += kAlignThreads) cnt[e] = 0;
-  for (int i = tid; i < kAlignWaves * kAlignMaxExperts; i += kAlignThreads)
-    (&wave_cnt[0][0])[i] = 0;
+  for (int i = tid; i < runs * kAlignMaxExperts; i += kAlignThreads)
+    (&wave_pos[0][0])[i] = 0;
   __syncthreads();
 
-  // 1. histogram
-  for (int s = tid; s < S; s += kAlignThreads) {
-    int e = ids[s];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  // 1. per-wave histogram of its run
+  for (int base = r0; base < r1; base += kWave * kAlignBatch) {
+    int ev[kAlignBatch];
+#pragma unroll
+    for (int i = 0; i < kAlignBatch; ++i) {
+      const int s = base + i * kWave + lane;
+      ev[i] = s < r1 ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kAlignBatch; ++i) {
+      if (base + i * kWave >= r1) break;  // uniform across the wave
+      if (ev[i] >= 0 && ev[i] < E) atomicAdd(&wave_pos[wave][ev[i]], 1);
+    }
   }
   __syncthreads();
 
-  // 2. exclusive scan of p_e = ceil(c_e / B) * B over experts (E <= 1024:
-  //    one value per thread; wave-level inclusive scan, then across waves).
-  int p = 0;
-  if (tid < E) p = ((cnt[tid] + B - 1) / B) * B;
+  // 2. per-expert totals, exclusive scan of p_e = ceil(c_e / B) * B over
+  //    experts (E <= 1024: one value per thread; wave-level inclusive scan,
+  //    then across waves), and each wave's first position per expert
+  int c = 0;
+  if (tid < E)
+    for (int w = 0; w < runs; ++w) c += wave_pos[w][tid];
+  const int p = ((c + B - 1) / B) * B;
   int incl = p;
   for (int d = 1; d < kWave; d <<= 1) {
     int v = __shfl_up(incl, d, kWave);
@@ -65,9 +85,16 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   for (int w = 0; w < wave; ++w) before += wave_sum[w];
   int total = 0;
   for (int w = 0; w < kAlignWaves; ++w) total += wave_sum[w];
+  const int o_e = before + incl - p;
   if (tid < E) {
-    off[tid] = before + incl - p;
-    run[tid] = before + incl - p;
+    off[tid] = o_e;
+    cnt[tid] = c;
+    int next = o_e;
+    for (int w = 0; w < runs; ++w) {
+      const int t = wave_pos[w][tid];
+      wave_pos[w][tid] = next;
+      next += t;
+    }
   }
   if (tid == 0) *post_pad = total;
   __syncthreads();
@@ -87,58 +114,53 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     }
     expert_ids[b] = e;
   }
-  // 4. PAD: the tail of each expert's segment and everything past `total`.
+  // 4. PAD: the tail of each expert's segment (under 32 positions: one thread
+  //    per expert; otherwise one wave per expert, lanes on consecutive
+  //    positions) and everything past `total`.
   const int32_t pad = S;
-  if (tid < E) {
-    int start = off[tid] + cnt[tid];
-    int end = off[tid] + p;
-    for (int q = start; q < end; ++q) sorted_ids[q] = pad;
+  if (B <= 32) {
+    if (tid < E)
+      for (int q = o_e + c; q < o_e + p; ++q) sorted_ids[q] = pad;
+  } else {
+    for (int e = wave; e < E; e += kAlignWaves) {
+      const int o = off[e], c_e = cnt[e];
+      const int end = o + ((c_e + B - 1) / B) * B;
+      for (int q = o + c_e + lane; q < end; q += kWave) sorted_ids[q] = pad;
+    }
   }
   const int64_t len = (int64_t)max_blocks * B;
   for (int64_t q = total + tid; q < len; q += kAlignThreads) sorted_ids[q] = pad;
 
-  // 5. stable scatter, 1024 slots per step, kAlignBatch steps per batch of loads.
-  for (int base = 0; base < S; base += kAlignThreads * kAlignBatch) {
+  // 5. each wave scatters its run in order, 64 slots at a time
+  for (int base = r0; base < r1; base += kWave * kAlignBatch) {
     int ev[kAlignBatch];
 #pragma unroll
     for (int i = 0; i < kAlignBatch; ++i) {
-      int s = base + i * kAlignThreads + tid;
-      ev[i] = s < S ? ids[s] : -1;
+      const int s = base + i * kWave + lane;
+      ev[i] = s < r1 ? ids[s] : -1;
     }
 #pragma unroll
     for (int i = 0; i < kAlignBatch; ++i) {
-      const int s = base + i * kAlignThreads + tid;
-      if (base + i * kAlignThreads >= S) break;  // uniform across the workgroup
+      if (base + i * kWave >= r1) break;  // uniform across the wave
+      const int s = base + i * kWave + lane;
       const int e = ev[i];
       const bool valid = e >= 0 && e < E;
-      // lanes of this wave holding the same expert id
+      // lanes of this batch holding the same expert id
       uint64_t m = __ballot(valid);
 #pragma unroll
       for (int bit = 0; bit < 10; ++bit) {
-        bool one = (e >> bit) & 1;
-        uint64_t bal = __ballot(one);
+        const bool one = (e >> bit) & 1;
+        const uint64_t bal = __ballot(one);
         m &= one ? bal : ~bal;
       }
-      const uint64_t below = m & ((1ull << lane) - 1ull);
-      const int rank = __popcll(below);
-      if (valid && below == 0) wave_cnt[wave][e] = __popcll(m);
-      __syncthreads();
-      if (valid) {
-        int pos = run[e] + rank;
-        for (int w = 0; w < wave; ++w) pos += wave_cnt[w][e];
-        sorted_ids[pos] = s;
-      }
-      __syncthreads();
-      if (tid < E) {
-        int add = 0;
-#pragma unroll
-        for (int w = 0; w < kAlignWaves; ++w) {
-          add += wave_cnt[w][tid];
-          wave_cnt[w][tid] = 0;
-        }
-        run[tid] += add;
-      }
-      __syncthreads();
+      const int rank = __popcll(m & ((1ull << lane) - 1ull));
+      int pos = 0;
+      if (valid) pos = wave_pos[wave][e] + rank;
+      // the lowest lane of each expert advances the wave's counter; its
+      // write depends on its own read, and one wave's LDS operations run in
+      // order, so every lane has read the position first
+      if (valid && rank == 0) wave_pos[wave][e] = pos + __popcll(m);
+      if (valid) sorted_ids[pos] = s;
     }
   }
 }

@@ -135,7 +135,8 @@ moe_status moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t top_k,
     return fail(MOE_ERR_UNSUPPORTED, "num_experts %d > %d", num_experts, kAlignMaxExperts);
   if (block_m < 1 || block_m > 256) return fail(MOE_ERR_INVALID_ARGUMENT, "block_m %d not in [1, 256]", block_m);
   const int64_t S = num_tokens * top_k;
-  if (S >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens * top_k must be < 2^31");
+  // the kernel's slot indices run up to 512 past the last slot
+  if (S > INT32_MAX - 65536) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens * top_k must be <= 2^31 - 2^16");
   const int64_t need = moe_align_max_blocks(S, num_experts, block_m);
   if (max_blocks < need)
     return fail(MOE_ERR_INVALID_ARGUMENT, "max_blocks %lld < required %lld", (long long)max_blocks,

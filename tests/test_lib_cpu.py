@@ -120,6 +120,9 @@ def test_align_rejects(no_device):
     assert _align(ids=None) == INVALID
     assert _align(p=None) == INVALID
     assert _align(s=None) == INVALID
+    # slot counts within 2^16 of 2^31 are refused before any launch
+    assert _align(T=(2 ** 31 - 2 ** 16) // 2 + 1, k=2, E=8, B=1) == INVALID
+    assert b"2^16" in L.moe_last_error()
 
 
 def _gemm_args(**kw):
