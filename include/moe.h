@@ -220,7 +220,9 @@ typedef struct {
   const int32_t* expert_ids;       /* (device) */
   const int32_t* num_tokens_post_pad; /* (device) */
   int32_t block_m;        /* must equal moe_gemm_block_m(a_dtype, w_dtype, T) */
-  int64_t max_blocks;     /* length of expert_ids */
+  int64_t max_blocks;     /* length of expert_ids; only the first
+                             moe_align_max_blocks(S, E, block_m) blocks
+                             (every block moe_align can fill) are read */
 } moe_gemm_args;
 
 /* Requirements: k % 32 == 0 and k >= 32; n >= 1 (even with SwiGLU);

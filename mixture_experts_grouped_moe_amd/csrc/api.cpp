@@ -259,7 +259,9 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   p.S = (int32_t)S;
   p.N = (int32_t)a.n;
   p.K = (int32_t)a.k;
-  p.max_blocks = (int32_t)a.max_blocks;
+  // at most `need` blocks are in use (one per started BLOCK_M rows of each
+  // touched expert); the rest are sentinels, so the grid stops there
+  p.max_blocks = (int32_t)need;
   p.relu2 = a.epilogue == MOE_EPILOGUE_RELU2 ? 1 : 0;
   p.E = a.num_experts;
   const bool bias = a.bias != nullptr;
