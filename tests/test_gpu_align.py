@@ -106,3 +106,15 @@ def test_deterministic():
     b = _run(synth.bits(ids), 256, 64)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("S", [63, 64, 65, 511, 512, 513, 959, 960, 961, 1023, 1024, 1025, 8191])
+def test_run_boundaries(S):
+    # the slots split into one run per 64 slots, at most 16 runs: slot counts
+    # on either side of a run edge, with block sizes on both sides of the
+    # per-thread / per-wave padding switch (32), one heavy expert spanning runs
+    rng = np.random.default_rng(S)
+    for E, B in ((3, 1), (128, 32), (128, 33), (1024, 64)):
+        ids = rng.integers(0, E, size=(S, 1)).astype(np.int32)
+        ids[S // 3: S // 3 + S // 4, 0] = E - 1
+        _check(ids, E, B, extra_blocks=1)
