@@ -350,3 +350,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         f'LIB_PATH = {str(tmp_path / "missing.so")!r}')
     with pytest.raises(ImportError):
         exec(compile(src, spec.origin, "exec"), mod.__dict__)
+
+
+def test_max_blocks_bounds_the_used_blocks():
+    # the grouped GEMM launches moe_align_max_blocks(S, E, B) routing blocks:
+    # the oracle's used block count never exceeds it, and it is reached when
+    # every touched expert needs one more block than S / B alone would give
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        E = int(rng.integers(1, 300))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 400))
+        B = int(rng.choice([1, 2, 8, 16, 64, 128, 256]))
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32).reshape(T, k)
+        _, _, post_pad = oalign.moe_align(ids, E, B)
+        assert post_pad % B == 0
+        assert post_pad // B <= moe.moe_align_max_blocks(T * k, E, B)
+    # tight case: E experts with one slot each
+    E, B = 40, 16
+    _, _, post_pad = oalign.moe_align(np.arange(E, dtype=np.int32).reshape(E, 1), E, B)
+    assert post_pad // B == moe.moe_align_max_blocks(E, E, B) == E
