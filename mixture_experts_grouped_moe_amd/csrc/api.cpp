@@ -446,7 +446,7 @@ moe_status moe_grouped_gemm_per_token(const moe_per_token_args* g, moe_stream_t 
   if (a.w_layout != MOE_LAYOUT_ROWS && a.w_layout != MOE_LAYOUT_KBLOCK)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown w_layout %d", a.w_layout);
   const bool kblock = a.w_layout == MOE_LAYOUT_KBLOCK;
-  if (kblock && a.k % 32 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "the K-block layout needs k % 32 == 0");
+  if (kblock && a.k % 32 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "the K-block layout needs k %% 32 == 0");
   const int64_t nblk = (a.k + 63) / 64;
   if (a.w_ld % 16 != 0 || a.w_stride_e % 16 != 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld and w_stride_e must be multiples of 16 bytes");

@@ -275,6 +275,7 @@ def test_grouped_gemm_per_token_rejects(no_device):
     assert _per_token(w_stride_e=100) == INVALID
     assert _per_token(w_layout=7) == INVALID
     assert _per_token(k=48, a_ld=48, w_ld=48, w_stride_e=256 * 48, w_layout=moe.MOE_LAYOUT_KBLOCK) == INVALID
+    assert L.moe_last_error().endswith(b"needs k % 32 == 0")
     assert _per_token(w_layout=moe.MOE_LAYOUT_KBLOCK, w_ld=256 * 64 - 16) == INVALID
     assert _per_token(c_ld=255) == INVALID
     assert _per_token(bias=0x100000, bias_stride_e=-1) == INVALID
