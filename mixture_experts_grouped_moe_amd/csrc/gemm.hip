@@ -55,7 +55,7 @@ namespace moe {
 template <int WDT> struct WTraits;
 template <> struct WTraits<W_E2M1> { static constexpr int kRowBytes = 32, kNT = 4, kStages = 3; };
 template <> struct WTraits<W_E4M3> { static constexpr int kRowBytes = 64, kNT = 4, kStages = 2; };
-template <> struct WTraits<W_BF16> { static constexpr int kRowBytes = 128, kNT = 2, kStages = 3; };
+template <> struct WTraits<W_BF16> { static constexpr int kRowBytes = 128, kNT = 2, kStages = 2; };
 
 template <int WDT, bool SWIGLU, bool BIAS>
 __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmParams p) {
@@ -80,12 +80,13 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
   static_assert(WAIT_N < 64, "vmcnt range");
 
-  // LDS: STAGES x [A tile | weight tile] (E4M3: two 40 KB stages, so two
-  // workgroups fill a CU's 160 KB exactly; the block's slot list is read from
-  // global memory until the epilogue, which keeps it in stage 0)
+  // LDS: STAGES x [A tile | weight tile] (E4M3 and bf16: two 40 KB stages,
+  // so two workgroups fill a CU's 160 KB exactly; with three stages a bf16
+  // workgroup had the CU to itself and ran 19% slower. The block's slot list
+  // is read from global memory until the epilogue, which keeps it in stage 0)
   constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][STAGE_BYTES];
-  static_assert(kMinBlocks * STAGES * STAGE_BYTES <= 160 * 1024 || WDT == W_BF16, "two workgroups per CU");
+  static_assert(kMinBlocks * STAGES * STAGE_BYTES <= 160 * 1024, "two workgroups per CU");
 
   const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
   const int b = L % p.max_blocks;
