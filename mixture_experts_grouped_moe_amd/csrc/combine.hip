@@ -14,6 +14,8 @@ namespace moe {
 
 constexpr int kCombineThreads = 256;
 
+constexpr int kCombineBatch = 8;  // slots whose loads are issued together
+
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const uint16_t* __restrict__ c, int64_t c_ld, const float* __restrict__ w,
     int64_t T, int32_t top_k, int32_t n8, uint16_t* __restrict__ y, int64_t y_ld) {
@@ -24,13 +26,26 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int j = 0; j < top_k; ++j) {
-    const float wj = w[t * top_k + j];
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(c + (t * top_k + j) * c_ld + col);
+  // up to 8 slots' weights and rows are loaded before any is used (one
+  // memory round trip instead of one per slot); the sum runs over j in order
+  for (int j0 = 0; j0 < top_k; j0 += kCombineBatch) {
+    float wj[kCombineBatch];
+    u32x4_t v[kCombineBatch];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += wj * bf16_bits_to_f32(v[q] & 0xffffu);
-      acc[2 * q + 1] += wj * bf16_bits_to_f32(v[q] >> 16);
+    for (int jj = 0; jj < kCombineBatch; ++jj) {
+      const int64_t sl = t * top_k + j0 + jj;
+      const bool ok = j0 + jj < top_k;
+      wj[jj] = ok ? w[sl] : 0.0f;
+      v[jj] = ok ? *reinterpret_cast<const u32x4_t*>(c + sl * c_ld + col) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int jj = 0; jj < kCombineBatch; ++jj) {
+      if (j0 + jj >= top_k) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += wj[jj] * bf16_bits_to_f32(v[jj][q] & 0xffffu);
+        acc[2 * q + 1] += wj[jj] * bf16_bits_to_f32(v[jj][q] >> 16);
+      }
     }
   }
   u32x4_t o;
