@@ -217,3 +217,31 @@ def test_config4_mxfp8_full_size_sampled():
                                           ids, E, slots=slots)
     assert routed_mask[slots].all()
     assert_parity(bf16_to_f64(C[slots]), ref[slots], what="config4 sampled slots")
+
+
+def test_bf16_packed_swiglu_large_sampled():
+    # bf16 weights at a gate+up shape (N = 5760 -> 2880 SwiGLU columns,
+    # K = 2880) in the packed layout, many routing blocks per expert: the
+    # two-stage bf16 kernel checked on first / middle / last slots of three
+    # experts
+    moe = _moe()
+    from helpers import LazyRows
+    T, k, E, N, K = 2048, 4, 32, 5760, 2880
+    d = synth.gemm_case(T, k, E, N, K, "bf16", seed=31, bias=True, w_std=0.02, device="cuda")
+    pw = moe.moe_pack_weights(d["w"], "bf16")
+    routing = moe.moe_align(d["ids"], E, moe.moe_gemm_block_m("bf16", T))
+    C = torch.full((T * k, N // 2), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(d["x"], pw, "bf16", routing, T, k, E, k, bias=d["bias"], epilogue="swiglu", out=C)
+    torch.cuda.synchronize()
+    ids = synth.bits(d["ids"]).reshape(-1)
+    counts = np.bincount(ids, minlength=E)
+    slots = []
+    for e in (int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30))), E - 1):
+        es = np.nonzero(ids == e)[0]
+        if es.size:
+            slots += [int(es[0]), int(es[len(es) // 2]), int(es[-1])]
+    slots = sorted(set(slots))
+    ref, routed_mask = ogemm.grouped_gemm(synth.bits(d["x"]), k, LazyRows(d["w"]), "bf16", None, ids, E,
+                                          bias=synth.bits(d["bias"]), epilogue="swiglu", slots=slots)
+    assert routed_mask[slots].all()
+    assert_parity(bf16_to_f64(C[slots]), ref[slots], what="bf16 packed SwiGLU sampled slots")
