@@ -56,3 +56,31 @@ def test_grouped_gemm_random_shapes(seed):
                                      bias=h["bias"], epilogue=c["epilogue"])
     assert routed.all()
     assert_parity(bf16_to_f64(out), ref, what=f"case {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mxfp8_activation_gemm_random_shapes(seed):
+    # E4M3 activation codes with E8M0 scales (the scaled fp8 MFMA kernel):
+    # the same random shapes, activations drawn directly as codes and scales
+    import mixture_experts_grouped_moe_amd as moe
+    c = _case(3 * seed + 1)
+    print("case", seed, c, flush=True)
+    T, k, E, N, K = c["T"], c["k"], c["E"], c["N"], c["K"]
+    a_rows, a_row_div = (T * k, 1) if c["over_slots"] else (T, k)
+    d = synth.gemm_case(T, k, E, N, K, "e4m3", seed=seed, bias=c["bias"], a_rows=a_rows, w_std=0.5, device="cuda")
+    a_codes = synth.e4m3_normal((a_rows, K), 1.0, seed, "xq")
+    a_scales = synth.e8m0_uniform((a_rows, K // 32), 120, 130, seed, "xs")
+    w = moe.moe_pack_weights(d["w"], "e4m3", w_scale=d["w_scale"]) if c["packed"] else d["w"]
+    routing = moe.moe_align(d["ids"], E, moe.moe_gemm_block_m("e4m3", T, moe.MOE_E4M3))
+    n_out = N // 2 if c["epilogue"] == "swiglu" else N
+    out = torch.full((T * k, n_out), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(a_codes.cuda(), w, "e4m3", routing, T, k, E, a_row_div,
+                         w_scale=None if c["packed"] else d["w_scale"], bias=d["bias"], epilogue=c["epilogue"],
+                         out=out, a_scale=a_scales.cuda())
+    torch.cuda.synchronize()
+    h = host(d)
+    ref, routed = ogemm.grouped_gemm(synth.bits(a_codes), a_row_div, h["w"], "e4m3", h["w_scale"], h["ids"], E,
+                                     bias=h["bias"], epilogue=c["epilogue"], a_dtype="e4m3",
+                                     a_scale=synth.bits(a_scales))
+    assert routed.all()
+    assert_parity(bf16_to_f64(out), ref, what=f"mxfp8 activations, case {seed}")
