@@ -84,3 +84,27 @@ def test_mxfp8_activation_gemm_random_shapes(seed):
                                      a_scale=synth.bits(a_scales))
     assert routed.all()
     assert_parity(bf16_to_f64(out), ref, what=f"mxfp8 activations, case {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_per_token_gemm_random_groups(seed):
+    # the group_sizes interface: random expert counts (about a third of the
+    # groups empty), random N, K a multiple of 16, bias and packed weights
+    # (K a multiple of 32) at random
+    import mixture_experts_grouped_moe_amd as moe
+    rng = np.random.default_rng(2000 + seed)
+    E = int(rng.integers(1, 40))
+    gs = [0 if rng.random() < 0.3 else int(rng.integers(1, 300)) for _ in range(E)]
+    N = int(rng.integers(1, 1100))
+    K = 16 * int(rng.integers(1, 80))
+    bias = bool(rng.integers(0, 2))
+    packed = K % 32 == 0 and bool(rng.integers(0, 2))
+    print("case", seed, dict(E=E, R=sum(gs), N=N, K=K, bias=bias, packed=packed), flush=True)
+    d = synth.per_token_case(gs, N, K, seed, bias=bias, device="cuda")
+    w = moe.moe_pack_weights(d["w"], "e4m3") if packed else d["w"]
+    mapping = moe.moe_block_mapping(d["group_sizes"], d["R"])
+    out = moe.moe_grouped_gemm_per_token(d["a"], d["a_scale"], w, d["w_scale"], mapping, bias=d["bias"])
+    torch.cuda.synchronize()
+    h = {k: synth.bits(v) if isinstance(v, torch.Tensor) else v for k, v in d.items()}
+    ref = ogemm.grouped_gemm_per_token(h["a"], h["a_scale"], h["w"], h["w_scale"], h["group_sizes"], bias=h["bias"])
+    assert_parity(bf16_to_f64(out), ref, what=f"per-token case {seed}")
