@@ -108,3 +108,28 @@ def test_per_token_gemm_random_groups(seed):
     h = {k: synth.bits(v) if isinstance(v, torch.Tensor) else v for k, v in d.items()}
     ref = ogemm.grouped_gemm_per_token(h["a"], h["a_scale"], h["w"], h["w_scale"], h["group_sizes"], bias=h["bias"])
     assert_parity(bf16_to_f64(out), ref, what=f"per-token case {seed}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_wgrad_random_shapes(seed):
+    # dW[e] = sum over e's slots of grad[s]^T x[s // k] on random shapes
+    # (N and K multiples of 32, empty experts likely at large E), every
+    # expert checked in full
+    import mixture_experts_grouped_moe_amd as moe
+    from oracle import wgrad as owgrad
+    rng = np.random.default_rng(3000 + seed)
+    E = int(rng.integers(1, 48))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(1, 500))
+    N, K = 32 * int(rng.integers(1, 12)), 32 * int(rng.integers(1, 12))
+    print("case", seed, dict(T=T, k=k, E=E, N=N, K=K), flush=True)
+    d = synth.config5(seed=seed, T=T, E=E, N=N, K=K, k=k, device="cuda")
+    routing = moe.moe_align(d["ids"], E, moe.moe_wgrad_block_m())
+    dw = torch.full((E, N, K), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_wgrad(d["x"], d["grad"], routing, T, k, E, out=dw)
+    torch.cuda.synchronize()
+    h = host(d)
+    ref = owgrad.wgrad(h["x"], h["grad"], h["ids"], k, E)
+    got = dw.cpu().double().numpy()
+    for e in range(E):
+        assert_parity(got[e], ref[e], what=f"wgrad case {seed}, expert {e}")
