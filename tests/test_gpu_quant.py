@@ -79,3 +79,22 @@ def test_mxfp8_workload_activation_shape():
     # the MXFP8 workload's activations (the same draw as its x): [4096, 7168] bf16 N(0,1)
     x = synth.bf16_normal((4096, 7168), 1.0, 1004, "x", "cuda")
     _check(x)
+
+
+def test_every_bf16_value_under_a_power_of_two_block_max():
+    # every finite bf16 value v with |v| <= M, in 32-element blocks led by M,
+    # for block maxima M = 2^e across the range: each value's code at each
+    # block scale, bit-exact with the oracle
+    allbits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    vals = allbits.double()
+    vals = vals[torch.isfinite(vals)]
+    blocks = []
+    for e in range(-126, 128, 9):
+        M = 2.0 ** e
+        v = vals[vals.abs() <= M]
+        v = torch.cat([v, torch.zeros((-v.numel()) % 31, dtype=torch.float64)]).reshape(-1, 31)
+        blocks.append(torch.cat([torch.full((v.shape[0], 1), M, dtype=torch.float64), v], dim=1))
+    b = torch.cat(blocks)
+    b = torch.cat([b, torch.zeros(((-b.shape[0]) % 32, 32), dtype=torch.float64)])
+    x = b.reshape(-1, 1024).to(torch.bfloat16).cuda()
+    _check(x)
