@@ -21,6 +21,9 @@ other than itself:
     align.moe_align         pinned  (brute force on tiny inputs, invariants, hand-worked example)
     gemm.dequant_expert     pinned  (constant-input closed form, Fraction brute force)
     gemm.grouped_gemm       pinned  (constant input, bias, linearity, Fraction brute force)
+    gemm.dequant_act        pinned  (MXFP8 activations, a_scale by token row: constant input
+                                     with per-row and per-block scales, Fraction brute
+                                     force at a_row_div 1 and top_k, one scale row per token)
     gemm.silu / swiglu      pinned  (closed forms and the odd-part identity)
     gemm.relu2              pinned  (closed forms; constant-input GEMM epilogue)
     gemm.build_block_mapping pinned (hand-worked example; every row in exactly one block)

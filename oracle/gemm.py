@@ -53,7 +53,13 @@ def dequant_expert(w_codes, w_dtype, w_scale=None):
 def dequant_act(a_codes, a_dtype, a_scale=None):
     """Activation rows -> float64: "bf16" (uint16 bit patterns), "e4m3"
     (uint8 codes with E8M0 scale [R, K/32], the both-operands-MXFP8 form) or
-    "f64" (values already in float64, e.g. an earlier GEMM's unrounded output)."""
+    "f64" (values already in float64, e.g. an earlier GEMM's unrounded output).
+
+    Pinned (the "e4m3" form, through grouped_gemm with a_scale indexed by
+    the activation row s // a_row_div): tests/test_oracle_gemm.py (constant
+    codes with scales that vary per row and per K block, a Fraction triple
+    loop decoded by torch's float8_e4m3fn, one scale row per token).
+    """
     if a_dtype == "f64":
         return np.asarray(a_codes, dtype=np.float64)
     if a_dtype == "bf16":

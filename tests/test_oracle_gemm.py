@@ -288,3 +288,93 @@ def test_per_token_gemm_scalar_loop():
         for n in range(N):
             acc = sum(dec(a[r, k]) * dec(w[e, n, k]) for k in range(K))
             assert C[r, n] == pytest.approx(acc * a_s[r] * w_s[e], rel=1e-12)
+
+
+# ---- the both-operands-MXFP8 branch (a_dtype="e4m3" with an E8M0 a_scale):
+# the aiter kernel decodes an a_scale and a b_scale byte per 32-element K
+# block (second review). Pins: a constant-input closed form whose activation
+# and weight scales differ per K block and per token row, an exact Fraction
+# triple loop decoded with torch's float8_e4m3fn and Fraction powers of two,
+# and slots of one token reading one scale row.
+
+@pytest.mark.parametrize("a_row_div", ["top_k", 1])
+def test_mxfp8_activations_constant_input_closed_form(a_row_div):
+    # A codes == ca, W codes == cw; a_scale[r, b] and w_scale[e, n, b] vary
+    # with the row, the K block and the weight row, so
+    # C[s, n] = sum_b 32 dec(ca) dec(cw) 2^(sa[r, b] + sw[e, n, b] - 254), r = s // d
+    T, k, E, N, K = 5, 3, 4, 6, 128
+    d = k if a_row_div == "top_k" else 1
+    R = T * k // d
+    ids = _routing(T, k, E, 11)
+    ca, cw = 0x40, 0xBC  # 2.0 and -1.5
+    a = np.full((R, K), ca, dtype=np.uint8)
+    w = np.full((E, N, K), cw, dtype=np.uint8)
+    nb = K // 32
+    sa = np.array([[120 + (r % 5) + 2 * b for b in range(nb)] for r in range(R)], dtype=np.uint8)
+    sw = np.array([[[125 + e + (n % 3) - b for b in range(nb)] for n in range(N)] for e in range(E)],
+                  dtype=np.uint8)
+    C, routed = gemm.grouped_gemm(a, d, w, "e4m3", sw, ids, E, a_dtype="e4m3", a_scale=sa)
+    assert routed.all()
+    flat = ids.reshape(-1)
+    for s in range(T * k):
+        r, e = s // d, flat[s]
+        for n in range(N):
+            expect = sum(32 * 2.0 * -1.5 * 2.0 ** (int(sa[r, b]) + int(sw[e, n, b]) - 254) for b in range(nb))
+            assert C[s, n] == expect, (s, n)
+
+
+def test_mxfp8_activations_one_scale_row_per_token():
+    # a_row_div = top_k: the top_k slots of a token read one activation row
+    # and one scale row. With every expert's weights equal, those slots'
+    # outputs are equal, and each token's differ from its neighbours' (its
+    # own scale row), so reading the scale by slot (or by the wrong token)
+    # changes the result.
+    T, k, E, N, K = 4, 3, 5, 4, 64
+    ids = _routing(T, k, E, 12)
+    rng = np.random.default_rng(13)
+    codes = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    a = rng.choice(codes, size=(T, K)).astype(np.uint8)
+    sa = (124 + np.arange(T)[:, None] + np.array([[0, 3]])).astype(np.uint8)  # per token and block
+    w1 = rng.choice(codes, size=(1, N, K)).astype(np.uint8)
+    w = np.repeat(w1, E, axis=0)
+    sw = np.full((E, N, K // 32), 127, dtype=np.uint8)
+    C, _ = gemm.grouped_gemm(a, k, w, "e4m3", sw, ids, E, a_dtype="e4m3", a_scale=sa)
+    for t in range(T):
+        for j in range(1, k):
+            np.testing.assert_array_equal(C[t * k + j], C[t * k])
+    # the same rows with token 0's scales in place of token 1's: token 1's outputs change
+    sa2 = sa.copy()
+    sa2[1] = sa[0]
+    C2, _ = gemm.grouped_gemm(a, k, w, "e4m3", sw, ids, E, a_dtype="e4m3", a_scale=sa2)
+    assert not np.array_equal(C2[k:2 * k], C[k:2 * k])
+    np.testing.assert_array_equal(C2[:k], C[:k])
+
+
+@pytest.mark.parametrize("a_row_div", ["top_k", 1])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_mxfp8_activations_fraction_brute_force(a_row_div, seed):
+    rng = np.random.default_rng(200 + seed)
+    T, k, E, N, K = 4, 2, 3, 3, 64   # N, K, T and the row count all differ
+    d = k if a_row_div == "top_k" else 1
+    R = T * k // d
+    ids = _routing(T, k, E, 20 + seed).reshape(-1).copy()
+    ids[rng.integers(0, ids.size)] = -1  # one unrouted slot
+    codes = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    a = rng.choice(codes, size=(R, K)).astype(np.uint8)
+    sa = rng.integers(118, 137, (R, K // 32), dtype=np.uint8)
+    w = rng.choice(codes, size=(E, N, K)).astype(np.uint8)
+    sw = rng.integers(118, 137, (E, N, K // 32), dtype=np.uint8)
+    a_elem = torch.from_numpy(a).view(torch.float8_e4m3fn).double().numpy()
+    w_elem = torch.from_numpy(w).view(torch.float8_e4m3fn).double().numpy()
+    a_vals = [[_frac(a_elem[r, kk]) * Fraction(2) ** (int(sa[r, kk // 32]) - 127) for kk in range(K)]
+              for r in range(R)]
+    w_vals = [[[_frac(w_elem[e, n, kk]) * Fraction(2) ** (int(sw[e, n, kk // 32]) - 127) for kk in range(K)]
+               for n in range(N)] for e in range(E)]
+    expect = _fraction_gemm(a_vals, d, w_vals, ids.tolist(), E, None)
+    C, routed = gemm.grouped_gemm(a, d, w, "e4m3", sw, ids, E, a_dtype="e4m3", a_scale=sa)
+    assert sorted(np.nonzero(routed)[0].tolist()) == sorted(expect)
+    for s, row in expect.items():
+        for n in range(N):
+            exact = row[n]
+            got = Fraction(float(C[s, n]))
+            assert abs(got - exact) <= Fraction(1, 2 ** 45) * (1 + abs(exact)), (s, n)
