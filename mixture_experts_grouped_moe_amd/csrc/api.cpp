@@ -388,8 +388,9 @@ moe_status moe_wgrad(const void* x, int64_t x_ld, const void* grad, int64_t grad
   const int64_t tiles = (int64_t)num_experts * ((n + 255) / 256) * ((k + 255) / 256);
   if (tiles >= (int64_t)INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "too many dW tiles");
   // x and grad are read through 32-bit buffer offsets
-  if (num_tokens * x_ld * 2 >= (int64_t)0x80000000 || S * grad_ld * 2 >= (int64_t)0x80000000)
-    return fail(MOE_ERR_UNSUPPORTED, "x or grad spans 2 GB or more");
+  if (num_tokens * x_ld * 2 >= (int64_t)0x80000000 || S * grad_ld * 2 >= (int64_t)0x80000000 ||
+      n * k * 4 >= (int64_t)0x80000000)
+    return fail(MOE_ERR_UNSUPPORTED, "x, grad or one expert's dW spans 2 GB or more");
   (void)num_tokens_post_pad;
   moe_status st = check_device();
   if (st != MOE_OK) return st;

@@ -76,7 +76,8 @@ constexpr int kWgStores = 8 * 4;             // 16-byte stores per lane per tile
 constexpr int kWgPerCU = 1;                  // resident workgroups per CU
 constexpr int kWgMaxExperts = 1024;
 constexpr int kWgGroupN = 8;                 // N tiles per group of the tile order
-constexpr uint32_t kWgOOB = 0x80000000u;     // buffer offset past x and grad (each below 2 GB): reads 0
+constexpr uint32_t kWgOOB = 0x80000000u;     // buffer offset past x, grad and one expert's dW (each below 2 GB)
+constexpr int kWgStoreNT = 2;                // cache-policy bits of the dW stores: non-temporal
 static_assert(kWgGLoads == 2 && kWgXLoads == 2, "each wave loads the same 4 slot rows of both parts");
 
 typedef __attribute__((address_space(3))) uint8_t wg_lds_u8_t;
@@ -342,7 +343,11 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
     // 512-byte row pieces with 16-byte stores.
     __syncthreads();
     {
-      float* out = p.dw + (int64_t)t.e * p.N * p.K;
+      // every lane issues its kWgStores stores, also at the N and K edges
+      // (lanes past them write through an offset past the expert's dW, which
+      // the buffer drops), so the waits above, which count them, stay exact
+      const __amdgpu_buffer_rsrc_t dw_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.dw + (int64_t)t.e * p.N * p.K), 0, (int)(uint32_t)((int64_t)p.N * p.K * 4), 0x00020000);
       const int free_stage = st == 0 ? kWgStages - 1 : st - 1;
       __attribute__((address_space(3))) float* scr =
           (__attribute__((address_space(3))) float*)&lds[free_stage][wave * 8 * 512];
@@ -361,7 +366,8 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
           const f32x4_t v = *(const __attribute__((address_space(3))) f32x4_t*)&scr[lr * 128 + ((4 * l32) ^ (32 * (lr / 4)))];
           const int n = t.n0 + wn * 64 + i * 32 + 8 * q + lr;
           const int k = t.k0 + wk * 128 + 4 * l32;
-          if (n < p.N && k < p.K) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(&out[(int64_t)n * p.K + k]));
+          const uint32_t off = (n < p.N && k < p.K) ? (uint32_t)(((int64_t)n * p.K + k) * 4) : kWgOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(wg_i32x4_t, v), dw_rsrc, off, 0, kWgStoreNT);
         }
       }
     }
