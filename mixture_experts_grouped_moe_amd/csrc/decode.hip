@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kThreadsDec, 4) void moe_decode_kernel(GemmParams p
   const int b = blockIdx.x % p.max_blocks;
   const int chunk = blockIdx.x / p.max_blocks;
   const int e = p.expert_ids[b];
-  if (e < 0) return;  // sentinel block
+  if (e < 0 || e >= p.E) return;  // sentinel block (or an id outside this layer's experts)
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;

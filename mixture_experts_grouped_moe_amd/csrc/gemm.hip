@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   const int b = L % p.max_blocks;
   const int tile_n = L / p.max_blocks;
   const int e = p.expert_ids[b];
-  if (e < 0) return;  // sentinel block
+  if (e < 0 || e >= p.E) return;  // sentinel block (or an id outside this layer's experts)
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
