@@ -275,9 +275,12 @@ moe_status moe_packed_sizes(int32_t w_dtype, int64_t n, int64_t k, int64_t* w_un
  *                   +-448, sign bit when v_i < 0)
  * x (device) bf16 rows with stride x_ld elements; q (device) uint8 rows with
  * stride q_ld bytes; scales (device) uint8 rows with stride scales_ld.
+ * A block holding a NaN or an infinity is written as a NaN block: scale byte
+ * 0xFF and every code 0x7F (its dequantised values are all NaN; the other
+ * blocks are unaffected).
  * Requirements: k % 32 == 0, k >= 32; x_ld >= k and a multiple of 8; q_ld >= k
  * and a multiple of 16; scales_ld >= k / 32; x and q 16-byte aligned.
- * Otherwise MOE_ERR_INVALID_ARGUMENT, nothing launched. Inputs are finite.
+ * Otherwise MOE_ERR_INVALID_ARGUMENT, nothing launched.
  * ---------------------------------------------------------------------- */
 moe_status moe_quantize_mxfp8(const void* x, int64_t x_ld, int64_t rows, int64_t k,
                               void* q, int64_t q_ld, uint8_t* scales, int64_t scales_ld,

@@ -8,6 +8,10 @@
 //       clamped to [-127, 127]; an all-zero block takes -127; byte X + 127;
 //   code = E4M3 nearest to v / 2^X, ties to even, saturating at +-448,
 //       sign bit set when v < 0.
+// A block holding a NaN or an infinity has no finite shared exponent: it is
+// written as a NaN block (scale byte 0xFF, every code 0x7F), so the
+// non-finite input never turns into finite codes or leaks into the bytes of
+// its neighbours.
 //
 // HBM-bound: one thread per (row, 32-element block) reads 64 bytes, writes
 // 32 code bytes and one scale byte; a wave covers 4 KB of contiguous input.
@@ -54,6 +58,14 @@ __global__ __launch_bounds__(kQuantThreads) void quant_mxfp8_kernel(
         amax = max(amax, v[j][w] & 0x7FFFu);
         amax = max(amax, (v[j][w] >> 16) & 0x7FFFu);
       }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(q + row * q_ld + (int64_t)b * 32);
+    if (amax >= 0x7F80u) {  // exponent field all ones: a NaN or an infinity in the block
+      const uint32_t nan4 = 0x7F7F7F7Fu;
+      dst[0] = u32x4_t{nan4, nan4, nan4, nan4};
+      dst[1] = u32x4_t{nan4, nan4, nan4, nan4};
+      s[row * s_ld + b] = (uint8_t)0xFF;
+      continue;
+    }
     // floor(log2(max)) from the exponent field; a zero or subnormal maximum
     // (below 2^-126) gives X below -127, so the clamp decides
     const int e = (int)(amax >> 7);
@@ -75,7 +87,6 @@ __global__ __launch_bounds__(kQuantThreads) void quant_mxfp8_kernel(
         // elements 8j + 2w, 8j + 2w + 1 -> bytes 2w, 2w + 1 of dword j / 2 half j % 2
         out[2 * j + w / 2] = (w % 2 == 0) ? pair : (out[2 * j + w / 2] | (pair << 16));
       }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(q + row * q_ld + (int64_t)b * 32);
     dst[0] = u32x4_t{out[0], out[1], out[2], out[3]};
     dst[1] = u32x4_t{out[4], out[5], out[6], out[7]};
     s[row * s_ld + b] = (uint8_t)(X + 127);

@@ -15,7 +15,13 @@ row and each block of 32 consecutive K elements v_0 .. v_31:
              magnitudes above 448 (the largest finite E4M3) saturate to 448,
              sign bit set exactly when v_i < 0
 
-so that dec(code_i) * 2^X approximates v_i. Inputs are finite.
+so that dec(code_i) * 2^X approximates v_i.
+
+A block holding a NaN or an infinity has no finite shared exponent: it
+converts to a NaN block, scale byte 0xFF (the E8M0 NaN) and every code 0x7F
+(an E4M3 NaN), so the non-finite input is never replaced by finite numbers
+and neighbouring blocks are unaffected (a reading: the pages give no
+conversion, and the MX format's NaN scale marks the whole block NaN).
 
 Pinned by tests/test_oracle_quant.py: every finite code survives a round trip
 at a fixed shared exponent, saturation, ties, zero and clamped blocks, and
@@ -62,14 +68,16 @@ def mx_quantize_e4m3(x):
     R, K = x.shape
     assert K % MX_BLOCK == 0
     blocks = x.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    bad = ~np.isfinite(blocks).all(axis=2)          # blocks holding a NaN or an infinity
+    blocks = np.where(bad[:, :, None], 0.0, blocks)
     amax = np.abs(blocks).max(axis=2)
     # floor(log2(amax)) exactly: amax = m * 2^e with m in [0.5, 1)
     _, e = np.frexp(np.where(amax > 0, amax, 1.0))
     X = np.where(amax > 0, e - 1 - E4M3_EMAX, -127)
     X = np.clip(X, -127, 127)
     q = blocks / np.ldexp(1.0, X)[:, :, None]
-    codes = e4m3_round(q).reshape(R, K)
-    scales = (X + 127).astype(np.uint8)
+    codes = np.where(bad[:, :, None], np.uint8(0x7F), e4m3_round(q)).astype(np.uint8).reshape(R, K)
+    scales = np.where(bad, 0xFF, X + 127).astype(np.uint8)
     return codes, scales
 
 

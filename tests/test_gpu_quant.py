@@ -98,3 +98,23 @@ def test_every_bf16_value_under_a_power_of_two_block_max():
     b = torch.cat([b, torch.zeros(((-b.shape[0]) % 32, 32), dtype=torch.float64)])
     x = b.reshape(-1, 1024).to(torch.bfloat16).cuda()
     _check(x)
+
+
+def test_non_finite_blocks():
+    # blocks holding a NaN, +inf or -inf become NaN blocks (scale 0xFF, codes
+    # 0x7F) exactly as the oracle defines; their neighbours are unaffected
+    g = synth.gen(11, "quant")
+    x = torch.randn((6, 128), generator=g).to(torch.bfloat16)
+    x[0, 5] = float("nan")
+    x[1, 40] = float("inf")
+    x[2, 127] = float("-inf")
+    x[3, 64:96] = float("nan")
+    x[4, 0] = float("inf")
+    x[4, 33] = float("nan")
+    _check(x.cuda())
+    moe = _moe()
+    q, s = moe.moe_quantize_mxfp8(x.cuda())
+    torch.cuda.synchronize()
+    s = synth.bits(s)
+    assert s[0, 0] == 0xFF and s[1, 1] == 0xFF and s[2, 3] == 0xFF and s[3, 2] == 0xFF
+    assert (s[5] != 0xFF).all()

@@ -108,3 +108,23 @@ def test_dequantize_error_bound():
     assert np.array_equal(back[sat], np.sign(x[sat]) * 448.0 * np.ldexp(1.0, X[sat]))
     bound = np.maximum(np.abs(x) * 2.0 ** -4, np.ldexp(1.0, X - 10))
     assert (np.abs(back - x) <= bound)[~sat].all()
+
+
+def test_non_finite_blocks_become_nan_blocks():
+    # a block holding a NaN, +inf or -inf converts to scale 0xFF (E8M0 NaN)
+    # and codes 0x7F (E4M3 NaN); the other blocks of the row are unaffected
+    row = np.zeros((3, 96))
+    row[:, 32:64] = np.linspace(-3.0, 5.0, 32)
+    row[:, 64:] = 256.0
+    row[0, 40] = np.nan
+    row[1, 33] = np.inf
+    row[2, 63] = -np.inf
+    codes, scales = quant.mx_quantize_e4m3(row)
+    assert (scales[:, 1] == 0xFF).all() and (codes[:, 32:64] == 0x7F).all()
+    clean = np.zeros((1, 96))
+    clean[0, 64:] = 256.0
+    c0, s0 = quant.mx_quantize_e4m3(clean)
+    assert (scales[:, [0, 2]] == s0[:, [0, 2]]).all()
+    assert (codes[:, :32] == c0[:, :32]).all() and (codes[:, 64:] == c0[:, 64:]).all()
+    deq = quant.mx_dequantize_e4m3(codes, scales)
+    assert np.isnan(deq[:, 32:64]).all() and not np.isnan(deq[:, :32]).any() and not np.isnan(deq[:, 64:]).any()
