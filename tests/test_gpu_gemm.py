@@ -188,35 +188,57 @@ def test_empty_token_guard():
     assert y.shape == (0, 128)
 
 
-def test_config4_mxfp8_full_size_sampled():
+class _Cols:
+    """Rows `cols` of each expert's [N, ...] weights (or scales), fetched from
+    the device per expert: the oracle applied to a subset of weight rows
+    gives exactly those output columns, as every output column depends on its
+    own weight row only."""
+
+    def __init__(self, t, cols):
+        self.t, self.cols = t, torch.as_tensor(np.asarray(cols, dtype=np.int64), device=t.device)
+        self.shape = (t.shape[0], len(cols)) + tuple(t.shape[2:])
+
+    def __getitem__(self, e):
+        return synth.bits(self.t[int(e)].index_select(0, self.cols))
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_config4_mxfp8_full_size_sampled(bias):
     # The MXFP8 workload at its full size (E=256, top-8, K=7168, N=4096,
     # T=4096, Zipf routing with 16 empty experts) in the launch configuration
-    # the benchmark times (packed weights), checked on sampled slots: the
-    # hottest expert, the highest-numbered routed expert (its weights start
-    # past 2^31 elements) and two more, first / middle / last slot of each.
+    # the benchmark times (packed weights): one slot of every routed expert
+    # (its first, middle or last slot in turn; expert 255's weights start past
+    # 2^31 elements), plus the first / middle / last slot of the hottest
+    # expert, each on 96 output columns spread over every N tile (both edges
+    # of each 512-row tile among them).
     moe = _moe()
-    from helpers import LazyRows
-    d = synth.config4(device="cuda")
-    T, k, E = 4096, 8, 256
+    d = synth.config4(device="cuda", bias=bias)
+    T, k, E, N = 4096, 8, 256, 4096
     pw = moe.moe_pack_weights(d["w"], "e4m3", w_scale=d["w_scale"])
     bm = moe.moe_gemm_block_m("e4m3", T)
     routing = moe.moe_align(d["ids"], E, bm)
-    C = torch.full((T * k, 4096), float("nan"), dtype=torch.bfloat16, device="cuda")
-    moe.moe_grouped_gemm(d["x"], pw, "e4m3", routing, T, k, E, k, out=C)
+    C = torch.full((T * k, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(d["x"], pw, "e4m3", routing, T, k, E, k, bias=d["bias"], out=C)
     torch.cuda.synchronize()
     ids = synth.bits(d["ids"]).reshape(-1)
     counts = np.bincount(ids, minlength=E)
     routed = np.nonzero(counts)[0]
-    experts = {int(np.argmax(counts)), int(routed.max()), int(routed[len(routed) // 3]), int(routed[2 * len(routed) // 3])}
+    assert routed.size == E - 16 and routed.max() == 255
     slots = []
-    for e in sorted(experts):
+    for i, e in enumerate(routed):
         es = np.nonzero(ids == e)[0]
-        slots += [int(es[0]), int(es[len(es) // 2]), int(es[-1])]
-    slots = sorted(set(slots))
-    ref, routed_mask = ogemm.grouped_gemm(synth.bits(d["x"]), k, LazyRows(d["w"]), "e4m3", LazyRows(d["w_scale"]),
-                                          ids, E, slots=slots)
+        slots.append(int(es[(0, len(es) // 2, -1)[i % 3]]))
+    hot = np.nonzero(ids == int(np.argmax(counts)))[0]
+    slots = sorted(set(slots + [int(hot[0]), int(hot[len(hot) // 2]), int(hot[-1])]))
+    rng = np.random.default_rng(7)
+    cols = sorted(set([0, N - 1] + [t * 512 + o for t in range(N // 512) for o in (0, 511)] +
+                      rng.choice(N, 60, replace=False).tolist()))
+    bias_cols = None if d["bias"] is None else synth.bits(d["bias"])[:, cols]
+    ref, routed_mask = ogemm.grouped_gemm(synth.bits(d["x"]), k, _Cols(d["w"], cols), "e4m3",
+                                          _Cols(d["w_scale"], cols), ids, E, bias=bias_cols, slots=slots)
     assert routed_mask[slots].all()
-    assert_parity(bf16_to_f64(C[slots]), ref[slots], what="config4 sampled slots")
+    got = bf16_to_f64(C[slots][:, cols])
+    assert_parity(got, ref[slots], what=f"config4 one slot per routed expert (bias={bias})")
 
 
 def test_bf16_packed_swiglu_large_sampled():

@@ -77,7 +77,30 @@ def test_gpt_oss_layer_sampled_parity(big_layer, bias):
     T = 8192
     h, c2, y, _ = run_layer(d, T, pad=False)
     hh = host(d)
-    tokens = [0, 4097, 8191]
+    # h of 64 tokens spread over [0, 8192) (all 256 of their slots) on 96
+    # SwiGLU columns, both edges of every 256-column tile among them: the
+    # oracle's up GEMM over the matching gate and up weight rows
+    rng = np.random.default_rng(8)
+    tokens64 = sorted(set([0, 8191] + rng.choice(np.arange(1, 8191), 62, replace=False).tolist()))
+    slots64 = [t * 4 + j for t in tokens64 for j in range(4)]
+    half = 2880
+    cols = sorted(set([0, half - 1] + [c for t in range(half // 256 + 1) for c in (256 * t, 256 * t + 255)
+                                        if c < half] + rng.choice(half, 60, replace=False).tolist()))
+    rows = torch.as_tensor(np.array(cols + [half + c for c in cols], dtype=np.int64), device=d["w1"].device)
+
+    class _Rows:
+        def __init__(self, t):
+            self.t, self.shape = t, (t.shape[0], rows.numel()) + tuple(t.shape[2:])
+
+        def __getitem__(self, e):
+            return synth.bits(self.t[int(e)].index_select(0, rows))
+
+    b1 = None if hh["b1"] is None else synth.bits(d["b1"].index_select(1, rows))
+    rh64, _ = ogemm.grouped_gemm(hh["x"], 4, _Rows(d["w1"]), "e2m1x2", _Rows(d["s1"]), hh["ids"], 128,
+                                 bias=b1, epilogue="swiglu", slots=slots64)
+    assert_parity(bf16_to_f64(h[slots64][:, cols]), rh64[slots64], what="h of 64 tokens")
+    # the whole layer (h, c2, y in full width) for 8 tokens
+    tokens = [0, 1, 1234, 4097, 5000, 6553, 7680, 8191]
     slots = [t * 4 + j for t in tokens for j in range(4)]
     rh, rc2, _ = olayer.w4a16_layer(hh["x"], hh["ids"], hh["topk_w"], 4, 128, hh["w1"], hh["s1"], hh["b1"],
                                     hh["w2"], hh["s2"], hh["b2"], slots=slots)

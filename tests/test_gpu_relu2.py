@@ -74,12 +74,22 @@ def test_relu2_epilogue_mxfp8_activations():
 @pytest.mark.parametrize("M", [1, 7, 28, 120])
 def test_nemotron_relu2_layer(M):
     # the full Nemotron-shaped layer: the decode GEMM for M <= 32, the large-M
-    # one at 120 (the steady-state mid-M bucket); y and the intermediate h
+    # one at 120 (the steady-state mid-M bucket). The layer's steps run one
+    # by one so that h (after the relu2 epilogue) and the down GEMM's c2 are
+    # checked as well as y; the binding's one-call layer gives y's bits.
     moe = _moe()
     d = synth.nemotron_layer(M, device="cuda", bias=(M == 7))
+    k, E = 6, 128
+    routing = moe.moe_align(d["ids"], E, moe.moe_gemm_block_m("bf16", M))
+    h = moe.moe_grouped_gemm(d["x"], d["w1"], "bf16", routing, M, k, E, k, bias=d["b1"], epilogue="relu2")
+    c2 = moe.moe_grouped_gemm(h, d["w2"], "bf16", routing, M, k, E, 1, bias=d["b2"])
+    y_steps = moe.moe_combine(c2, d["topk_w"], k)
     y = moe.moe_relu2_layer(d["x"], d["ids"], d["topk_w"], d["w1"], d["w2"], b1=d["b1"], b2=d["b2"])
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_steps.view(torch.int16))
     hh = host(d)
-    _, _, ry = olayer.relu2_layer(hh["x"], hh["ids"], hh["topk_w"], 6, 128, hh["w1"], hh["b1"], hh["w2"],
-                                  hh["b2"])
+    rh, rc2, ry = olayer.relu2_layer(hh["x"], hh["ids"], hh["topk_w"], k, E, hh["w1"], hh["b1"], hh["w2"],
+                                     hh["b2"])
+    assert_parity(bf16_to_f64(h), rh, what=f"nemotron h M={M}")
+    assert_parity(bf16_to_f64(c2), rc2, what=f"nemotron c2 M={M}")
     assert_parity(bf16_to_f64(y), ry, what=f"nemotron layer M={M}")
