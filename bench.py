@@ -1,25 +1,36 @@
 """Benchmark of the MoE expert-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--phase both|cold|warm]
                     [--workload decode|nemotron|w4a16|mxfp8|mxfp8a|pertoken|wgrad|copy]
 
 Prints one JSON line. The default workload is the bf16 decode MoE
 (E=128, N=1856, K=2048, top-6) at the MTP6 verify token counts
-M = 1, 7, 14, 21, 28: one step runs, for each M, moe_align -> decode grouped
-GEMM -> moe_combine on a fresh routing (a seeded set of routings is cycled).
-`value` is the step's algorithmic HBM bytes over its time (GB/s); the
-per-call microseconds are reported beside it. The other workloads (the
-gpt-oss-shaped W4A16 MXFP4 layer, the 256-expert MXFP8 grouped GEMM with
-bf16 or MXFP8 activations, the per-token-scaled FP8 grouped GEMM over
-group_sizes, the weight gradient) are selected with --workload and report
-TFLOP/s.
+M = 1, 7, 14, 21, 28; a step runs, for each M, moe_align -> decode grouped
+GEMM -> moe_combine.
 
-Inputs are synthetic (seeded), generated on the device before the timed
-region. Steps are replayed from HIP graphs captured once per routing variant.
-The dominant kernel's launch duration is measured with HIP events on the
-launch stream in a second timed pass of eager launches; the roofline fraction
-uses algorithmic bytes (or flops) per launch. The CPU baseline is the float64
-oracle on a bounded sample of the same workload, timed on this host.
+Headline (`value`, `roofline`): the decode step with a cold cache. Every call
+runs on a routing and activations drawn for it alone, after a 1 GiB device
+copy that evicts the previous call's weights from the 256 MB MALL and the L2s;
+HIP events on the launch stream bracket each call and its GEMM launch (the
+copy is outside), and a GPU spin at the head of each step lets the host queue
+the whole step first. `value` = the timed calls' algorithmic HBM bytes over
+their summed event time (GB/s); `roofline` = the decode GEMM's algorithmic
+bytes over its summed launch time; `cold.per_m` gives median / p10 / p90 per
+M. `warm` holds the same workload warm (graph-replayed steps on a cycled set
+of routings, and back-to-back launches of the GEMM). `large_m` holds the
+large-M half of the metric: the W4A16 gate+up GEMM, the MXFP8 grouped GEMM and
+the weight gradient, each kernel's TFLOP/s and fraction of the bf16 MFMA peak
+and of HBM bandwidth. The GPU clock (amdsmi, read-only) is sampled in each
+timed region.
+
+The other workloads (the Nemotron relu2 decode layer, the W4A16 layer, the
+MXFP8 grouped GEMM with bf16 or MXFP8 activations, the per-token-scaled FP8
+grouped GEMM over group_sizes, the weight gradient, a 1 GiB copy) are
+selected with --workload and measured warm.
+
+Inputs are synthetic (seeded), generated on the device before any timed
+region. The CPU baseline is the float64 oracle on a bounded sample of the same
+workload, timed on this host.
 """
 
 import argparse
@@ -46,8 +57,9 @@ def parse():
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "nemotron", "w4a16", "mxfp8", "mxfp8a", "pertoken", "wgrad", "copy"])
     ap.add_argument("--variants", type=int, default=4, help="routing variants cycled across steps")
-    ap.add_argument("--launch-reps", type=int, default=10,
-                    help="back-to-back launches per event pair when timing the dominant kernel")
+    ap.add_argument("--launch-reps", type=int, default=5,
+                    help="launches of the dominant kernel per step when timing it (one event pair each, "
+                         "back to back)")
     ap.add_argument("--layout", default="auto", choices=["auto", "rows", "kblock"],
                     help="expert weight layout: rows ([E][N][K]) or kblock (packed once by moe_pack_weights "
                          "before timing); auto = kblock for the large-M workloads, rows for decode")
@@ -56,6 +68,10 @@ def parse():
                     help="no GPU run: read rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv files (-o fetch, -o write) "
                          "from DIR and record the workload's per-launch HBM traffic in profiles/counters.json")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    ap.add_argument("--phase", default="both", choices=["both", "cold", "warm"],
+                    help="decode workload: cold-cache calls (the headline), warm graph replays, or both "
+                         "(both also runs the large-M block)")
+    ap.add_argument("--no-large-m", action="store_true", help="decode workload: skip the large-M block")
     return ap.parse_args()
 
 
@@ -428,6 +444,13 @@ class W4A16(Workload):
         c = self.calls[v]
         return [(lambda c=c: self._up(c), 2 * c["T"] * self.k * 2 * self.I * self.H)]
 
+    def dominant_flops_bytes(self, v):
+        """Algorithmic flops and HBM bytes of the gate+up GEMM: the 128
+        experts' E2M1 codes and E8M0 bytes, the token rows read, h written."""
+        T = self.calls[v]["T"]
+        w = self.E * 2 * self.I * self.H // 2 * (1 + 1 / 16)
+        return 2 * T * self.k * 2 * self.I * self.H, int(w + T * self.H * 2 + T * self.k * self.I * 2)
+
     def extra(self, per_call_us):
         return {"tokens": [c["T"] for c in self.calls], "buckets": [c["Tb"] for c in self.calls]}
 
@@ -499,6 +522,9 @@ class MXFP8(Workload):
 
     def dominant_launches(self, v):
         return [(self._gemm, self.gemm_bytes())]
+
+    def dominant_flops_bytes(self, v):
+        return self.step_flops(v), self.gemm_bytes()
 
     def extra(self, per_call_us):
         return {"touched_experts": self.touched, "empty_experts": self.empty}
@@ -704,6 +730,9 @@ class Wgrad(Workload):
     def dominant_launches(self, v):
         return [(self._wgrad, self.wgrad_bytes())]
 
+    def dominant_flops_bytes(self, v):
+        return self.step_flops(v), self.wgrad_bytes()
+
     def extra(self, per_call_us):
         return {}
 
@@ -809,6 +838,277 @@ def cpu_baseline(wl, target_s):
                       f"({wl.cpu_sample_desc}), {dt:.1f} s"}
 
 
+def stats(xs):
+    """median, p10, p90 and mean of a list of numbers (linear interpolation)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 3), "p10": round(float(np.percentile(a, 10)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3), "mean": round(float(a.mean()), 3), "n": int(a.size)}
+
+
+class ClockSampler:
+    """Reads the GPU's current graphics clock through amdsmi (read-only
+    queries) in a background thread while a named region runs; regions
+    report the median, min and max of their samples in MHz."""
+
+    def __init__(self, torch):
+        import threading
+        self.samples, self.region, self.err, self.h = {}, None, None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            handles = amdsmi.amdsmi_get_processor_handles()
+            want = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+            self.h = handles[0]
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                if want is not None and int(bdf.split(":")[1], 16) == int(want):
+                    self.h = h
+            self.read()
+        except Exception as ex:  # no clock readings: reported as such
+            self.err, self.h = f"{type(ex).__name__}: {ex}", None
+        self.stop = False
+        if self.h is not None:
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
+
+    def read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        vals = m.get("current_gfxclks")
+        if isinstance(vals, (list, tuple)):
+            vals = [v for v in vals if isinstance(v, (int, float)) and 0 < v < 10000]
+            if vals:
+                return sum(vals) / len(vals)
+        for key in ("current_gfxclk", "average_gfxclk_frequency"):
+            v = m.get(key)
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                return float(v)
+        return None
+
+    def _run(self):
+        import time as _t
+        while not self.stop:
+            r = self.region
+            if r is not None:
+                try:
+                    v = self.read()
+                    if v is not None:
+                        self.samples.setdefault(r, []).append(v)
+                except Exception as ex:
+                    self.err = f"{type(ex).__name__}: {ex}"
+            _t.sleep(0.01)
+
+    def summary(self, region):
+        xs = self.samples.get(region, [])
+        if not xs:
+            return {"mhz": None, "note": self.err or "no sample taken in this region"}
+        xs = sorted(xs)
+        return {"median_mhz": round(xs[len(xs) // 2]), "min_mhz": round(xs[0]), "max_mhz": round(xs[-1]),
+                "samples": len(xs)}
+
+    def close(self):
+        self.stop = True
+
+
+DECODE_MS = (1, 7, 14, 21, 28)
+SPIN_CYCLES = 10_000_000  # torch.cuda._sleep cycles (a few ms) ahead of each cold decode step
+
+
+def decode_cold(torch, moe, dev, stream, args, clock):
+    """The decode workload with a cold cache: every call (align -> decode GEMM
+    -> combine for one M) runs on a routing and activations drawn for it
+    alone, after a 1 GiB device copy (512 MiB read, 512 MiB written) that
+    evicts the previous call's weights from the 256 MB MALL and the L2s. The
+    copy runs outside the timed span: HIP events on the launch stream bracket
+    the call and, inside it, the GEMM launch. W warmup steps, then K timed
+    steps; a step is one call for each M in 1, 7, 14, 21, 28."""
+    import numpy as np
+    import synth
+    E, N, K, k = 128, 1856, 2048, 6
+    w = synth.bf16_normal((E, N, K), 0.02, 1002, "w", dev)
+    n_steps = args.warmup + args.steps
+    calls = {}
+    for M in DECODE_MS:
+        bm = moe.moe_gemm_block_m("bf16", M)
+        lst = []
+        for r in range(n_steps):
+            x = synth.bf16_normal((M, K), 1.0, 1002, f"cold-x{M}c{r}", dev)
+            ids, tw = synth.softmax_topk_routing(M, E, k, 1002, f"cold-route{M}c{r}", dev)
+            routing = _routing_buffers(torch, M, k, E, bm, dev)
+            C = torch.empty((M * k, N), dtype=torch.bfloat16, device=dev)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            gemm, _ = moe.moe_grouped_gemm_prepare(x, w, "bf16", routing, M, k, E, k, out=C, stream=stream)
+            touched = len(np.unique(ids.cpu().numpy()))
+            S, mb = M * k, routing[1].numel()
+            gemm_bytes = touched * N * K * 2 + M * K * 2 + S * N * 2
+            call_bytes = gemm_bytes + (S * 4 + mb * bm * 4 + mb * 4 + 4) + (S * N * 2 + M * N * 2 + S * 4)
+            lst.append(dict(ids=ids, tw=tw, bm=bm, routing=routing, C=C, y=y, gemm=gemm, touched=touched,
+                            gemm_bytes=gemm_bytes, call_bytes=call_bytes))
+        calls[M] = lst
+    flush_src = torch.ones(1 << 29, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    torch.cuda.synchronize()
+    timed = []  # (M, events, call)
+    clock.region = "decode_cold"
+    with torch.cuda.stream(stream):
+        for step in range(n_steps):
+            # a spin of a few ms at the head of each step, so that the host has
+            # queued all of the step's launches before the first one runs: no
+            # host-side gap can fall inside an event pair
+            torch.cuda._sleep(SPIN_CYCLES)
+            for M in DECODE_MS:
+                c = calls[M][step]
+                flush_dst.copy_(flush_src)
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                ev[0].record(stream)
+                moe.moe_align(c["ids"], E, c["bm"], out=c["routing"], stream=stream)
+                ev[1].record(stream)
+                c["gemm"]()
+                ev[2].record(stream)
+                moe.moe_combine(c["C"], c["tw"], k, out=c["y"], stream=stream)
+                ev[3].record(stream)
+                if step >= args.warmup:
+                    timed.append((M, ev, c))
+            stream.synchronize()
+    torch.cuda.synchronize()
+    clock.region = None
+    per_m = {M: {"call": [], "gemm": [], "align": [], "combine": [], "touched": []} for M in DECODE_MS}
+    tot_bytes = tot_us = gemm_bytes = gemm_us = 0.0
+    for M, ev, c in timed:
+        call = ev[0].elapsed_time(ev[3]) * 1e3
+        g = ev[1].elapsed_time(ev[2]) * 1e3
+        d = per_m[M]
+        d["call"].append(call)
+        d["gemm"].append(g)
+        d["align"].append(ev[0].elapsed_time(ev[1]) * 1e3)
+        d["combine"].append(ev[2].elapsed_time(ev[3]) * 1e3)
+        d["touched"].append(c["touched"])
+        tot_bytes += c["call_bytes"]
+        tot_us += call
+        gemm_bytes += c["gemm_bytes"]
+        gemm_us += g
+    out = {}
+    for M in DECODE_MS:
+        d = per_m[M]
+        gb = [c["gemm_bytes"] for (m, _, c) in timed if m == M]
+        out[str(M)] = {"gemm_us": stats(d["gemm"]), "call_us": stats(d["call"]), "align_us": stats(d["align"]),
+                       "combine_us": stats(d["combine"]),
+                       "gemm_hbm_frac_median": round(float(np.median(np.array(gb) / np.array(d["gemm"]) / 1e3))
+                                                     / PEAK_HBM_GBS, 4),
+                       "touched_experts_mean": round(float(np.mean(d["touched"])), 1)}
+    del calls, flush_src, flush_dst, w
+    torch.cuda.empty_cache()
+    return {"value": tot_bytes / (tot_us * 1e-6) / 1e9, "ms_per_step": tot_us / args.steps / 1e3,
+            "gemm_GBps": gemm_bytes / (gemm_us * 1e-6) / 1e9, "gemm_avg_us": gemm_us / len(timed),
+            "per_m": out, "calls": len(timed)}
+
+
+def measure(wl, torch, stream, args, nv, clock, region):
+    """Warm measurement of a workload: K graph-replayed steps (W warmup), then
+    the dominant kernel's launch durations from HIP events on its stream, one
+    event pair per launch, launched back to back on resident inputs."""
+    graphs = []
+    with torch.cuda.stream(stream):
+        for v in range(nv):
+            wl.step(v)  # eager run first (warms caches of the library and allocator)
+        torch.cuda.synchronize()
+        for v in range(nv):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                wl.step(v)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % nv].replay()
+    torch.cuda.synchronize()
+    clock.region = region
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % nv].replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    step_bytes = sum(wl.step_bytes(i % nv) for i in range(args.steps))
+    step_flops = sum(wl.step_flops(i % nv) for i in range(args.steps))
+    per_call, durs, units_all = {}, [], []
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            v = i % nv
+            launches = wl.dominant_launches(v)
+            for j, (fn, units) in enumerate(launches):
+                fn()  # queue ahead so the timed launches run back to back
+                for _ in range(args.launch_reps):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    fn()
+                    b.record(stream)
+                    durs.append((a, b, units, j, v))
+    torch.cuda.synchronize()
+    clock.region = None
+    dom_ms, dom_units = 0.0, 0.0
+    us = []
+    variants = []
+    for a, b, units, j, v in durs:
+        variants.append(v)
+        t = a.elapsed_time(b)
+        dom_ms += t
+        dom_units += units
+        us.append(t * 1e3)
+        per_call.setdefault(j, []).append(t * 1e3)
+    del graphs
+    return dict(dt=dt, step_bytes=step_bytes, step_flops=step_flops, dom_ms=dom_ms, dom_units=dom_units,
+                launch_us=us, per_call=per_call, n=len(us), launch_variant=variants)
+
+
+def roofline_of(wl, m):
+    if wl.bound == "hbm":
+        achieved = m["dom_units"] / (m["dom_ms"] * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved = m["dom_units"] / (m["dom_ms"] * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    return {"bound": wl.bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(wl.name, None),
+            "kernel": wl.dominant, "avg_launch_us": round(m["dom_ms"] / m["n"] * 1e3, 3),
+            "launch_us": stats(m["launch_us"])}
+
+
+LARGE_M = ("w4a16", "mxfp8", "wgrad")
+
+
+def large_m_block(torch, dev, stream, args, clock):
+    """The large-M half of the metric: per workload, the dominant kernel's
+    TFLOP/s and fractions of the bf16 MFMA peak and of HBM bandwidth (sums
+    of algorithmic flops and bytes over sums of launch times; the launch
+    times' median, p10 and p90 beside them) and the whole step's TFLOP/s."""
+    out = {}
+    for name in LARGE_M:
+        wl = WORKLOADS[name](torch, dev, args.variants)
+        nv = len(wl.calls) if name == "w4a16" else 1
+        m = measure(wl, torch, stream, args, nv, clock, f"large_m_{name}")
+        roof = roofline_of(wl, m)
+        flops = sum(wl.dominant_flops_bytes(v)[0] for v in m["launch_variant"])
+        nbytes = sum(wl.dominant_flops_bytes(v)[1] for v in m["launch_variant"])
+        secs = m["dom_ms"] * 1e-3
+        out[name] = {
+            "workload": CONFIG_NAMES[name], "kernel": wl.dominant, "launch_us": roof["launch_us"],
+            "tflops": round(flops / secs / 1e12, 1),
+            "bf16_peak_frac": round(flops / secs / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "hbm_GBps": round(nbytes / secs / 1e9, 1),
+            "hbm_frac": round(nbytes / secs / 1e9 / PEAK_HBM_GBS, 4),
+            "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+            "step_tflops": round(m["step_flops"] / m["dt"] / 1e12, 1),
+            "ms_per_step": round(m["dt"] / args.steps * 1e3, 4),
+            "clock": clock.summary(f"large_m_{name}"),
+        }
+        out[name].update(wl.extra(None))
+        del wl, m
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.counters_from:
@@ -825,104 +1125,101 @@ def main():
     if args.layout != "auto":
         for name in LAYOUT:
             LAYOUT[name] = args.layout
-    wl = WORKLOADS[args.workload](torch, dev, args.variants)
-    nv = len(getattr(wl, "calls", [None])) if args.workload in ("decode", "nemotron", "w4a16") else 1
+    clock = ClockSampler(torch)
     stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-
-    # capture one graph per routing variant (the step's launches only)
-    graphs = []
-    with torch.cuda.stream(stream):
-        for v in range(nv):
-            wl.step(v)  # eager run first (warms caches of the library and allocator)
-        torch.cuda.synchronize()
-        for v in range(nv):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                wl.step(v)
-            graphs.append(g)
-    torch.cuda.synchronize()
-
-    for i in range(args.warmup):
-        graphs[i % nv].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % nv].replay()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_per_step = dt / args.steps * 1e3
-    step_bytes = sum(wl.step_bytes(i % nv) for i in range(args.steps))
-    step_flops = sum(wl.step_flops(i % nv) for i in range(args.steps))
-
-    # dominant kernel: HIP events on the launch stream around a run of
-    # back-to-back launches of it (same inputs; each launch overwrites its
-    # output), so the average excludes host-side launch cost
-    n_dom = 0
-    dom_units, dom_time_ms = 0.0, 0.0
-    per_call = {}
-    reps = args.launch_reps
-    with torch.cuda.stream(stream):
-        for i in range(args.steps):
-            v = i % nv
-            for j, (fn, units) in enumerate(wl.dominant_launches(v)):
-                fn()  # queue ahead so the timed launches run back to back
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(reps):
-                    fn()
-                b.record(stream)
-                b.synchronize()
-                t = a.elapsed_time(b) / reps
-                dom_time_ms += t
-                dom_units += units
-                n_dom += 1
-                per_call.setdefault(j, []).append(t * 1e3)
-    torch.cuda.synchronize()
-    avg_launch_us = dom_time_ms / n_dom * 1e3
-    if wl.bound == "hbm":
-        achieved = dom_units / (dom_time_ms * 1e-3) / 1e9
-        peak, unit = PEAK_HBM_GBS, "GB/s"
+    if args.workload == "decode":
+        line = decode_main(torch, moe, dev, stream, args, clock)
     else:
-        achieved = dom_units / (dom_time_ms * 1e-3) / 1e12
-        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
-    traffic = load_traffic(wl.name, None)
-    roofline = {"bound": wl.bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": wl.dominant, "avg_launch_us": round(avg_launch_us, 3)}
+        line = workload_main(torch, dev, stream, args, clock)
+    clock.close()
+    print(json.dumps(line), flush=True)
 
-    if args.workload in ("decode", "nemotron", "copy"):
-        value = step_bytes / dt / 1e9
+
+def decode_main(torch, moe, dev, stream, args, clock):
+    """The headline: the decode workload with a cold cache (value, roofline),
+    its warm figures under "warm", and the large-M block."""
+    cold = decode_cold(torch, moe, dev, stream, args, clock) if args.phase in ("cold", "both") else None
+    warm = None
+    wl = None
+    if args.phase in ("warm", "both") or cold is None:
+        wl = Decode(torch, dev, args.variants)
+        nv = len(wl.calls)
+        m = measure(wl, torch, stream, args, nv, clock, "decode_warm")
+        roof = roofline_of(wl, m)
+        per_call = [sum(v) / len(v) for _, v in sorted(m["per_call"].items())]
+        warm = {"value": round(m["step_bytes"] / m["dt"] / 1e9, 3), "unit": "GB/s",
+                "ms_per_step": round(m["dt"] / args.steps * 1e3, 4), "routing_variants": nv,
+                "roofline": roof, "launch_reps": args.launch_reps, "clock": clock.summary("decode_warm")}
+        warm.update(wl.extra(per_call))
+    if cold is not None:
+        roof_cold = {"bound": "hbm", "achieved": round(cold["gemm_GBps"], 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(cold["gemm_GBps"] / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode", None),
+                     "kernel": "moe_decode_kernel", "avg_launch_us": round(cold["gemm_avg_us"], 3),
+                     "cache": "cold (1 GiB copy between calls)"}
+        value, ms = cold["value"], cold["ms_per_step"]
+        roofline = roof_cold
+    else:
+        value, ms, roofline = warm["value"], warm["ms_per_step"], warm["roofline"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        if wl is None:
+            wl = Decode(torch, dev, 1)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+    line = {"metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": CONFIG_NAMES["decode"],
+                       "cache": "cold: every call on its own routing, after a 1 GiB copy that evicts the MALL",
+                       "weight_layout": LAYOUT["decode"], "parallelism": "single GPU"},
+            "roofline": roofline, "cpu_baseline": cpu}
+    if cold is not None:
+        line["hbm_frac_step"] = round(value / PEAK_HBM_GBS, 4)
+        line["cold"] = {"per_m": cold["per_m"], "calls": cold["calls"], "clock": clock.summary("decode_cold"),
+                        "ms_per_step_note": "device time of the step's launches (events); the copies that "
+                                            "evict the cache between calls are outside it"}
+    if warm is not None:
+        line["warm"] = warm
+    if not args.no_large_m and args.phase == "both":
+        del wl
+        torch.cuda.empty_cache()
+        line["large_m"] = large_m_block(torch, dev, stream, args, clock)
+    return line
+
+
+def workload_main(torch, dev, stream, args, clock):
+    """One workload chosen with --workload (warm, graph-replayed steps)."""
+    wl = WORKLOADS[args.workload](torch, dev, args.variants)
+    nv = len(getattr(wl, "calls", [None])) if args.workload in ("nemotron", "w4a16") else 1
+    m = measure(wl, torch, stream, args, nv, clock, "workload")
+    roofline = roofline_of(wl, m)
+    dt = m["dt"]
+    if args.workload in ("nemotron", "copy"):
+        value = m["step_bytes"] / dt / 1e9
         unit_v = "GB/s"
-        extra = wl.extra([sum(v) / len(v) for _, v in sorted(per_call.items())])
+        extra = wl.extra([sum(v) / len(v) for _, v in sorted(m["per_call"].items())])
         extra["hbm_frac_step"] = round(value / PEAK_HBM_GBS, 4)
         dtype = "u8" if args.workload == "copy" else "bf16"
     else:
-        value = step_flops / dt / 1e12
+        value = m["step_flops"] / dt / 1e12
         unit_v = "TFLOP/s"
         extra = wl.extra(None)
         extra["mfma_frac_step_bf16"] = round(value / PEAK_BF16_TFLOPS, 4)
         if args.workload in ("mxfp8a", "pertoken"):
             extra["mfma_frac_step_fp8"] = round(value / (2 * PEAK_BF16_TFLOPS), 4)
-        extra["hbm_GBps_step"] = round(step_bytes / dt / 1e9, 1)
+        extra["hbm_GBps_step"] = round(m["step_bytes"] / dt / 1e9, 1)
         dtype = {"w4a16": "bf16 x e2m1 (bf16 MFMA)", "mxfp8": "bf16 x e4m3 (bf16 MFMA)",
                  "mxfp8a": "e4m3 x e4m3, E8M0 per 32 (scaled fp8 MFMA)",
                  "pertoken": "e4m3 x e4m3, fp32 per-row and per-expert scales (fp8 MFMA)",
                  "wgrad": "bf16 (bf16 MFMA, fp32 out)"}[args.workload]
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
-
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seconds)
     line = {"metric": METRIC, "value": round(value, 3), "unit": unit_v, "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "warmup": args.warmup, "ms_per_step": round(dt / args.steps * 1e3, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
             "config": {"workload": CONFIG_NAMES[args.workload], "routing_variants": nv,
                        "weight_layout": LAYOUT.get(args.workload, "n/a"), "parallelism": "single GPU"},
-            "roofline": roofline, "cpu_baseline": cpu}
+            "roofline": roofline, "cpu_baseline": cpu, "clock": clock.summary("workload")}
     line.update(extra)
-    print(json.dumps(line), flush=True)
+    return line
 
 
 if __name__ == "__main__":
