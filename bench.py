@@ -10,9 +10,11 @@ GEMM -> moe_combine.
 
 Headline (`value`, `roofline`): the decode step with a cold cache. Every call
 runs on a routing and activations drawn for it alone, after a 1 GiB device
-copy that evicts the previous call's weights from the 256 MB MALL and the L2s;
-HIP events on the launch stream bracket each call and its GEMM launch (the
-copy is outside), and a GPU spin at the head of each step lets the host queue
+copy that evicts the previous call's weights from the 256 MB MALL and the L2s,
+and its inputs (activations, routing) are then written by small copies as
+their producers would, so only the weights are cold; HIP events on the launch
+stream bracket each call and its GEMM launch (the copies are outside), and a
+GPU spin at the head of each step lets the host queue
 the whole step first. `value` = the timed calls' algorithmic HBM bytes over
 their summed event time (GB/s); `roofline` = the decode GEMM's algorithmic
 bytes over its summed launch time; `cold.per_m` gives median / p10 / p90 per
@@ -34,6 +36,7 @@ workload, timed on this host.
 """
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -72,6 +75,7 @@ def parse():
                     help="decode workload: cold-cache calls (the headline), warm graph replays, or both "
                          "(both also runs the large-M block)")
     ap.add_argument("--no-large-m", action="store_true", help="decode workload: skip the large-M block")
+
     return ap.parse_args()
 
 
@@ -912,17 +916,34 @@ class ClockSampler:
 
 
 DECODE_MS = (1, 7, 14, 21, 28)
-SPIN_CYCLES = 10_000_000  # torch.cuda._sleep cycles (a few ms) ahead of each cold decode step
+SPIN_MS = 20.0  # GPU spin ahead of each cold decode step
+
+
+def spin_cycles(torch, stream, ms):
+    """torch.cuda._sleep cycles that spin the GPU for about `ms` (measured)."""
+    n = 1_000_000
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(n)  # first launch outside the measurement
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        torch.cuda._sleep(n)
+        b.record(stream)
+    b.synchronize()
+    per_ms = n / max(a.elapsed_time(b), 1e-3)
+    return int(per_ms * ms)
 
 
 def decode_cold(torch, moe, dev, stream, args, clock):
     """The decode workload with a cold cache: every call (align -> decode GEMM
     -> combine for one M) runs on a routing and activations drawn for it
     alone, after a 1 GiB device copy (512 MiB read, 512 MiB written) that
-    evicts the previous call's weights from the 256 MB MALL and the L2s. The
-    copy runs outside the timed span: HIP events on the launch stream bracket
-    the call and, inside it, the GEMM launch. W warmup steps, then K timed
-    steps; a step is one call for each M in 1, 7, 14, 21, 28."""
+    evicts the previous call's weights from the 256 MB MALL and the L2s; the
+    call's activations, ids and routing weights are then written by small
+    copies, as the kernels that produce them would, so only the expert
+    weights are cold. The copies run outside the timed span: HIP events on
+    the launch stream bracket the call and, inside it, the GEMM launch. W
+    warmup steps, then K timed steps; a step is one call for each M in 1, 7,
+    14, 21, 28."""
     import numpy as np
     import synth
     E, N, K, k = 128, 1856, 2048, 6
@@ -933,34 +954,42 @@ def decode_cold(torch, moe, dev, stream, args, clock):
         bm = moe.moe_gemm_block_m("bf16", M)
         lst = []
         for r in range(n_steps):
-            x = synth.bf16_normal((M, K), 1.0, 1002, f"cold-x{M}c{r}", dev)
-            ids, tw = synth.softmax_topk_routing(M, E, k, 1002, f"cold-route{M}c{r}", dev)
+            x_src = synth.bf16_normal((M, K), 1.0, 1002, f"cold-x{M}c{r}", dev)
+            ids_src, tw_src = synth.softmax_topk_routing(M, E, k, 1002, f"cold-route{M}c{r}", dev)
+            x, ids, tw = torch.empty_like(x_src), torch.empty_like(ids_src), torch.empty_like(tw_src)
             routing = _routing_buffers(torch, M, k, E, bm, dev)
             C = torch.empty((M * k, N), dtype=torch.bfloat16, device=dev)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             gemm, _ = moe.moe_grouped_gemm_prepare(x, w, "bf16", routing, M, k, E, k, out=C, stream=stream)
-            touched = len(np.unique(ids.cpu().numpy()))
+            touched = len(np.unique(ids_src.cpu().numpy()))
             S, mb = M * k, routing[1].numel()
             gemm_bytes = touched * N * K * 2 + M * K * 2 + S * N * 2
             call_bytes = gemm_bytes + (S * 4 + mb * bm * 4 + mb * 4 + 4) + (S * N * 2 + M * N * 2 + S * 4)
-            lst.append(dict(ids=ids, tw=tw, bm=bm, routing=routing, C=C, y=y, gemm=gemm, touched=touched,
+            lst.append(dict(ids=ids, tw=tw, x=x, srcs=((x, x_src), (ids, ids_src), (tw, tw_src)),
+                            bm=bm, routing=routing, C=C, y=y, gemm=gemm, touched=touched,
                             gemm_bytes=gemm_bytes, call_bytes=call_bytes))
         calls[M] = lst
     flush_src = torch.ones(1 << 29, dtype=torch.uint8, device=dev)
     flush_dst = torch.empty_like(flush_src)
+    spin = spin_cycles(torch, stream, SPIN_MS)
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in DECODE_MS] for _ in range(n_steps)]
     torch.cuda.synchronize()
     timed = []  # (M, events, call)
     clock.region = "decode_cold"
+    gc.collect()
+    gc.disable()  # no collector pause inside a step (the spin below covers the host's queueing of it)
     with torch.cuda.stream(stream):
         for step in range(n_steps):
-            # a spin of a few ms at the head of each step, so that the host has
-            # queued all of the step's launches before the first one runs: no
-            # host-side gap can fall inside an event pair
-            torch.cuda._sleep(SPIN_CYCLES)
-            for M in DECODE_MS:
+            # a spin at the head of each step, so that the host has queued all
+            # of the step's launches before the first one runs: no host-side
+            # gap falls inside an event pair
+            torch.cuda._sleep(spin)
+            for i, M in enumerate(DECODE_MS):
                 c = calls[M][step]
                 flush_dst.copy_(flush_src)
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                for dst, src in c["srcs"]:  # the call's inputs, written just before it as their producer would
+                    dst.copy_(src)
+                ev = events[step][i]
                 ev[0].record(stream)
                 moe.moe_align(c["ids"], E, c["bm"], out=c["routing"], stream=stream)
                 ev[1].record(stream)
@@ -971,6 +1000,7 @@ def decode_cold(torch, moe, dev, stream, args, clock):
                 if step >= args.warmup:
                     timed.append((M, ev, c))
             stream.synchronize()
+    gc.enable()
     torch.cuda.synchronize()
     clock.region = None
     per_m = {M: {"call": [], "gemm": [], "align": [], "combine": [], "touched": []} for M in DECODE_MS}
@@ -992,7 +1022,8 @@ def decode_cold(torch, moe, dev, stream, args, clock):
     for M in DECODE_MS:
         d = per_m[M]
         gb = [c["gemm_bytes"] for (m, _, c) in timed if m == M]
-        out[str(M)] = {"gemm_us": stats(d["gemm"]), "call_us": stats(d["call"]), "align_us": stats(d["align"]),
+        out[str(M)] = {"gemm_us": stats(d["gemm"]), "call_us": stats(d["call"]),
+                       "align_us": stats(d["align"]),
                        "combine_us": stats(d["combine"]),
                        "gemm_hbm_frac_median": round(float(np.median(np.array(gb) / np.array(d["gemm"]) / 1e3))
                                                      / PEAK_HBM_GBS, 4),
