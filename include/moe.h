@@ -238,6 +238,40 @@ typedef struct {
 moe_status moe_grouped_gemm(const moe_gemm_args* args, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The decode MoE step in one launch: routing, the routed grouped GEMM and the
+ * top-k combine for a few tokens ([TA] What it does: the M <= 32 bucket
+ * dominates the decode step, where the launches around the GEMM are a fixed
+ * cost of every call; "Follow-up on this table": moe_align_block_size and the
+ * fused MoE GEMM on the tiny-M path). For token t < T and slot s = t*top_k + j
+ * routed to expert e = topk_ids[s] (device, int32 [T][top_k]):
+ *   C[s][n] = bf16( epilogue( A[t] . W_hat[e][n] + bias[e][n] ) )
+ *   y[t][n] = bf16( sum_{j < top_k, ascending} topk_w[s] * C[s][n] )   (fp32)
+ * with the arithmetic of moe_align -> moe_grouped_gemm (decode variant) ->
+ * moe_combine, so C and y are bit-identical to those three calls. A slot
+ * whose id lies outside [0, E) contributes 0 to y (and its C row is not
+ * written).
+ * args describes A (bf16 token rows: a_dtype MOE_BF16, a_row_div = top_k),
+ * the weights, scales and bias exactly as for moe_grouped_gemm; epilogue
+ * MOE_EPILOGUE_NONE or MOE_EPILOGUE_RELU2. args->c (device, bf16 [S][n], row
+ * stride c_ld >= n) receives C when not NULL; no other memory is written
+ * besides y. The routing fields (sorted_token_ids, expert_ids,
+ * num_tokens_post_pad, block_m, max_blocks) are not read. topk_w (device)
+ * fp32 [T][top_k]; y (device) bf16 [T][n], row stride y_ld >= n; every row
+ * t < T is written.
+ * Limits (moe_decode_layer_fits): T <= 32, T * top_k <= 256, E <= 1024,
+ * k <= 4096 and T * k <= 65536 (the activations of all tokens are held on
+ * chip). Outside them, with SwiGLU or with MOE_E4M3 activations:
+ * MOE_ERR_UNSUPPORTED. Other requirements as for moe_grouped_gemm.
+ * No workspace.
+ * ---------------------------------------------------------------------- */
+moe_status moe_decode_layer(const moe_gemm_args* args, const int32_t* topk_ids, const float* topk_w,
+                            void* y, int64_t y_ld, moe_stream_t stream);
+
+/* 1 when moe_decode_layer takes T tokens of top_k slots over num_experts
+ * experts with contraction length k (the limits above), else 0. */
+int32_t moe_decode_layer_fits(int64_t num_tokens, int32_t top_k, int32_t num_experts, int64_t k);
+
+/* ------------------------------------------------------------------------
  * Weight repacking (a one-time step at weight-load time, outside the
  * method: it moves codes and scale bytes, computes nothing).
  * Copies E experts' codes and scales from MOE_LAYOUT_ROWS (w, w_scale with

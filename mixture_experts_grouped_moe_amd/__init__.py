@@ -22,7 +22,8 @@ __all__ = [
     "moe_quantize_mxfp8", "moe_block_mapping", "moe_grouped_gemm_per_token",
     "moe_grouped_gemm_per_token_prepare",
     "moe_pack_weights", "moe_packed_sizes", "PackedWeights", "MOE_LAYOUT_ROWS", "MOE_LAYOUT_KBLOCK",
-    "moe_w4a16_layer", "moe_relu2_layer",
+    "moe_w4a16_layer", "moe_relu2_layer", "moe_decode_layer", "moe_decode_layer_prepare",
+    "moe_decode_layer_fits",
     "LIB_PATH",
 ]
 
@@ -103,6 +104,8 @@ def _load():
         "moe_packed_sizes": (i32, [i32, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
         "moe_block_mapping": (i32, [vp, i32, i64, i32, vp, vp, vp, i64, vp, vp]),
         "moe_grouped_gemm_per_token": (i32, [ctypes.POINTER(MoePerTokenArgs), vp]),
+        "moe_decode_layer": (i32, [ctypes.POINTER(MoeGemmArgs), vp, vp, vp, i64, vp]),
+        "moe_decode_layer_fits": (i32, [i64, i32, i32, i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -266,6 +269,41 @@ def moe_align(topk_ids, num_experts, block_m, num_tokens=None, out=None, stream=
     return sorted_ids, expert_ids, post_pad
 
 
+def _weight_args(g, w, w_dtype, w_scale, bias, K):
+    """Checks the weights, scales and bias of a routed GEMM and fills their
+    fields of the MoeGemmArgs g. Returns (E, N, codes, scales)."""
+    wd = _W_DTYPES[w_dtype]
+    packed = isinstance(w, PackedWeights)
+    if packed:
+        if w.w_dtype != w_dtype or w.k != K:
+            raise ValueError("packed weights do not match w_dtype / a's K")
+        if w_scale is not None:
+            raise ValueError("packed weights carry their own scales")
+        E, N = w.num_experts, w.n
+        w_t, w_scale = w.codes, w.scales
+        _need(w_t, "w.codes", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 4)
+    else:
+        w_t = w
+        _need(w_t, "w", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 3)
+        E, N = w_t.shape[0], w_t.shape[1]
+        if w_t.shape[2] * (2 if w_dtype == "e2m1x2" else 1) != K:
+            raise ValueError("w's K does not match a's")
+        if w_dtype != "bf16":
+            _need(w_scale, "w_scale", torch.uint8, 3)
+            if tuple(w_scale.shape) != (E, N, K // 32):
+                raise ValueError(f"w_scale must be [E, N, K/32] = {(E, N, K // 32)}")
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or not bias.is_cuda or tuple(bias.shape) != (E, N):
+            raise TypeError("bias must be a bf16 [E, N] device tensor")
+    g.w_dtype, g.w, g.w_stride_e, g.w_ld = wd, w_t.data_ptr(), w_t.stride(0), w_t.stride(1)
+    g.w_layout = MOE_LAYOUT_KBLOCK if packed else MOE_LAYOUT_ROWS
+    if w_scale is not None:
+        g.w_scale, g.w_scale_stride_e, g.w_scale_ld = w_scale.data_ptr(), w_scale.stride(0), w_scale.stride(1)
+    if bias is not None:
+        g.bias, g.bias_stride_e, g.bias_stride_n = bias.data_ptr(), bias.stride(0), bias.stride(1)
+    return E, N, w_t, w_scale
+
+
 def moe_grouped_gemm(a, w, w_dtype, routing, num_tokens, top_k, num_experts, a_row_div,
                      w_scale=None, bias=None, epilogue="none", out=None, block_m=None,
                      stream=None, a_scale=None):
@@ -293,7 +331,6 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     captured here, with the arguments checked and marshalled once (for tight
     loops and graph capture).
     """
-    wd = _W_DTYPES[w_dtype]
     a_f8 = isinstance(a, torch.Tensor) and a.dtype == torch.uint8
     if a_f8:
         _need(a, "a", torch.uint8, 2)
@@ -309,30 +346,10 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     a_dt = MOE_E4M3 if a_f8 else MOE_BF16
     K = a.shape[1]
     S = int(num_tokens) * int(top_k)
-    packed = isinstance(w, PackedWeights)
-    if packed:
-        if w.w_dtype != w_dtype or w.k != K:
-            raise ValueError("packed weights do not match w_dtype / a's K")
-        if w_scale is not None:
-            raise ValueError("packed weights carry their own scales")
-        E, N = w.num_experts, w.n
-        w_t, w_scale = w.codes, w.scales
-        _need(w_t, "w.codes", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 4)
-    else:
-        w_t = w
-        _need(w_t, "w", torch.bfloat16 if w_dtype == "bf16" else torch.uint8, 3)
-        E, N = w_t.shape[0], w_t.shape[1]
-        if w_t.shape[2] * (2 if w_dtype == "e2m1x2" else 1) != K:
-            raise ValueError("w's K does not match a's")
-        if w_dtype != "bf16":
-            _need(w_scale, "w_scale", torch.uint8, 3)
-            if tuple(w_scale.shape) != (E, N, K // 32):
-                raise ValueError(f"w_scale must be [E, N, K/32] = {(E, N, K // 32)}")
+    g = MoeGemmArgs()
+    E, N, w_t, w_scale = _weight_args(g, w, w_dtype, w_scale, bias, K)
     if a.shape[0] * int(a_row_div) < S:
         raise ValueError("a has too few rows for num_tokens * top_k slots")
-    if bias is not None:
-        if bias.dtype != torch.bfloat16 or not bias.is_cuda or tuple(bias.shape) != (E, N):
-            raise TypeError("bias must be a bf16 [E, N] device tensor")
     ep = _EPILOGUES[epilogue]
     out_w = N // 2 if ep == 1 else N
     if out is None:
@@ -344,18 +361,11 @@ def moe_grouped_gemm_prepare(a, w, w_dtype, routing, num_tokens, top_k, num_expe
     bm = moe_gemm_block_m(w_dtype, num_tokens, a_dt) if block_m is None else block_m
     if sorted_ids.numel() < expert_ids.numel() * bm:
         raise ValueError("routing arrays do not match block_m")
-    g = MoeGemmArgs()
     g.num_tokens, g.top_k, g.num_experts = int(num_tokens), int(top_k), int(num_experts)
     g.n, g.k = N, K
     g.a_dtype, g.a_row_div, g.a, g.a_ld = a_dt, int(a_row_div), a.data_ptr(), a.stride(0)
     if a_f8:
         g.a_scale, g.a_scale_ld = a_scale.data_ptr(), a_scale.stride(0)
-    g.w_dtype, g.w, g.w_stride_e, g.w_ld = wd, w_t.data_ptr(), w_t.stride(0), w_t.stride(1)
-    g.w_layout = MOE_LAYOUT_KBLOCK if packed else MOE_LAYOUT_ROWS
-    if w_scale is not None:
-        g.w_scale, g.w_scale_stride_e, g.w_scale_ld = w_scale.data_ptr(), w_scale.stride(0), w_scale.stride(1)
-    if bias is not None:
-        g.bias, g.bias_stride_e, g.bias_stride_n = bias.data_ptr(), bias.stride(0), bias.stride(1)
     g.epilogue, g.c, g.c_ld = ep, out.data_ptr(), out.stride(0)
     g.sorted_token_ids, g.expert_ids = sorted_ids.data_ptr(), expert_ids.data_ptr()
     g.num_tokens_post_pad = post_pad.data_ptr()
@@ -484,6 +494,69 @@ def moe_combine(c, topk_w, top_k, num_tokens=None, out=None, stream=None):
     _check(lib.moe_combine(_ptr(c), c.stride(0), _ptr(topk_w), T, int(top_k), N,
                            _ptr(out), out.stride(0), _stream(stream)))
     return out
+
+
+def moe_decode_layer_fits(num_tokens, top_k, num_experts, k):
+    """True when moe_decode_layer takes this many tokens, slots, experts and K."""
+    return bool(lib.moe_decode_layer_fits(int(num_tokens), int(top_k), int(num_experts), int(k)))
+
+
+def moe_decode_layer(x, topk_ids, topk_w, w, w_dtype, w_scale=None, bias=None, epilogue="none", out=None,
+                     c_out=None, stream=None):
+    """See moe_decode_layer_prepare; this builds the call and runs it once."""
+    call, out = moe_decode_layer_prepare(x, topk_ids, topk_w, w, w_dtype, w_scale=w_scale, bias=bias,
+                                         epilogue=epilogue, out=out, c_out=c_out, stream=stream)
+    call()
+    return out
+
+
+def moe_decode_layer_prepare(x, topk_ids, topk_w, w, w_dtype, w_scale=None, bias=None, epilogue="none",
+                             out=None, c_out=None, stream=None):
+    """The decode MoE step in one launch: y[t] = sum_j topk_w[t, j] *
+    epilogue(x[t] . W_hat[topk_ids[t, j]]^T + bias), with the bits of
+    moe_align -> moe_grouped_gemm -> moe_combine.
+
+    x: bf16 [T, K] token rows (T <= 32); topk_ids int32 and topk_w fp32
+    [T, top_k] (contiguous); w, w_scale, bias as for moe_grouped_gemm;
+    epilogue "none" or "relu2". c_out (bf16 [T * top_k, N]), when given,
+    receives the expert outputs C. Returns (call, y) with y bf16 [T, N];
+    call() launches the layer on the stream captured here.
+    """
+    _need(x, "x", torch.bfloat16, 2)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    if not (topk_ids.is_contiguous() and topk_w.is_contiguous()):
+        raise ValueError("topk_ids and topk_w must be contiguous")
+    T, K = x.shape
+    k = topk_ids.shape[1]
+    if topk_ids.shape[0] != T or tuple(topk_w.shape) != (T, k):
+        raise ValueError("topk_ids and topk_w must be [T, top_k] for x's T rows")
+    g = MoeGemmArgs()
+    E, N, w_t, w_scale = _weight_args(g, w, w_dtype, w_scale, bias, K)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if out.shape[0] < T or out.shape[1] < N:
+        raise ValueError(f"out must be at least [{T}, {N}]")
+    if c_out is not None:
+        _need(c_out, "c_out", torch.bfloat16, 2)
+        if c_out.shape[0] < T * k or c_out.shape[1] < N:
+            raise ValueError(f"c_out must be at least [{T * k}, {N}]")
+        g.c, g.c_ld = c_out.data_ptr(), c_out.stride(0)
+    g.num_tokens, g.top_k, g.num_experts = T, k, E
+    g.n, g.k = N, K
+    g.a_dtype, g.a_row_div, g.a, g.a_ld = MOE_BF16, k, x.data_ptr(), x.stride(0)
+    g.epilogue = _EPILOGUES[epilogue]
+    st = _stream(stream)
+    ref = ctypes.byref(g)
+    ids_p, tw_p, y_p, y_ld = _ptr(topk_ids), _ptr(topk_w), _ptr(out), out.stride(0)
+    keep = (x, topk_ids, topk_w, w_t, w_scale, bias, out, c_out)  # the call holds its tensors alive
+
+    def call():
+        _check(lib.moe_decode_layer(ref, ids_p, tw_p, y_p, y_ld, st))
+        return keep[6]
+    call.args = g
+    return call, out
 
 
 def moe_quantize_mxfp8(x, out=None, out_scales=None, stream=None):

@@ -30,7 +30,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["api.cpp", "align.hip", "gemm.hip", "decode.hip", "combine.hip", "wgrad.hip", "pack.hip", "quant.hip", "gemm_f8.hip"]
+SOURCES = ["api.cpp", "align.hip", "gemm.hip", "decode.hip", "decode_layer.hip", "combine.hip", "wgrad.hip", "pack.hip",
+           "quant.hip", "gemm_f8.hip"]
 
 
 def _hipcc():

@@ -68,6 +68,51 @@ int64_t bucket(int64_t m) {
 
 bool valid_w_dtype(int32_t d) { return d == MOE_BF16 || d == MOE_E4M3 || d == MOE_E2M1X2; }
 
+// The weight, scale and bias arguments of a routed GEMM (everything the two
+// entry points that take moe_gemm_args share): layout, strides and the byte
+// geometry the kernels address them with.
+struct WeightGeom {
+  bool kblock;
+  int64_t elem_bytes;  // bytes per storage unit of the codes
+  int64_t blk_units;   // storage units per row per 64-element K block
+  int64_t nblk;        // 64-element K blocks
+  int64_t w_span;      // bytes of one expert's codes, ws_span of its scales
+  int64_t ws_span;
+};
+
+moe_status check_weights(const moe_gemm_args& a, WeightGeom* g) {
+  if (a.w_layout != MOE_LAYOUT_ROWS && a.w_layout != MOE_LAYOUT_KBLOCK)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown w_layout %d", a.w_layout);
+  const bool kblock = a.w_layout == MOE_LAYOUT_KBLOCK;
+  const int64_t w_elem_bytes = a.w_dtype == MOE_BF16 ? 2 : 1;
+  const int64_t blk_units = a.w_dtype == MOE_E2M1X2 ? 32 : 64;
+  const int64_t nblk = (a.k + 63) / 64;
+  if ((a.w_ld * w_elem_bytes) % 16 != 0 || (a.w_stride_e * w_elem_bytes) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld and w_stride_e must be multiples of 16 bytes");
+  if (!kblock) {
+    if (a.w_ld < a.k * blk_units / 64) return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a row");
+    if (a.w_stride_e < a.n * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < n * w_ld");
+  } else {
+    if (a.w_ld < a.n * blk_units) return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a K block of n rows");
+    if (a.w_stride_e < nblk * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < ceil(k/64) * w_ld");
+  }
+  if (a.w_dtype != MOE_BF16) {
+    if (a.w_scale == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale is null");
+    const bool ok = !kblock ? (a.w_scale_ld >= a.k / 32 && a.w_scale_stride_e >= a.n * a.w_scale_ld)
+                            : (a.w_scale_ld >= 2 * a.n && a.w_scale_stride_e >= nblk * a.w_scale_ld);
+    if (!ok) return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale strides too small");
+  }
+  if (a.bias != nullptr && (a.bias_stride_e < 0 || a.bias_stride_n < 0))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "negative bias stride");
+  g->kblock = kblock;
+  g->elem_bytes = w_elem_bytes;
+  g->blk_units = blk_units;
+  g->nblk = nblk;
+  g->w_span = (kblock ? nblk : a.n) * a.w_ld * w_elem_bytes;
+  g->ws_span = a.w_dtype == MOE_BF16 ? 0 : (kblock ? nblk : a.n) * a.w_scale_ld;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,29 +225,12 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "a_ld must be >= k and a multiple of %d", a_f8 ? 16 : 8);
   if (a_f8 && (a.a_scale == nullptr || a.a_scale_ld < a.k / 32))
     return fail(MOE_ERR_INVALID_ARGUMENT, "MXFP8 activations need a_scale with a_scale_ld >= k / 32");
-  if (a.w_layout != MOE_LAYOUT_ROWS && a.w_layout != MOE_LAYOUT_KBLOCK)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown w_layout %d", a.w_layout);
-  const bool kblock = a.w_layout == MOE_LAYOUT_KBLOCK;
-  const int64_t w_elem_bytes = a.w_dtype == MOE_BF16 ? 2 : 1;
-  const int64_t blk_units = a.w_dtype == MOE_E2M1X2 ? 32 : 64;  // units per row per 64-element K block
-  const int64_t nblk = (a.k + 63) / 64;
-  if ((a.w_ld * w_elem_bytes) % 16 != 0 || (a.w_stride_e * w_elem_bytes) % 16 != 0)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld and w_stride_e must be multiples of 16 bytes");
-  if (!kblock) {
-    if (a.w_ld < a.k * blk_units / 64) return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a row");
-    if (a.w_stride_e < a.n * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < n * w_ld");
-  } else {
-    if (a.w_ld < a.n * blk_units) return fail(MOE_ERR_INVALID_ARGUMENT, "w_ld must cover a K block of n rows");
-    if (a.w_stride_e < nblk * a.w_ld) return fail(MOE_ERR_INVALID_ARGUMENT, "w_stride_e < ceil(k/64) * w_ld");
-  }
-  if (a.w_dtype != MOE_BF16) {
-    if (a.w_scale == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale is null");
-    const bool ok = !kblock ? (a.w_scale_ld >= a.k / 32 && a.w_scale_stride_e >= a.n * a.w_scale_ld)
-                            : (a.w_scale_ld >= 2 * a.n && a.w_scale_stride_e >= nblk * a.w_scale_ld);
-    if (!ok) return fail(MOE_ERR_INVALID_ARGUMENT, "w_scale strides too small");
-  }
-  if (a.bias != nullptr && (a.bias_stride_e < 0 || a.bias_stride_n < 0))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "negative bias stride");
+  WeightGeom wg;
+  moe_status wst = check_weights(a, &wg);
+  if (wst != MOE_OK) return wst;
+  const bool kblock = wg.kblock;
+  const int64_t w_elem_bytes = wg.elem_bytes;
+  const int64_t blk_units = wg.blk_units;
   if (a.c_ld < out_w) return fail(MOE_ERR_INVALID_ARGUMENT, "c_ld must be >= the output width");
   const int32_t bm = moe_gemm_block_m(a.a_dtype, a.w_dtype, a.num_tokens);
   if (a.block_m != bm)
@@ -221,8 +249,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   // scales through 32-bit buffer offsets
   const int64_t a_rows = S > 0 ? (S - 1) / a.a_row_div + 1 : 0;
   constexpr int64_t kBufMax = (int64_t)0x80000000;
-  const int64_t w_span = (kblock ? nblk : a.n) * a.w_ld * w_elem_bytes;
-  const int64_t ws_span = a.w_dtype == MOE_BF16 ? 0 : (kblock ? nblk : a.n) * a.w_scale_ld;
+  const int64_t w_span = wg.w_span, ws_span = wg.ws_span;
   if (a_rows * a.a_ld * (a_f8 ? 1 : 2) >= kBufMax || w_span >= kBufMax || ws_span >= kBufMax ||
       (a_f8 && a_rows * a.a_scale_ld >= kBufMax))
     return fail(MOE_ERR_UNSUPPORTED, "A, its scales, one expert's weights or its scales span 2 GB or more");
@@ -270,6 +297,99 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   return hip_status(decode ? moe::launch_gemm_decode(p, a.w_dtype, swiglu, bias, (hipStream_t)stream)
                            : moe::launch_gemm_large(p, a.w_dtype, swiglu, bias, (hipStream_t)stream),
                     "moe_grouped_gemm launch");
+}
+
+int32_t moe_decode_layer_fits(int64_t num_tokens, int32_t top_k, int32_t num_experts, int64_t k) {
+  return num_tokens >= 0 && num_tokens <= kDecodeMaxTokens && top_k >= 1 &&
+         num_tokens * top_k <= moe::decode_layer_max_slots() && num_experts >= 1 &&
+         num_experts <= moe::decode_layer_max_experts() && k >= 32 && k % 32 == 0 &&
+         k <= moe::decode_layer_max_k() && num_tokens * k <= moe::decode_layer_max_act_elems();
+}
+
+moe_status moe_decode_layer(const moe_gemm_args* g, const int32_t* topk_ids, const float* topk_w, void* y,
+                            int64_t y_ld, moe_stream_t stream) {
+  if (g == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "args is null");
+  const moe_gemm_args& a = *g;
+  if (a.num_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (a.top_k < 1 || a.num_experts < a.top_k)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "need 1 <= top_k (%d) <= num_experts (%d)", a.top_k, a.num_experts);
+  if (a.a_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the decode layer takes bf16 activations");
+  if (!valid_w_dtype(a.w_dtype)) return fail(MOE_ERR_UNSUPPORTED, "w_dtype %d not supported", a.w_dtype);
+  if (a.n < 1 || a.n >= INT32_MAX) return fail(MOE_ERR_INVALID_ARGUMENT, "n out of range");
+  if (a.k < 32 || a.k % 32 != 0 || a.k >= INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "k (%lld) must be a positive multiple of 32", (long long)a.k);
+  if (a.epilogue == MOE_EPILOGUE_SWIGLU)
+    return fail(MOE_ERR_UNSUPPORTED, "the decode layer has no SwiGLU epilogue");
+  if (a.epilogue != MOE_EPILOGUE_NONE && a.epilogue != MOE_EPILOGUE_RELU2)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown epilogue %d", a.epilogue);
+  if (a.a_row_div != a.top_k) return fail(MOE_ERR_INVALID_ARGUMENT, "a_row_div must be top_k (A holds token rows)");
+  if (a.a_ld < a.k || a.a_ld % 8 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "a_ld must be >= k and a multiple of 8");
+  WeightGeom wg;
+  moe_status wst = check_weights(a, &wg);
+  if (wst != MOE_OK) return wst;
+  if (a.c != nullptr && a.c_ld < a.n) return fail(MOE_ERR_INVALID_ARGUMENT, "c_ld must be >= n");
+  if (y_ld < a.n) return fail(MOE_ERR_INVALID_ARGUMENT, "y_ld must be >= n");
+  if (!moe_decode_layer_fits(a.num_tokens, a.top_k, a.num_experts, a.k))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the decode layer takes num_tokens <= %lld, num_tokens * top_k <= %d, num_experts <= %d, "
+                "k <= %d and num_tokens * k <= %lld",
+                (long long)kDecodeMaxTokens, moe::decode_layer_max_slots(), moe::decode_layer_max_experts(),
+                moe::decode_layer_max_k(), (long long)moe::decode_layer_max_act_elems());
+  if (a.num_tokens > 0 &&
+      (a.a == nullptr || a.w == nullptr || topk_ids == nullptr || topk_w == nullptr || y == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (((uintptr_t)a.a | (uintptr_t)a.w) % 16 != 0 || ((uintptr_t)a.c | (uintptr_t)y) % 2 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "a and w must be 16-byte aligned, c and y 2-byte aligned");
+  // the kernel reads the token rows, each weight row's codes and scales and
+  // the bias through 32-bit buffer ranges
+  const int64_t x_bytes = a.num_tokens > 0 ? ((a.num_tokens - 1) * a.a_ld + a.k) * 2 : 0;
+  const int64_t w_row = wg.kblock ? wg.blk_units * wg.elem_bytes : a.w_ld * wg.elem_bytes;
+  const int64_t w_blk = wg.kblock ? a.w_ld * wg.elem_bytes : wg.blk_units * wg.elem_bytes;
+  const int64_t piece = 8 * wg.blk_units * wg.elem_bytes / 64;  // bytes of 8 codes
+  const int64_t w_rspan = ((a.k - 8) / 64) * w_blk + ((a.k - 8) % 64) * piece / 8 + piece;
+  const int64_t ws_row = wg.kblock ? 2 : a.w_scale_ld, ws_blk = wg.kblock ? a.w_scale_ld : 2;
+  const int64_t ws_rspan = a.w_dtype == MOE_BF16 ? 0 : ((a.k - 1) / 64) * ws_blk + ((a.k - 1) % 64) / 32 + 1;
+  const int64_t bias_bytes =
+      a.bias != nullptr ? ((a.num_experts - 1) * a.bias_stride_e + (a.n - 1) * a.bias_stride_n + 1) * 2 : 0;
+  constexpr int64_t kBufMax = (int64_t)0x80000000;
+  if (x_bytes >= kBufMax || w_rspan >= kBufMax || ws_rspan >= kBufMax || bias_bytes >= kBufMax)
+    return fail(MOE_ERR_UNSUPPORTED, "A, one weight row, its scales or the bias spans 2 GB or more");
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  if (a.num_tokens == 0) return ok();
+
+  moe::DecodeLayerParams p{};
+  p.x = static_cast<const uint16_t*>(a.a);
+  p.x_ld = a.a_ld;
+  p.topk_ids = topk_ids;
+  p.topk_w = topk_w;
+  p.w = static_cast<const uint8_t*>(a.w);
+  p.w_stride_e = a.w_stride_e * wg.elem_bytes;
+  p.w_row = w_row;
+  p.w_blk = w_blk;
+  p.ws = a.w_scale;
+  p.ws_stride_e = a.w_scale_stride_e;
+  p.ws_row = ws_row;
+  p.ws_blk = ws_blk;
+  p.bias = static_cast<const uint16_t*>(a.bias);
+  p.bias_se = a.bias_stride_e;
+  p.bias_sn = a.bias_stride_n;
+  p.c = static_cast<uint16_t*>(a.c);
+  p.c_ld = a.c_ld;
+  p.y = static_cast<uint16_t*>(y);
+  p.y_ld = y_ld;
+  p.S = (int32_t)(a.num_tokens * a.top_k);
+  p.top_k = a.top_k;
+  p.E = a.num_experts;
+  p.N = (int32_t)a.n;
+  p.K = (int32_t)a.k;
+  p.relu2 = a.epilogue == MOE_EPILOGUE_RELU2 ? 1 : 0;
+  p.x_bytes = (uint32_t)x_bytes;
+  p.w_rspan = (uint32_t)w_rspan;
+  p.ws_rspan = (uint32_t)ws_rspan;
+  p.bias_bytes = (uint32_t)bias_bytes;
+  return hip_status(moe::launch_decode_layer(p, a.w_dtype, a.bias != nullptr, (hipStream_t)stream),
+                    "moe_decode_layer launch");
 }
 
 moe_status moe_packed_sizes(int32_t w_dtype, int64_t n, int64_t k, int64_t* w_units, int64_t* scale_bytes) {

@@ -1,0 +1,197 @@
+"""The fused decode layer (moe_decode_layer: routing, the decode grouped GEMM
+and the top-k combine in one launch) on the GPU. Its y and its expert outputs
+C equal, bit for bit, those of moe_align -> moe_grouped_gemm -> moe_combine
+on the same inputs, and both match the float64 oracle: every weight encoding,
+with and without bias and the relu2 epilogue, K short of a pass and across
+two passes, N not a multiple of 8, skewed and repeated routing, ids outside
+[0, E), and the launch's limits (256 slots, 1024 experts, K = 4096,
+M x K = 65536)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import assert_parity, bf16_to_f64, host, need_gpu, to_dev
+from oracle import gemm as ogemm
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _moe():
+    import mixture_experts_grouped_moe_amd as moe
+    return moe
+
+
+def _nan(rows, cols):
+    return torch.full((rows, cols), float("nan"), dtype=torch.bfloat16, device="cuda")
+
+
+def _unfused(dd, T, k, E, N, wd, epilogue):
+    moe = _moe()
+    routing = moe.moe_align(dd["ids"], E, moe.moe_gemm_block_m(wd, T))
+    C = _nan(T * k, N)
+    moe.moe_grouped_gemm(dd["x"], dd["w"], wd, routing, T, k, E, k, w_scale=dd["w_scale"], bias=dd["bias"],
+                         epilogue=epilogue, out=C)
+    y = moe.moe_combine(C, dd["topk_w"], k)
+    return C, y
+
+
+def _fused(dd, T, k, N, wd, epilogue):
+    moe = _moe()
+    C = _nan(T * k, N)
+    y = moe.moe_decode_layer(dd["x"], dd["ids"], dd["topk_w"], dd["w"], wd, w_scale=dd["w_scale"],
+                             bias=dd["bias"], epilogue=epilogue, c_out=C)
+    return C, y
+
+
+def _oracle(d, T, k, E, wd, epilogue):
+    h = host(d)
+    C, routed = ogemm.grouped_gemm(h["x"], k, h["w"], wd, h["w_scale"], h["ids"], E, bias=h["bias"],
+                                   epilogue=epilogue)
+    return C, routed, ogemm.combine(C, h["topk_w"], k)
+
+
+def _same_bits(a, b, what):
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), what
+
+
+CASES = [
+    # T, k, E, N, K, w_dtype, bias, epilogue
+    (5, 6, 16, 200, 352, "bf16", True, "relu2"),      # K short of one 2048 pass
+    (24, 6, 32, 264, 2688, "bf16", True, "relu2"),    # the Nemotron hidden size: two passes, M x K = 64512
+    (32, 8, 64, 256, 2048, "bf16", False, "none"),    # 256 slots
+    (16, 4, 32, 256, 4096, "e4m3", True, "none"),     # K = 4096 and M x K = 65536
+    (28, 4, 16, 256, 2080, "e4m3", False, "relu2"),
+    (7, 2, 8, 640, 320, "e2m1x2", True, "none"),
+    (12, 4, 1024, 64, 256, "e2m1x2", False, "none"),  # 1024 experts
+    (3, 1, 4, 128, 64, "bf16", False, "none"),        # top-1, K = 64
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "T{}k{}E{}N{}K{}{}{}{}".format(
+    *c[:6], "b" if c[6] else "", c[7]))
+def test_decode_layer_equals_three_launches_and_oracle(case):
+    T, k, E, N, K, wd, bias, ep = case
+    d = synth.gemm_case(T, k, E, N, K, wd, seed=T * 7 + N + K, bias=bias, w_std=0.5)
+    dd = to_dev(d)
+    C3, y3 = _unfused(dd, T, k, E, N, wd, ep)
+    C1, y1 = _fused(dd, T, k, N, wd, ep)
+    torch.cuda.synchronize()
+    _same_bits(C1, C3, f"C {case}")
+    _same_bits(y1, y3, f"y {case}")
+    rC, routed, ry = _oracle(d, T, k, E, wd, ep)
+    assert routed.all()
+    assert_parity(bf16_to_f64(C1), rC, what=f"C {case}")
+    assert_parity(bf16_to_f64(y1), ry, what=f"y {case}")
+
+
+@pytest.mark.parametrize("M", [1, 7, 14, 21, 28, 32])
+def test_decode_shape_equals_three_launches(M):
+    # the decode workload: E=128, N=1856, K=2048, top-6, bf16 weights; the
+    # oracle checks 64 sampled output columns
+    d = synth.config2(M, device="cuda")
+    T, k, E, N = M, 6, 128, 1856
+    C3, y3 = _unfused(d, T, k, E, N, "bf16", "none")
+    C1, y1 = _fused(d, T, k, N, "bf16", "none")
+    torch.cuda.synchronize()
+    _same_bits(C1, C3, f"C M={M}")
+    _same_bits(y1, y3, f"y M={M}")
+    cols = np.sort(np.random.default_rng(M).choice(N, 64, replace=False))
+    sub = dict(d, w=d["w"][:, torch.from_numpy(cols).cuda(), :].contiguous())
+    rC, _, ry = _oracle(sub, T, k, E, "bf16", "none")
+    assert_parity(bf16_to_f64(C1)[:, cols], rC, what=f"C M={M}")
+    assert_parity(bf16_to_f64(y1)[:, cols], ry, what=f"y M={M}")
+
+
+def test_nemotron_up_projection_equals_three_launches():
+    # hidden 2688 (two K passes) at M = 24, the largest token count whose
+    # activations fit on chip at that K, with bias and relu2
+    d = synth.nemotron_layer(24, device="cuda", bias=True)
+    dd = {"x": d["x"], "ids": d["ids"], "topk_w": d["topk_w"], "w": d["w1"], "w_scale": None, "bias": d["b1"]}
+    C3, y3 = _unfused(dd, 24, 6, 128, 1856, "bf16", "relu2")
+    C1, y1 = _fused(dd, 24, 6, 1856, "bf16", "relu2")
+    torch.cuda.synchronize()
+    _same_bits(C1, C3, "C")
+    _same_bits(y1, y3, "y")
+
+
+def test_ragged_n_against_oracle():
+    # N = 203: the last workgroup owns three live columns (moe_combine needs
+    # N % 8 == 0, so the oracle alone is the reference here)
+    T, k, E, N, K = 9, 3, 12, 203, 512
+    d = synth.gemm_case(T, k, E, N, K, "e4m3", seed=31, bias=True, w_std=0.5)
+    dd = to_dev(d)
+    C1, y1 = _fused(dd, T, k, N, "e4m3", "relu2")
+    torch.cuda.synchronize()
+    rC, _, ry = _oracle(d, T, k, E, "e4m3", "relu2")
+    assert_parity(bf16_to_f64(C1), rC, what="C")
+    assert_parity(bf16_to_f64(y1), ry, what="y")
+
+
+@pytest.mark.parametrize("kind", ["zipf", "repeated"])
+def test_skewed_and_repeated_routing(kind):
+    # zipf: a few experts take most slots (long slot lists per expert);
+    # repeated: a token names one expert several times
+    T, k, E, N, K = 32, 6, 64, 256, 1024
+    d = synth.gemm_case(T, k, E, N, K, "bf16", seed=41, w_std=0.5)
+    if kind == "zipf":
+        d["ids"], d["topk_w"] = synth.zipf_topk_routing(T, E, k, 1.5, 8, 41)
+    else:
+        g = torch.Generator().manual_seed(41)
+        d["ids"] = torch.randint(0, 4, (T, k), generator=g, dtype=torch.int32)
+    dd = to_dev(d)
+    C3, y3 = _unfused(dd, T, k, E, N, "bf16", "none")
+    C1, y1 = _fused(dd, T, k, N, "bf16", "none")
+    torch.cuda.synchronize()
+    _same_bits(C1, C3, "C")
+    _same_bits(y1, y3, "y")
+    rC, _, ry = _oracle(d, T, k, E, "bf16", "none")
+    assert_parity(bf16_to_f64(y1), ry, what="y")
+
+
+def test_ids_outside_the_experts_contribute_zero():
+    T, k, E, N, K = 6, 4, 16, 128, 256
+    d = synth.gemm_case(T, k, E, N, K, "bf16", seed=51, bias=True, w_std=0.5)
+    ids = d["ids"].clone()
+    ids[0, 1], ids[3, 0], ids[5, 3] = -1, E, 1 << 30
+    d["ids"] = ids
+    dd = to_dev(d)
+    C1, y1 = _fused(dd, T, k, N, "bf16", "none")
+    torch.cuda.synchronize()
+    rC, routed, ry = _oracle(d, T, k, E, "bf16", "none")
+    assert routed.sum() == T * k - 3
+    got = bf16_to_f64(C1)
+    assert np.isnan(got[~routed]).all()          # rows of unrouted slots are not written
+    assert_parity(got[routed], rC[routed], what="C")
+    assert_parity(bf16_to_f64(y1), ry, what="y")
+
+
+def test_repeated_calls_identical_and_empty():
+    # the slots of an expert are grouped with LDS atomics, in any order; each
+    # output is computed on its own, so every call gives the same bits
+    moe = _moe()
+    d = to_dev(synth.gemm_case(20, 6, 32, 256, 2048, "e2m1x2", seed=61, bias=True))
+    ys = [moe.moe_decode_layer(d["x"], d["ids"], d["topk_w"], d["w"], "e2m1x2", w_scale=d["w_scale"],
+                               bias=d["bias"]) for _ in range(4)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        _same_bits(y, ys[0], "repeat")
+    y0 = moe.moe_decode_layer(d["x"][:0], d["ids"][:0], d["topk_w"][:0], d["w"], "e2m1x2", w_scale=d["w_scale"])
+    torch.cuda.synchronize()
+    assert tuple(y0.shape) == (0, 256)
+
+
+def test_outside_the_limits_is_refused():
+    moe = _moe()
+    assert not moe.moe_decode_layer_fits(25, 6, 128, 2688)
+    d = to_dev(synth.gemm_case(25, 6, 8, 64, 2688, "bf16", seed=71))
+    with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
+        moe.moe_decode_layer(d["x"], d["ids"], d["topk_w"], d["w"], "bf16")
+    with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
+        moe.moe_decode_layer(d["x"][:4], d["ids"][:4], d["topk_w"][:4], d["w"], "bf16", epilogue="swiglu")

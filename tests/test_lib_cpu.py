@@ -39,7 +39,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol():
     syms = _declared_symbols()
-    assert len(syms) == 18, syms
+    assert len(syms) == 20, syms
     for name in syms:
         assert hasattr(L, name), name
 
@@ -196,6 +196,52 @@ def test_grouped_gemm_rejects(no_device):
                  w_scale_ld=512, w_scale_stride_e=1024) == INVALID            # expert stride too small
     assert _gemm(w_layout=moe.MOE_LAYOUT_KBLOCK, w_ld=256 * 32, w_stride_e=2 * 256 * 32,
                  w_scale_ld=500, w_scale_stride_e=1024) == INVALID            # scale block stride < 2n
+
+
+def test_decode_layer_fits():
+    f = moe.moe_decode_layer_fits
+    assert f(28, 6, 128, 2048) and f(32, 8, 1024, 2048) and f(0, 6, 128, 2048)
+    assert f(24, 6, 128, 2688) and not f(25, 6, 128, 2688)   # M x K <= 65536
+    assert f(16, 6, 128, 4096) and not f(1, 6, 128, 4128)    # K <= 4096
+    assert not f(33, 1, 128, 256)                            # beyond the decode bucket
+    assert not f(32, 9, 128, 256)                            # 288 slots
+    assert not f(1, 6, 1025, 256)
+    assert not f(1, 6, 128, 100) and not f(-1, 6, 128, 256) and not f(1, 0, 128, 256)
+
+
+def _dl(ids=FAKE, tw=FAKE, y=FAKE, y_ld=None, **kw):
+    for key, v in (("T", 7), ("k", 6), ("E", 128), ("N", 256), ("K", 2048)):
+        kw.setdefault(key, v)
+    g = _gemm_args(**kw)
+    return L.moe_decode_layer(ctypes.byref(g), ids, tw, y, g.n if y_ld is None else y_ld, None)
+
+
+def test_decode_layer_rejects(no_device):
+    assert L.moe_decode_layer(None, FAKE, FAKE, FAKE, 256, None) == INVALID
+    assert _dl(T=33) == UNSUPPORTED                  # beyond the decode bucket
+    assert _dl(T=32, K=4096) == UNSUPPORTED          # M x K > 65536
+    assert _dl(K=4128) == UNSUPPORTED                # K > 4096
+    assert _dl(E=1025) == UNSUPPORTED
+    assert _dl(T=32, k=9, E=16) == UNSUPPORTED       # 288 slots
+    assert _dl(epilogue=1) == UNSUPPORTED            # SwiGLU
+    assert _dl(a_dtype=moe.MOE_E4M3) == UNSUPPORTED
+    assert _dl(w_dtype=moe.MOE_FP32) == UNSUPPORTED
+    assert _dl(epilogue=7) == INVALID
+    assert _dl(a_row_div=1) == INVALID               # A must hold token rows
+    assert _dl(K=100) == INVALID
+    assert _dl(num_tokens=-1) == INVALID
+    assert _dl(k=9, E=8) == INVALID                  # top_k > E
+    assert _dl(a_ld=2040) == INVALID                 # < K
+    assert _dl(y_ld=100) == INVALID                  # < N
+    assert _dl(c_ld=100) == INVALID                  # C given with c_ld < N
+    assert _dl(w_ld=16) == INVALID
+    assert _dl(w_scale=0) == INVALID
+    assert _dl(ids=None) == INVALID
+    assert _dl(tw=None) == INVALID
+    assert _dl(y=None) == INVALID
+    assert _dl(y=ctypes.c_void_p(0x100001)) == INVALID   # odd address
+    assert _dl(a=0x100004) == INVALID                # misaligned
+    assert _dl(bias=0x100000, bias_stride_e=-1) == INVALID
 
 
 def test_packed_sizes():
