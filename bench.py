@@ -5,25 +5,30 @@
 
 Prints one JSON line. The default workload is the bf16 decode MoE
 (E=128, N=1856, K=2048, top-6) at the MTP6 verify token counts
-M = 1, 7, 14, 21, 28; a step runs, for each M, moe_align -> decode grouped
-GEMM -> moe_combine.
+M = 1, 7, 14, 21, 28; a step runs, for each M, the decode MoE step (routing,
+grouped GEMM, top-k combine) through the fused layer moe_decode_layer (one
+launch), and the same step through the three launches moe_align -> decode
+grouped GEMM -> moe_combine.
 
-Headline (`value`, `roofline`): the decode step with a cold cache. Every call
-runs on a routing and activations drawn for it alone, after a 1 GiB device
-copy that evicts the previous call's weights from the 256 MB MALL and the L2s,
-and its inputs (activations, routing) are then written by small copies as
-their producers would, so only the weights are cold; HIP events on the launch
-stream bracket each call and its GEMM launch (the copies are outside), and a
-GPU spin at the head of each step lets the host queue
-the whole step first. `value` = the timed calls' algorithmic HBM bytes over
-their summed event time (GB/s); `roofline` = the decode GEMM's algorithmic
-bytes over its summed launch time; `cold.per_m` gives median / p10 / p90 per
-M. `warm` holds the same workload warm (graph-replayed steps on a cycled set
-of routings, and back-to-back launches of the GEMM). `large_m` holds the
-large-M half of the metric: the W4A16 gate+up GEMM, the MXFP8 grouped GEMM and
-the weight gradient, each kernel's TFLOP/s and fraction of the bf16 MFMA peak
-and of HBM bandwidth. The GPU clock (amdsmi, read-only) is sampled in each
-timed region.
+Headline (`value`, `roofline`): the fused decode step with a cold cache.
+Every call runs on a routing and activations drawn for it alone, after a
+1 GiB device copy that evicts the previous call's weights from the 256 MB
+MALL and the L2s, and its inputs (activations, routing) are then written by
+small copies as their producers would, so only the weights are cold; HIP
+events on the launch stream bracket each call (the copies are outside), and
+a GPU spin at the head of each step lets the host queue the whole step
+first. `value` = the bytes the timed calls must move (touched experts'
+weights, activations, ids and routing weights in, y out) over their summed
+event time (GB/s); `roofline` = the same for the layer kernel, the step's
+only launch. `cold.per_m` gives median / p10 / p90 per M for both paths;
+`cold.three_launch` the three-launch figures and the decode GEMM's own
+roofline. `warm` holds both paths warm (graph-replayed steps on a cycled set
+of routings, and back-to-back launches of the layer kernel and of the
+decode GEMM).
+`large_m` holds the large-M half of the metric: the W4A16 gate+up GEMM, the
+MXFP8 grouped GEMM and the weight gradient, each kernel's TFLOP/s and
+fraction of the bf16 MFMA peak and of HBM bandwidth. The GPU clock (amdsmi,
+read-only) is sampled in each timed region.
 
 The other workloads (the Nemotron relu2 decode layer, the W4A16 layer, the
 MXFP8 grouped GEMM with bf16 or MXFP8 activations, the per-token-scaled FP8
@@ -50,6 +55,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 METRIC = "grouped-GEMM TFLOP/s & % MFMA peak (large M); decode µs/call & % HBM BW"
+DECODE_LAYER_KERNEL = "moe_decode_layer_kernel"
 
 
 def parse():
@@ -70,6 +76,9 @@ def parse():
     ap.add_argument("--counters-from", metavar="DIR",
                     help="no GPU run: read rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv files (-o fetch, -o write) "
                          "from DIR and record the workload's per-launch HBM traffic in profiles/counters.json")
+    ap.add_argument("--counters-key", choices=["decode_layer"],
+                    help="with --counters-from: record the fused decode layer kernel's traffic (the cold "
+                         "decode headline) instead of the workload's dominant kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--phase", default="both", choices=["both", "cold", "warm"],
                     help="decode workload: cold-cache calls (the headline), warm graph replays, or both "
@@ -80,7 +89,8 @@ def parse():
 
 
 # sources whose change can change a workload's dominant kernel
-KERNEL_SOURCES = {"decode": ["decode.hip"], "nemotron": ["decode.hip"], "w4a16": ["gemm.hip", "gemm_util.h"],
+KERNEL_SOURCES = {"decode": ["decode.hip"], "decode_layer": ["decode_layer.hip", "decode_layer.h"],
+                  "nemotron": ["decode.hip"], "w4a16": ["gemm.hip", "gemm_util.h"],
                   "mxfp8": ["gemm.hip", "gemm_util.h"], "mxfp8a": ["gemm_f8.hip", "gemm_util.h"],
                   "pertoken": ["gemm_f8.hip", "gemm_util.h"],
                   "wgrad": ["wgrad.hip"], "copy": []}
@@ -110,7 +120,7 @@ def record_counters(workload, directory):
     them by the copy calibration and store the result in profiles/counters.json
     under the current kernel source hash."""
     import csv
-    key = WORKLOADS[workload].dominant
+    key = DECODE_LAYER_KERNEL if workload == "decode_layer" else WORKLOADS[workload].dominant
     per = {}
     for counter, stem in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         path = os.path.join(directory, f"{stem}_counter_collection.csv")
@@ -290,6 +300,34 @@ class Decode(Workload):
             ogemm.combine(C, tw, self.k)
             return self._call_bytes(0, i)
         return items, run, "GB/s"
+
+
+class DecodeFused(Decode):
+    """The decode workload through the fused layer (moe_decode_layer): one
+    launch per M does the routing, the GEMM and the combine."""
+    name = "decode_layer"
+    dominant = DECODE_LAYER_KERNEL
+
+    def _layer(self, c):
+        if "layer_call" not in c:
+            c["layer_call"], _ = self.moe.moe_decode_layer_prepare(c["x"], c["ids"], c["tw"], self.wg, "bf16",
+                                                                   out=c["y"])
+        return c["layer_call"]()
+
+    def _layer_bytes(self, v, i):
+        c = self.calls[v][i]
+        S = c["M"] * self.k
+        return c["touched"] * self.N * self.K * 2 + c["M"] * self.K * 2 + S * 8 + c["M"] * self.N * 2
+
+    def step_bytes(self, v):
+        return sum(self._layer_bytes(v, i) for i in range(len(self.MS)))
+
+    def step(self, v):
+        for c in self.calls[v]:
+            self._layer(c)
+
+    def dominant_launches(self, v):
+        return [(lambda c=c: self._layer(c), self._layer_bytes(v, i)) for i, c in enumerate(self.calls[v])]
 
 
 class Nemotron(Workload):
@@ -934,16 +972,18 @@ def spin_cycles(torch, stream, ms):
 
 
 def decode_cold(torch, moe, dev, stream, args, clock):
-    """The decode workload with a cold cache: every call (align -> decode GEMM
-    -> combine for one M) runs on a routing and activations drawn for it
-    alone, after a 1 GiB device copy (512 MiB read, 512 MiB written) that
-    evicts the previous call's weights from the 256 MB MALL and the L2s; the
-    call's activations, ids and routing weights are then written by small
-    copies, as the kernels that produce them would, so only the expert
-    weights are cold. The copies run outside the timed span: HIP events on
-    the launch stream bracket the call and, inside it, the GEMM launch. W
-    warmup steps, then K timed steps; a step is one call for each M in 1, 7,
-    14, 21, 28."""
+    """The decode workload with a cold cache, through both of the library's
+    paths for the step: the fused layer (moe_decode_layer, one launch) and
+    the three launches moe_align -> decode grouped GEMM -> moe_combine. Every
+    call runs on a routing and activations drawn for it alone, after a 1 GiB
+    device copy (512 MiB read, 512 MiB written) that evicts the previous
+    call's weights from the 256 MB MALL and the L2s; the call's activations,
+    ids and routing weights are then written by small copies, as the kernels
+    that produce them would, so only the expert weights are cold. The copies
+    run outside the timed span: HIP events on the launch stream bracket each
+    call and, inside the three-launch call, each launch. W warmup steps, then
+    K timed steps; a step is, for each M in 1, 7, 14, 21, 28, one call of
+    each path (each on its own draw, each after its own eviction)."""
     import numpy as np
     import synth
     E, N, K, k = 128, 1856, 2048, 6
@@ -954,27 +994,43 @@ def decode_cold(torch, moe, dev, stream, args, clock):
         bm = moe.moe_gemm_block_m("bf16", M)
         lst = []
         for r in range(n_steps):
-            x_src = synth.bf16_normal((M, K), 1.0, 1002, f"cold-x{M}c{r}", dev)
-            ids_src, tw_src = synth.softmax_topk_routing(M, E, k, 1002, f"cold-route{M}c{r}", dev)
-            x, ids, tw = torch.empty_like(x_src), torch.empty_like(ids_src), torch.empty_like(tw_src)
-            routing = _routing_buffers(torch, M, k, E, bm, dev)
-            C = torch.empty((M * k, N), dtype=torch.bfloat16, device=dev)
-            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            gemm, _ = moe.moe_grouped_gemm_prepare(x, w, "bf16", routing, M, k, E, k, out=C, stream=stream)
-            touched = len(np.unique(ids_src.cpu().numpy()))
-            S, mb = M * k, routing[1].numel()
-            gemm_bytes = touched * N * K * 2 + M * K * 2 + S * N * 2
-            call_bytes = gemm_bytes + (S * 4 + mb * bm * 4 + mb * 4 + 4) + (S * N * 2 + M * N * 2 + S * 4)
-            lst.append(dict(ids=ids, tw=tw, x=x, srcs=((x, x_src), (ids, ids_src), (tw, tw_src)),
-                            bm=bm, routing=routing, C=C, y=y, gemm=gemm, touched=touched,
-                            gemm_bytes=gemm_bytes, call_bytes=call_bytes))
+            pair = []
+            for path in ("fused", "three"):
+                x_src = synth.bf16_normal((M, K), 1.0, 1002, f"cold-x{M}c{r}{path}", dev)
+                ids_src, tw_src = synth.softmax_topk_routing(M, E, k, 1002, f"cold-route{M}c{r}{path}", dev)
+                x, ids, tw = torch.empty_like(x_src), torch.empty_like(ids_src), torch.empty_like(tw_src)
+                y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                touched = len(np.unique(ids_src.cpu().numpy()))
+                S = M * k
+                # what the step has to move: the touched experts' weights, the
+                # activations, ids and routing weights in, y out
+                step_bytes = touched * N * K * 2 + M * K * 2 + S * 4 * 2 + M * N * 2
+                c = dict(path=path, srcs=((x, x_src), (ids, ids_src), (tw, tw_src)), touched=touched,
+                         step_bytes=step_bytes, y=y)
+                if path == "fused":
+                    c["layer"], _ = moe.moe_decode_layer_prepare(x, ids, tw, w, "bf16", out=y, stream=stream)
+                else:
+                    routing = _routing_buffers(torch, M, k, E, bm, dev)
+                    C = torch.empty((S, N), dtype=torch.bfloat16, device=dev)
+                    gemm, _ = moe.moe_grouped_gemm_prepare(x, w, "bf16", routing, M, k, E, k, out=C,
+                                                           stream=stream)
+                    mb = routing[1].numel()
+                    gemm_bytes = touched * N * K * 2 + M * K * 2 + S * N * 2
+                    call_bytes = gemm_bytes + (S * 4 + mb * bm * 4 + mb * 4 + 4) + (S * N * 2 + M * N * 2 + S * 4)
+                    c.update(ids=ids, tw=tw, bm=bm, routing=routing, C=C, gemm=gemm, gemm_bytes=gemm_bytes,
+                             call_bytes=call_bytes)
+                pair.append(c)
+            lst.append(pair)
         calls[M] = lst
     flush_src = torch.ones(1 << 29, dtype=torch.uint8, device=dev)
     flush_dst = torch.empty_like(flush_src)
     spin = spin_cycles(torch, stream, SPIN_MS)
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in DECODE_MS] for _ in range(n_steps)]
+    # per step, per M: events of the fused call (2) and of the three-launch call (4)
+    events = [[([torch.cuda.Event(enable_timing=True) for _ in range(2)],
+                [torch.cuda.Event(enable_timing=True) for _ in range(4)]) for _ in DECODE_MS]
+              for _ in range(n_steps)]
     torch.cuda.synchronize()
-    timed = []  # (M, events, call)
+    timed = []  # (M, fused events, fused call, three-launch events, three-launch call)
     clock.region = "decode_cold"
     gc.collect()
     gc.disable()  # no collector pause inside a step (the spin below covers the host's queueing of it)
@@ -985,54 +1041,74 @@ def decode_cold(torch, moe, dev, stream, args, clock):
             # gap falls inside an event pair
             torch.cuda._sleep(spin)
             for i, M in enumerate(DECODE_MS):
-                c = calls[M][step]
+                cf, c3 = calls[M][step]
+                evf, ev3 = events[step][i]
                 flush_dst.copy_(flush_src)
-                for dst, src in c["srcs"]:  # the call's inputs, written just before it as their producer would
+                for dst, src in cf["srcs"]:  # the call's inputs, written just before it as their producer would
                     dst.copy_(src)
-                ev = events[step][i]
-                ev[0].record(stream)
-                moe.moe_align(c["ids"], E, c["bm"], out=c["routing"], stream=stream)
-                ev[1].record(stream)
-                c["gemm"]()
-                ev[2].record(stream)
-                moe.moe_combine(c["C"], c["tw"], k, out=c["y"], stream=stream)
-                ev[3].record(stream)
+                evf[0].record(stream)
+                cf["layer"]()
+                evf[1].record(stream)
+                flush_dst.copy_(flush_src)
+                for dst, src in c3["srcs"]:
+                    dst.copy_(src)
+                ev3[0].record(stream)
+                moe.moe_align(c3["ids"], E, c3["bm"], out=c3["routing"], stream=stream)
+                ev3[1].record(stream)
+                c3["gemm"]()
+                ev3[2].record(stream)
+                moe.moe_combine(c3["C"], c3["tw"], k, out=c3["y"], stream=stream)
+                ev3[3].record(stream)
                 if step >= args.warmup:
-                    timed.append((M, ev, c))
+                    timed.append((M, evf, cf, ev3, c3))
             stream.synchronize()
     gc.enable()
     torch.cuda.synchronize()
     clock.region = None
-    per_m = {M: {"call": [], "gemm": [], "align": [], "combine": [], "touched": []} for M in DECODE_MS}
-    tot_bytes = tot_us = gemm_bytes = gemm_us = 0.0
-    for M, ev, c in timed:
-        call = ev[0].elapsed_time(ev[3]) * 1e3
-        g = ev[1].elapsed_time(ev[2]) * 1e3
+    keys = ("layer", "call", "gemm", "align", "combine", "touched", "layer_frac", "gemm_frac")
+    per_m = {M: {key: [] for key in keys} for M in DECODE_MS}
+    tot = {"layer_bytes": 0.0, "layer_us": 0.0, "call_bytes": 0.0, "call_step_bytes": 0.0, "call_us": 0.0,
+           "gemm_bytes": 0.0, "gemm_us": 0.0}
+    for M, evf, cf, ev3, c3 in timed:
+        layer = evf[0].elapsed_time(evf[1]) * 1e3
+        call = ev3[0].elapsed_time(ev3[3]) * 1e3
+        g = ev3[1].elapsed_time(ev3[2]) * 1e3
         d = per_m[M]
+        d["layer"].append(layer)
         d["call"].append(call)
         d["gemm"].append(g)
-        d["align"].append(ev[0].elapsed_time(ev[1]) * 1e3)
-        d["combine"].append(ev[2].elapsed_time(ev[3]) * 1e3)
-        d["touched"].append(c["touched"])
-        tot_bytes += c["call_bytes"]
-        tot_us += call
-        gemm_bytes += c["gemm_bytes"]
-        gemm_us += g
+        d["align"].append(ev3[0].elapsed_time(ev3[1]) * 1e3)
+        d["combine"].append(ev3[2].elapsed_time(ev3[3]) * 1e3)
+        d["touched"].append(cf["touched"])
+        d["layer_frac"].append(cf["step_bytes"] / layer / 1e3 / PEAK_HBM_GBS)
+        d["gemm_frac"].append(c3["gemm_bytes"] / g / 1e3 / PEAK_HBM_GBS)
+        tot["layer_bytes"] += cf["step_bytes"]
+        tot["layer_us"] += layer
+        tot["call_bytes"] += c3["call_bytes"]
+        tot["call_step_bytes"] += c3["step_bytes"]
+        tot["call_us"] += call
+        tot["gemm_bytes"] += c3["gemm_bytes"]
+        tot["gemm_us"] += g
     out = {}
     for M in DECODE_MS:
         d = per_m[M]
-        gb = [c["gemm_bytes"] for (m, _, c) in timed if m == M]
-        out[str(M)] = {"gemm_us": stats(d["gemm"]), "call_us": stats(d["call"]),
-                       "align_us": stats(d["align"]),
-                       "combine_us": stats(d["combine"]),
-                       "gemm_hbm_frac_median": round(float(np.median(np.array(gb) / np.array(d["gemm"]) / 1e3))
-                                                     / PEAK_HBM_GBS, 4),
+        out[str(M)] = {"layer_us": stats(d["layer"]),
+                       "layer_hbm_frac_median": round(float(np.median(d["layer_frac"])), 4),
+                       "three_launch": {"call_us": stats(d["call"]), "gemm_us": stats(d["gemm"]),
+                                        "align_us": stats(d["align"]), "combine_us": stats(d["combine"]),
+                                        "gemm_hbm_frac_median": round(float(np.median(d["gemm_frac"])), 4)},
                        "touched_experts_mean": round(float(np.mean(d["touched"])), 1)}
     del calls, flush_src, flush_dst, w
     torch.cuda.empty_cache()
-    return {"value": tot_bytes / (tot_us * 1e-6) / 1e9, "ms_per_step": tot_us / args.steps / 1e3,
-            "gemm_GBps": gemm_bytes / (gemm_us * 1e-6) / 1e9, "gemm_avg_us": gemm_us / len(timed),
-            "per_m": out, "calls": len(timed)}
+    n = len(timed)
+    return {"value": tot["layer_bytes"] / (tot["layer_us"] * 1e-6) / 1e9,
+            "ms_per_step": tot["layer_us"] / args.steps / 1e3, "layer_avg_us": tot["layer_us"] / n,
+            "three_launch": {"GBps": round(tot["call_step_bytes"] / (tot["call_us"] * 1e-6) / 1e9, 3),
+                             "GBps_with_intermediates": round(tot["call_bytes"] / (tot["call_us"] * 1e-6) / 1e9, 3),
+                             "ms_per_step": round(tot["call_us"] / args.steps / 1e3, 4),
+                             "gemm_GBps": round(tot["gemm_bytes"] / (tot["gemm_us"] * 1e-6) / 1e9, 3),
+                             "gemm_avg_us": round(tot["gemm_us"] / n, 3)},
+            "per_m": out, "calls": n}
 
 
 def measure(wl, torch, stream, args, nv, clock, region):
@@ -1143,7 +1219,7 @@ def large_m_block(torch, dev, stream, args, clock):
 def main():
     args = parse()
     if args.counters_from:
-        record_counters(args.workload, args.counters_from)
+        record_counters(args.counters_key or args.workload, args.counters_from)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of this "
@@ -1182,15 +1258,27 @@ def decode_main(torch, moe, dev, stream, args, clock):
                 "ms_per_step": round(m["dt"] / args.steps * 1e3, 4), "routing_variants": nv,
                 "roofline": roof, "launch_reps": args.launch_reps, "clock": clock.summary("decode_warm")}
         warm.update(wl.extra(per_call))
+        wf = DecodeFused(torch, dev, args.variants)
+        m = measure(wf, torch, stream, args, nv, clock, "decode_warm_fused")
+        per_call = [sum(v) / len(v) for _, v in sorted(m["per_call"].items())]
+        warm_fused = {"value": round(m["step_bytes"] / m["dt"] / 1e9, 3), "unit": "GB/s",
+                      "ms_per_step": round(m["dt"] / args.steps * 1e3, 4), "roofline": roofline_of(wf, m),
+                      "clock": clock.summary("decode_warm_fused")}
+        warm_fused.update(wf.extra(per_call))
+        warm = {"fused_layer": warm_fused, "three_launch": warm}
+        del wf, m
+        torch.cuda.empty_cache()
     if cold is not None:
-        roof_cold = {"bound": "hbm", "achieved": round(cold["gemm_GBps"], 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(cold["gemm_GBps"] / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode", None),
-                     "kernel": "moe_decode_kernel", "avg_launch_us": round(cold["gemm_avg_us"], 3),
+        # the fused layer is the step's one launch: its roofline is the step's
+        roof_cold = {"bound": "hbm", "achieved": round(cold["value"], 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(cold["value"] / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode_layer", None),
+                     "kernel": DECODE_LAYER_KERNEL, "avg_launch_us": round(cold["layer_avg_us"], 3),
                      "cache": "cold (1 GiB copy between calls)"}
         value, ms = cold["value"], cold["ms_per_step"]
         roofline = roof_cold
     else:
-        value, ms, roofline = warm["value"], warm["ms_per_step"], warm["roofline"]
+        wfl = warm["fused_layer"]
+        value, ms, roofline = wfl["value"], wfl["ms_per_step"], wfl["roofline"]
     cpu = None
     if not args.no_cpu_baseline:
         if wl is None:
@@ -1200,14 +1288,24 @@ def decode_main(torch, moe, dev, stream, args, clock):
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": CONFIG_NAMES["decode"],
+                       "path": "moe_decode_layer: routing, grouped GEMM and top-k combine in one launch",
                        "cache": "cold: every call on its own routing, after a 1 GiB copy that evicts the MALL",
                        "weight_layout": LAYOUT["decode"], "parallelism": "single GPU"},
             "roofline": roofline, "cpu_baseline": cpu}
     if cold is not None:
         line["hbm_frac_step"] = round(value / PEAK_HBM_GBS, 4)
-        line["cold"] = {"per_m": cold["per_m"], "calls": cold["calls"], "clock": clock.summary("decode_cold"),
+        three = dict(cold["three_launch"])
+        three["gemm_roofline"] = {"bound": "hbm", "achieved": three["gemm_GBps"], "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": round(three["gemm_GBps"] / PEAK_HBM_GBS, 4),
+                                  "traffic": load_traffic("decode", None), "kernel": "moe_decode_kernel"}
+        line["cold"] = {"per_m": cold["per_m"], "calls_per_path": cold["calls"],
+                        "three_launch": three, "clock": clock.summary("decode_cold"),
                         "ms_per_step_note": "device time of the step's launches (events); the copies that "
-                                            "evict the cache between calls are outside it"}
+                                            "evict the cache between calls are outside it",
+                        "bytes_note": "value counts the bytes the step must move (touched experts' weights, "
+                                      "activations, ids and routing weights in, y out); the three-launch "
+                                      "path also moves C and the routing buffers "
+                                      "(GBps_with_intermediates counts them)"}
     if warm is not None:
         line["warm"] = warm
     if not args.no_large_m and args.phase == "both":

@@ -11,6 +11,7 @@
 
 #include "moe.h"
 
+#include "decode_layer.h"
 #include "params.h"
 
 namespace {

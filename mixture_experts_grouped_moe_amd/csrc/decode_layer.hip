@@ -15,7 +15,7 @@
 //    of those columns end in one workgroup and the combine needs no
 //    cross-workgroup step and no scratch memory. Each wave streams its row of
 //    every touched expert in ascending expert order with non-temporal loads,
-//    kDlPrefetch experts ahead; every expert's weights are read once.
+//    two experts ahead; every expert's weights are read once.
 //  * Every global load before the combine is a buffer load whose
 //    out-of-range pieces read as zero, so none sits under a branch: the
 //    compiler can then wait for exactly the oldest row of the prefetch ring
@@ -39,7 +39,7 @@
 #include <type_traits>
 
 #include "common.h"
-#include "params.h"
+#include "decode_layer.h"
 
 namespace moe {
 
@@ -49,7 +49,6 @@ constexpr int kDlMaxE = 1024;
 constexpr int kDlMaxS = 256;                     // slots (tokens x top_k)
 constexpr int kDlMaxXElems = 65536;              // M x K activation elements in LDS (128 KB)
 constexpr int kDlXLoads = kDlMaxXElems / 8 / kDlThreads;  // 16-byte activation pieces per thread
-constexpr int kDlPrefetch = 4;                   // experts whose row is in flight per wave
 constexpr int kDlPass = 2048;                    // the decode kernel's K elements per pass
 constexpr int kDlPassPieces = kDlPass / 8 / kWave;  // 8-element pieces per lane per pass
 constexpr int kDlMaxPieces = 2 * kDlPassPieces;  // K <= 4096
@@ -80,12 +79,23 @@ __device__ __forceinline__ float dl_wave_sum(float v) {
   return v;
 }
 
+// f(integral_constant<int, R>) for R = R0 .. PF - 1, in order (the ring
+// slots are compile-time indices, so the rows stay in registers)
+template <int R0, int PF, class F>
+__device__ __forceinline__ void dl_for_slots(F&& f) {
+  if constexpr (R0 < PF) {
+    f(std::integral_constant<int, R0>{});
+    dl_for_slots<R0 + 1, PF>(f);
+  }
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dl_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kDlRsrcWord3);
 }
 
 // NP: 8-element pieces per lane per weight row (4 for K <= 2048, else 8).
-template <int WDT, bool BIAS, int NP>
+// PF: rows in flight per wave (the ring's depth).
+template <int WDT, bool BIAS, int NP, int PF>
 __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeLayerParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kDlMaxXElems];  // token rows, K elements each
   __shared__ int32_t s_cnt[kDlMaxE];    // slots per expert, then the scatter cursor
@@ -185,9 +195,9 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
   const int n = blockIdx.x * kDlWaves + wave;
   const bool row_live = n < p.N;
   constexpr int kWords = (WDT == W_BF16) ? 4 : (WDT == W_E4M3 ? 2 : 1);
-  uint32_t wraw[kDlPrefetch][NP][kWords];
-  uint32_t sraw[kDlPrefetch][NP];
-  uint32_t braw[kDlPrefetch];
+  uint32_t wraw[PF][NP][kWords];
+  uint32_t sraw[PF][NP];
+  uint32_t braw[PF];
   const __amdgpu_buffer_rsrc_t b_rsrc = dl_rsrc(p.bias, BIAS ? p.bias_bytes : 0u);
   auto load_row = [&](int idx, auto slot_tag) {
     constexpr int R = decltype(slot_tag)::value;
@@ -285,15 +295,7 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
       }
     }
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  static_assert(kDlPrefetch == 4, "the ring below is written for four slots");
-  load_row(0, S0{});
-  load_row(1, S1{});
-  load_row(2, S2{});
-  load_row(3, S3{});
+  dl_for_slots<0, PF>([&](auto r) { load_row(decltype(r)::value, r); });
   // the activations into LDS (their loads were issued before the rows')
 #pragma unroll
   for (int i = 0; i < kDlXLoads; ++i) {
@@ -301,16 +303,14 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
     if (q < nx) *reinterpret_cast<u32x4_t*>(&xs[(q / k8) * K + (q % k8) * 8]) = xr[i];
   }
   __syncthreads();
-  // row idx lives in ring slot idx % kDlPrefetch
-  for (int idx = 0; idx < nt; idx += kDlPrefetch) {
-    compute_row(idx, S0{});
-    load_row(idx + 4, S0{});
-    compute_row(idx + 1, S1{});
-    load_row(idx + 5, S1{});
-    compute_row(idx + 2, S2{});
-    load_row(idx + 6, S2{});
-    compute_row(idx + 3, S3{});
-    load_row(idx + 7, S3{});
+  // row idx lives in ring slot idx % PF; its slot is refilled with row
+  // idx + PF as soon as it has been used
+  for (int idx = 0; idx < nt; idx += PF) {
+    dl_for_slots<0, PF>([&](auto r) {
+      constexpr int R = decltype(r)::value;
+      compute_row(idx + R, r);
+      load_row(idx + R + PF, r);
+    });
   }
   __syncthreads();
 
@@ -343,8 +343,13 @@ int decode_layer_max_k() { return kDlMaxPieces / kDlPassPieces * kDlPass; }
 
 template <int WDT, int NP>
 static void launch_dl(const DecodeLayerParams& p, bool bias, dim3 grid, hipStream_t stream) {
-  if (bias) hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, true, NP>), grid, dim3(kDlThreads), 0, stream, p);
-  else hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, false, NP>), grid, dim3(kDlThreads), 0, stream, p);
+  // Two rows in flight per wave (8 KB per wave at K = 2048, 64 KB per CU):
+  // on a cold cache, depths 1, 2, 3, 4, 6 and 8 gave about 134, 121, 124, 123, 123
+  // and 124 us at M = 28 (K = 2048) and 172, 152, 154, 160 us at M = 24,
+  // K = 2688 (depths 1-4); deeper rings only lengthen the memory queues.
+  constexpr int PF = 2;
+  if (bias) hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, true, NP, PF>), grid, dim3(kDlThreads), 0, stream, p);
+  else hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, false, NP, PF>), grid, dim3(kDlThreads), 0, stream, p);
 }
 
 template <int WDT>

@@ -46,29 +46,6 @@ struct GemmParams {
   const float* exp_scale;
 };
 
-// The decode MoE step in one launch (routing, grouped GEMM, combine).
-struct DecodeLayerParams {
-  const uint16_t* x;     // bf16 token rows [T][K]
-  int64_t x_ld;          // elements
-  const int32_t* topk_ids;  // [T * top_k]
-  const float* topk_w;      // [T * top_k]
-  const uint8_t* w;      // weight codes; strides in bytes as in GemmParams
-  int64_t w_stride_e, w_row, w_blk;
-  const uint8_t* ws;     // E8M0 scales (block-scaled weights)
-  int64_t ws_stride_e, ws_row, ws_blk;
-  const uint16_t* bias;  // bf16 [E][N] or null
-  int64_t bias_se, bias_sn;
-  uint16_t* c;           // bf16 [S][N] expert outputs, or null (not written)
-  int64_t c_ld;
-  uint16_t* y;           // bf16 [T][N]
-  int64_t y_ld;
-  int32_t S, top_k, E, N, K;
-  int32_t relu2;
-  // byte ranges of the buffer loads (each < 2^31): the T token rows, one
-  // weight row's codes and scale bytes (from the row's first byte), the bias
-  uint32_t x_bytes, w_rspan, ws_rspan, bias_bytes;
-};
-
 struct WgradParams {
   const uint16_t* x;
   int64_t x_ld;
@@ -99,11 +76,6 @@ hipError_t launch_gemm_per_token(const GemmParams& p, bool bias, hipStream_t str
 hipError_t launch_combine(const uint16_t* c, int64_t c_ld, const float* w, int64_t T, int32_t top_k,
                           int64_t N, uint16_t* y, int64_t y_ld, hipStream_t stream);
 hipError_t launch_wgrad(const WgradParams& p, hipStream_t stream);
-hipError_t launch_decode_layer(const DecodeLayerParams& p, int wdt, bool bias, hipStream_t stream);
-int decode_layer_max_slots();
-int decode_layer_max_experts();
-int64_t decode_layer_max_act_elems();
-int decode_layer_max_k();
 // Copy one block of rows-layout codes/scales into the K-block layout.
 hipError_t launch_pack(const uint8_t* w, int64_t w_stride_e, int64_t w_ld, const uint8_t* ws,
                        int64_t ws_stride_e, int64_t ws_ld, int32_t E, int32_t N, int32_t K, int32_t row_bytes,
