@@ -63,6 +63,21 @@ def _routing(moe, T, k, E, bm):
             torch.empty(1, dtype=torch.int32, device="cuda"))
 
 
+def test_graph_fused_decode_layer():
+    # the decode step in one launch (routing in LDS, GEMM, combine), its
+    # expert outputs written too; e2m1 weights with bias
+    moe = _moe()
+    T, k, E, N, K = 9, 6, 32, 512, 1024
+    d = synth.gemm_case(T, k, E, N, K, "e2m1x2", seed=23, bias=True, device="cuda")
+    C = torch.empty((T * k, N), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        moe.moe_decode_layer(d["x"], d["ids"], d["topk_w"], d["w"], "e2m1x2", w_scale=d["w_scale"],
+                             bias=d["bias"], out=y, c_out=C)
+    _replays_match(step, [C, y])
+
+
 def test_graph_decode_step():
     moe = _moe()
     T, k, E, N, K = 7, 6, 32, 512, 1024
