@@ -25,10 +25,11 @@ only launch. `cold.per_m` gives median / p10 / p90 per M for both paths;
 roofline. `warm` holds both paths warm (graph-replayed steps on a cycled set
 of routings, and back-to-back launches of the layer kernel and of the
 decode GEMM).
-`large_m` holds the large-M half of the metric: the W4A16 gate+up GEMM, the
-MXFP8 grouped GEMM and the weight gradient, each kernel's TFLOP/s and
-fraction of the bf16 MFMA peak and of HBM bandwidth. The GPU clock (amdsmi,
-read-only) is sampled in each timed region.
+`large_m` holds the large-M half of the metric: the W4A16 gate+up GEMM (and
+its down GEMM under `large_m.w4a16.down`), the MXFP8 grouped GEMM and the
+weight gradient, each kernel's TFLOP/s and fraction of the bf16 MFMA peak
+and of HBM bandwidth. The GPU clock (amdsmi, read-only) is sampled in each
+timed region.
 
 The other workloads (the Nemotron relu2 decode layer, the W4A16 layer, the
 MXFP8 grouped GEMM with bf16 or MXFP8 activations, the per-token-scaled FP8
@@ -478,8 +479,7 @@ class W4A16(Workload):
         c, d, moe = self.calls[v], self.d, self.moe
         moe.moe_align(c["ids"], self.E, c["bm"], out=c["routing"])
         self._up(c)
-        moe.moe_grouped_gemm(c["h"], self.w2, "e2m1x2", c["routing"], c["Tb"], self.k, self.E, 1,
-                             w_scale=self.s2, out=c["c2"])
+        self._down(c)
         moe.moe_combine(c["c2"], c["tw"], self.k, num_tokens=c["T"], out=c["y"])
 
     def dominant_launches(self, v):
@@ -492,6 +492,19 @@ class W4A16(Workload):
         T = self.calls[v]["T"]
         w = self.E * 2 * self.I * self.H // 2 * (1 + 1 / 16)
         return 2 * T * self.k * 2 * self.I * self.H, int(w + T * self.H * 2 + T * self.k * self.I * 2)
+
+    def _down(self, c):
+        return self.moe.moe_grouped_gemm(c["h"], self.w2, "e2m1x2", c["routing"], c["Tb"], self.k, self.E, 1,
+                                         w_scale=self.s2, out=c["c2"])
+
+    def second_launches(self, v):
+        """The down GEMM (K = 2880 over h's slot rows, N = 2880), with its
+        algorithmic flops and HBM bytes (codes and scales, h read, C written)."""
+        c = self.calls[v]
+        S = c["T"] * self.k
+        w = self.E * self.H * self.I // 2 * (1 + 1 / 16)
+        return "down", [(lambda c=c: self._down(c), 2 * S * self.H * self.I,
+                         int(w + S * self.I * 2 + S * self.H * 2))]
 
     def extra(self, per_call_us):
         return {"tokens": [c["T"] for c in self.calls], "buckets": [c["Tb"] for c in self.calls]}
@@ -1184,6 +1197,36 @@ def roofline_of(wl, m):
 LARGE_M = ("w4a16", "mxfp8", "wgrad")
 
 
+def time_second_kernel(wl, torch, stream, args, nv):
+    """A workload's second GEMM timed like its dominant one: its launches
+    back to back on resident inputs, one event pair each, after the step's
+    earlier launches produced its input."""
+    durs = []
+    key = None
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            v = i % nv
+            wl.step(v)  # the second GEMM's input (h) for this variant
+            key, launches = wl.second_launches(v)
+            for fn, flops, nbytes in launches:
+                fn()
+                for _ in range(args.launch_reps):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    fn()
+                    b.record(stream)
+                    durs.append((a, b, flops, nbytes))
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b, _, _ in durs]
+    secs = sum(us) * 1e-6
+    flops = sum(f for _, _, f, _ in durs)
+    nbytes = sum(n for _, _, _, n in durs)
+    return {key: {"launch_us": stats(us), "tflops": round(flops / secs / 1e12, 1),
+                  "bf16_peak_frac": round(flops / secs / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "hbm_GBps": round(nbytes / secs / 1e9, 1)}}
+
+
 def large_m_block(torch, dev, stream, args, clock):
     """The large-M half of the metric: per workload, the dominant kernel's
     TFLOP/s and fractions of the bf16 MFMA peak and of HBM bandwidth (sums
@@ -1210,6 +1253,8 @@ def large_m_block(torch, dev, stream, args, clock):
             "clock": clock.summary(f"large_m_{name}"),
         }
         out[name].update(wl.extra(None))
+        if hasattr(wl, "second_launches"):
+            out[name].update(time_second_kernel(wl, torch, stream, args, nv))
         del wl, m
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
