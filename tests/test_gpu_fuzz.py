@@ -2,7 +2,8 @@
 weight encoding, both weight layouts, the three epilogues, bias on and off,
 GEMMs over token rows and over slot rows, decode and large-M token counts,
 checked in full against the float64 oracle (max|gpu - oracle| <= 5e-3 *
-max|oracle|)."""
+max|oracle|); likewise the MXFP8-activation and per-token GEMMs, the weight
+gradient and the fused decode layer (its C and y)."""
 
 import numpy as np
 import pytest
@@ -133,3 +134,42 @@ def test_wgrad_random_shapes(seed):
     got = dw.cpu().double().numpy()
     for e in range(E):
         assert_parity(got[e], ref[e], what=f"wgrad case {seed}, expert {e}")
+
+
+def _layer_case(seed):
+    rng = np.random.default_rng(3000 + seed)
+    wd = ("e2m1x2", "e4m3", "bf16")[seed % 3]
+    K = 32 * int(rng.integers(1, 129))                 # up to 4096
+    T = int(rng.integers(0, min(32, 65536 // K) + 1))  # activations fit on chip
+    E = int(rng.integers(1, 300))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    N = int(rng.integers(1, 700))
+    return dict(wd=wd, T=T, E=E, k=k, K=K, N=N, epilogue=("none", "relu2")[int(rng.integers(0, 2))],
+                bias=bool(rng.integers(0, 2)), packed=bool(rng.integers(0, 2)))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_layer_random_shapes(seed):
+    # the fused decode layer (routing, GEMM, combine in one launch) on random
+    # shapes within its limits: y and C against the oracle
+    import mixture_experts_grouped_moe_amd as moe
+    c = _layer_case(seed)
+    print("case", seed, c, flush=True)
+    T, k, E, N, K, wd = c["T"], c["k"], c["E"], c["N"], c["K"], c["wd"]
+    assert moe.moe_decode_layer_fits(T, k, E, K)
+    w_std = {"bf16": 0.05, "e4m3": 0.5, "e2m1x2": 1.0}[wd]
+    d = synth.gemm_case(T, k, E, N, K, wd, seed=seed, bias=c["bias"], w_std=w_std, device="cuda")
+    w = moe.moe_pack_weights(d["w"], wd, w_scale=d["w_scale"]) if c["packed"] else d["w"]
+    C = torch.full((T * k, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = moe.moe_decode_layer(d["x"], d["ids"], d["topk_w"], w, wd, w_scale=None if c["packed"] else d["w_scale"],
+                             bias=d["bias"], epilogue=c["epilogue"], c_out=C)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (T, N)
+    if T == 0:
+        return
+    h = host(d)
+    ref, routed = ogemm.grouped_gemm(h["x"], k, h["w"], wd, h["w_scale"], h["ids"], E, bias=h["bias"],
+                                     epilogue=c["epilogue"])
+    assert routed.all()
+    assert_parity(bf16_to_f64(C), ref, what=f"C case {seed}")
+    assert_parity(bf16_to_f64(y), ogemm.combine(ref, h["topk_w"], k), what=f"y case {seed}")
