@@ -4,8 +4,8 @@ C equal, bit for bit, those of moe_align -> moe_grouped_gemm -> moe_combine
 on the same inputs, and both match the float64 oracle: every weight encoding,
 with and without bias and the relu2 epilogue, K short of a pass and across
 two passes, N not a multiple of 8, skewed and repeated routing, ids outside
-[0, E), and the launch's limits (256 slots, 1024 experts, K = 4096,
-M x K = 65536)."""
+[0, E), NaN scale bytes, and the launch's limits (256 slots, 1024 experts,
+K = 4096, M x K = 65536)."""
 
 import numpy as np
 import pytest
@@ -195,3 +195,25 @@ def test_outside_the_limits_is_refused():
         moe.moe_decode_layer(d["x"], d["ids"], d["topk_w"], d["w"], "bf16")
     with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
         moe.moe_decode_layer(d["x"][:4], d["ids"][:4], d["topk_w"][:4], d["w"], "bf16", epilogue="swiglu")
+
+
+@pytest.mark.parametrize("wd", ["e4m3", "e2m1x2"])
+def test_nan_scale_bytes_propagate_like_the_oracle(wd):
+    # an E8M0 byte of 0xFF decodes to NaN: the C entries of the slots routed
+    # to that expert in that column turn NaN, and so do the y entries of
+    # their tokens; everything else stays finite (NaN positions must match)
+    T, k, E, N, K = 8, 4, 12, 96, 256
+    d = synth.gemm_case(T, k, E, N, K, wd, seed=81, w_std=0.5)
+    e = int(d["ids"][0, 0])
+    ws = d["w_scale"].clone()
+    ws[e, 5, 3] = 0xFF       # expert e, weight row 5, K block 3
+    ws[e, 40, :] = 0xFF      # expert e, weight row 40, every block
+    d["w_scale"] = ws
+    dd = to_dev(d)
+    C1, y1 = _fused(dd, T, k, N, wd, "none")
+    torch.cuda.synchronize()
+    rC, _, ry = _oracle(d, T, k, E, wd, "none")
+    got_c, got_y = bf16_to_f64(C1), bf16_to_f64(y1)
+    assert np.isnan(got_c[:, 5]).any() and np.isnan(got_y[0, 40])
+    assert_parity(got_c, rC, what="C")
+    assert_parity(got_y, ry, what="y")
