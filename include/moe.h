@@ -247,7 +247,8 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, moe_stream_t stream);
  *   C[s][n] = bf16( epilogue( A[t] . W_hat[e][n] + bias[e][n] ) )
  *   y[t][n] = bf16( sum_{j < top_k, ascending} topk_w[s] * C[s][n] )   (fp32)
  * with the arithmetic of moe_align -> moe_grouped_gemm (decode variant) ->
- * moe_combine, so C and y are bit-identical to those three calls. A slot
+ * moe_combine, so C and y are bit-identical to those three calls (for
+ * T * k <= 76288, see below). A slot
  * whose id lies outside [0, E) contributes 0 to y (and its C row is not
  * written).
  * args describes A (bf16 token rows: a_dtype MOE_BF16, a_row_div = top_k),
@@ -259,9 +260,14 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, moe_stream_t stream);
  * fp32 [T][top_k]; y (device) bf16 [T][n], row stride y_ld >= n; every row
  * t < T is written.
  * Limits (moe_decode_layer_fits): T <= 32, T * top_k <= 256, E <= 1024,
- * k <= 4096 and T * k <= 65536 (the activations of all tokens are held on
- * chip). Outside them, with SwiGLU or with MOE_E4M3 activations:
- * MOE_ERR_UNSUPPORTED. Other requirements as for moe_grouped_gemm.
+ * k <= 4096. The activations of all tokens are held on chip; when T * k >
+ * 76288 they are taken in two passes over halves of K (K/2 rounded up to a
+ * multiple of 32, then the rest) and each output is the sum of its passes'
+ * partial sums, so C and y may then differ
+ * from the three launches' in the last bit (both within the parity bar of
+ * the exact result). Outside the limits, with SwiGLU or with MOE_E4M3
+ * activations: MOE_ERR_UNSUPPORTED. Other requirements as for
+ * moe_grouped_gemm.
  * No workspace.
  * ---------------------------------------------------------------------- */
 moe_status moe_decode_layer(const moe_gemm_args* args, const int32_t* topk_ids, const float* topk_w,

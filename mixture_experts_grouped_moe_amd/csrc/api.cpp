@@ -304,7 +304,7 @@ int32_t moe_decode_layer_fits(int64_t num_tokens, int32_t top_k, int32_t num_exp
   return num_tokens >= 0 && num_tokens <= kDecodeMaxTokens && top_k >= 1 &&
          num_tokens * top_k <= moe::decode_layer_max_slots() && num_experts >= 1 &&
          num_experts <= moe::decode_layer_max_experts() && k >= 32 && k % 32 == 0 &&
-         k <= moe::decode_layer_max_k() && num_tokens * k <= moe::decode_layer_max_act_elems();
+         k <= moe::decode_layer_max_k();
 }
 
 moe_status moe_decode_layer(const moe_gemm_args* g, const int32_t* topk_ids, const float* topk_w, void* y,
@@ -332,10 +332,10 @@ moe_status moe_decode_layer(const moe_gemm_args* g, const int32_t* topk_ids, con
   if (y_ld < a.n) return fail(MOE_ERR_INVALID_ARGUMENT, "y_ld must be >= n");
   if (!moe_decode_layer_fits(a.num_tokens, a.top_k, a.num_experts, a.k))
     return fail(MOE_ERR_UNSUPPORTED,
-                "the decode layer takes num_tokens <= %lld, num_tokens * top_k <= %d, num_experts <= %d, "
-                "k <= %d and num_tokens * k <= %lld",
+                "the decode layer takes num_tokens <= %lld, num_tokens * top_k <= %d, num_experts <= %d "
+                "and k <= %d",
                 (long long)kDecodeMaxTokens, moe::decode_layer_max_slots(), moe::decode_layer_max_experts(),
-                moe::decode_layer_max_k(), (long long)moe::decode_layer_max_act_elems());
+                moe::decode_layer_max_k());
   if (a.num_tokens > 0 &&
       (a.a == nullptr || a.w == nullptr || topk_ids == nullptr || topk_w == nullptr || y == nullptr))
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");

@@ -35,7 +35,6 @@ struct DecodeLayerParams {
 hipError_t launch_decode_layer(const DecodeLayerParams& p, int wdt, bool bias, hipStream_t stream);
 int decode_layer_max_slots();
 int decode_layer_max_experts();
-int64_t decode_layer_max_act_elems();
 int decode_layer_max_k();
 
 }  // namespace moe

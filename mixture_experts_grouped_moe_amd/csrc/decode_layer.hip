@@ -25,8 +25,11 @@
 //    slot range and its place in the touched list, a scatter of the slots.
 //    The order of slots inside an expert does not matter: each output is
 //    computed on its own. The activation rows of all tokens are loaded while
-//    the routing runs and written to LDS (M x K bf16, at most 128 KB) once
-//    the first weight rows are on their way.
+//    the routing runs and written to LDS (M x K bf16, at most 149 KB) once
+//    the first weight rows are on their way; when they do not fit (M x K >
+//    76288, e.g. 32 tokens of 2688) they are staged in two passes over the
+//    halves of K, the weight rows are streamed in the same halves, and each
+//    output is the sum of its passes' wave sums.
 //  * Each output C[s, n] is computed with exactly the arithmetic of the decode
 //    kernel: lane l accumulates K pieces k = 8 (l + 64 i) in ascending i with
 //    v_dot2_f32_bf16 (pieces past K as zeros, so the instruction count per
@@ -34,7 +37,8 @@
 //    the wave with the butterfly's pairing, bias, epilogue, one bf16
 //    rounding. The combine sums w[t, j] * C[t k + j] over j ascending in
 //    fp32 from the bf16 values, as moe_combine does. The results are
-//    therefore bit-identical to the three launches; a slot whose expert id
+//    therefore bit-identical to the three launches (with passes, the sum is
+//    grouped by pass, so the last bit may differ); a slot whose expert id
 //    lies outside [0, E) contributes 0.
 #include <type_traits>
 
@@ -47,8 +51,10 @@ constexpr int kDlWaves = 8;                      // weight rows (output columns)
 constexpr int kDlThreads = kDlWaves * kWave;
 constexpr int kDlMaxE = 1024;
 constexpr int kDlMaxS = 256;                     // slots (tokens x top_k)
-constexpr int kDlMaxXElems = 65536;              // M x K activation elements in LDS (128 KB)
-constexpr int kDlXLoads = kDlMaxXElems / 8 / kDlThreads;  // 16-byte activation pieces per thread
+// M x K activation elements in LDS (149 KB: 28 tokens of 2688 fit); with
+// the other arrays the workgroup uses all but ~1 KB of the CU's 160 KB
+constexpr int kDlMaxXElems = 76288;
+constexpr int kDlXLoads = (kDlMaxXElems / 8 + kDlThreads - 1) / kDlThreads;  // 16-byte pieces per thread
 constexpr int kDlPass = 2048;                    // the decode kernel's K elements per pass
 constexpr int kDlPassPieces = kDlPass / 8 / kWave;  // 8-element pieces per lane per pass
 constexpr int kDlMaxPieces = 2 * kDlPassPieces;  // K <= 4096
@@ -93,12 +99,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dl_rsrc(const void* base, uint
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kDlRsrcWord3);
 }
 
-// NP: 8-element pieces per lane per weight row (4 for K <= 2048, else 8).
+// NP: 8-element pieces per lane per weight row and pass (4 for K <= 2048,
+// else 8 in one pass, or 4 in each of two passes when SPLIT).
 // PF: rows in flight per wave (the ring's depth).
-template <int WDT, bool BIAS, int NP, int PF>
+// SPLIT: the activations of all tokens do not fit in LDS at once (M x K >
+// kDlMaxXElems): K is taken in two halves of KH = K/2 rounded up to 32 elements
+// (KH <= 2048), the activations are staged and the weight rows streamed one
+// half at a time, and each output's sum is formed per half (wave sum of
+// each half, the halves added in order), so the bits may differ from the
+// three launches' in the last place.
+template <int WDT, bool BIAS, int NP, int PF, bool SPLIT>
 __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeLayerParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kDlMaxXElems];  // token rows, K elements each
-  __shared__ int32_t s_cnt[kDlMaxE];    // slots per expert, then the scatter cursor
+  // token rows, K elements each. Its last 4 KB hold the per-expert counts
+  // (then the scatter cursors) during the routing, before any row is
+  // written.
+  // (SPLIT: 32 tokens of at most kDlPass elements per pass, and room for
+  // the per-pass sums below)
+  constexpr int kXElems = SPLIT ? 32 * kDlPass : kDlMaxXElems;
+  __shared__ __attribute__((aligned(16))) uint32_t lds_x[kXElems / 2];
+  uint16_t* const xs = reinterpret_cast<uint16_t*>(lds_x);
+  int32_t* const s_cnt = reinterpret_cast<int32_t*>(&lds_x[kXElems / 2 - kDlMaxE]);
   __shared__ int32_t s_tl[kDlMaxS];     // touched experts, ascending
   __shared__ int32_t s_toff[kDlMaxS];   // first position of each touched expert's slots
   __shared__ int32_t s_tcnt[kDlMaxS];   // its slot count
@@ -106,6 +126,7 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
   __shared__ int32_t s_xoff[kDlMaxS];   // xs offset of each grouped slot's token row
   __shared__ int32_t s_id[kDlMaxS];     // routed expert of each slot (-1: none)
   __shared__ uint16_t s_c[kDlMaxS][kDlWaves];  // bf16 C of each slot, per column of the workgroup
+  __shared__ float s_acc[SPLIT ? kDlMaxS : 1][kDlWaves];  // (SPLIT) the sums of the earlier passes
   __shared__ int32_t s_part[2][kDlWaves];
   __shared__ int32_t s_ntouched;
 
@@ -115,18 +136,45 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
   const int S = p.S, E = p.E, K = p.K, top_k = p.top_k;
   const int M = S / top_k;
 
-  // ---- 1. the routing ids, then every token's activations into registers
+  // ---- 1. the routing ids, then every token's activations (of the first
+  //      pass) into registers. xs holds row t at t * XK: K elements, or a
+  //      pass of kDlPass when SPLIT (zeros past K).
   const uint32_t id_raw = __builtin_amdgcn_raw_buffer_load_b32(dl_rsrc(p.topk_ids, (uint32_t)S * 4u),
                                                                (uint32_t)tid * 4u, 0, 0);
-  const int k8 = K / 8, nx = M * k8;
+  const int XK = SPLIT ? ((K / 2 + 31) / 32) * 32 : K;  // K elements per pass (and xs row stride)
+  const int k8 = XK / 8;
+  const int npass = SPLIT ? 2 : 1;
   const __amdgpu_buffer_rsrc_t x_rsrc = dl_rsrc(p.x, p.x_bytes);
   u32x4_t xr[kDlXLoads];
+  // f(i, t, c) for this thread's pieces i: 16 bytes at row t, element 8 c
+  // (piece tid + kDlThreads * i; t and c stepped, not divided, per piece)
+  auto x_pieces = [&](auto&& f) {
+    const int dt = kDlThreads / k8, dc = kDlThreads % k8;
+    int t = tid / k8, c = tid % k8;
 #pragma unroll
-  for (int i = 0; i < kDlXLoads; ++i) {
-    const int q = tid + kDlThreads * i;
-    const uint32_t off = q < nx ? (uint32_t)(((int64_t)(q / k8) * p.x_ld + (q % k8) * 8) * 2) : kDlOOB;
-    xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, off, 0, 0));
-  }
+    for (int i = 0; i < kDlXLoads; ++i) {
+      f(i, t, c);
+      t += dt;
+      c += dc;
+      if (c >= k8) {
+        c -= k8;
+        ++t;
+      }
+    }
+  };
+  auto x_load = [&](int kbase) {
+    x_pieces([&](int i, int t, int c) {
+      const uint32_t off = (t < M && kbase + c * 8 < K) ? (uint32_t)(((int64_t)t * p.x_ld + kbase + c * 8) * 2)
+                                                        : kDlOOB;
+      xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, off, 0, 0));
+    });
+  };
+  auto x_store = [&]() {
+    x_pieces([&](int i, int t, int c) {
+      if (t < M) *reinterpret_cast<u32x4_t*>(&xs[t * XK + c * 8]) = xr[i];
+    });
+  };
+  x_load(0);
 
   // ---- 2. routing: counts, scan, scatter
   for (int e = tid; e < E; e += kDlThreads) s_cnt[e] = 0;
@@ -186,7 +234,7 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
   if (tid < S && s_id[tid] >= 0) {
     const int pos = atomicAdd(&s_cnt[s_id[tid]], 1);
     s_slot[pos] = tid;
-    s_xoff[pos] = (tid / top_k) * K;
+    s_xoff[pos] = (tid / top_k) * XK;
   }
   __syncthreads();
   const int nt = __builtin_amdgcn_readfirstlane(s_ntouched);
@@ -199,8 +247,9 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
   uint32_t sraw[PF][NP];
   uint32_t braw[PF];
   const __amdgpu_buffer_rsrc_t b_rsrc = dl_rsrc(p.bias, BIAS ? p.bias_bytes : 0u);
-  auto load_row = [&](int idx, auto slot_tag) {
+  auto load_row = [&](int idx, auto slot_tag, int kbase) {
     constexpr int R = decltype(slot_tag)::value;
+    const int kend = kbase + XK < K ? kbase + XK : K;
     const bool live = row_live && idx < nt;
     const int e = live ? __builtin_amdgcn_readfirstlane(s_tl[idx]) : 0;
     const int nn = live ? n : 0;
@@ -211,8 +260,8 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
                 (WDT != W_BF16 && live) ? p.ws_rspan : 0u);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int k = 8 * (lane + kWave * i);
-      const bool kin = k < K;
+      const int k = kbase + 8 * (lane + kWave * i);
+      const bool kin = k < kend;
       const uint32_t kb = (uint32_t)(k / 64);
       if constexpr (WDT == W_BF16) {
         const uint32_t off = kin ? kb * (uint32_t)p.w_blk + (uint32_t)(k % 64) * 2u : kDlOOB;
@@ -238,9 +287,10 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
       braw[R] = __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, boff, 0, 0);
     }
   };
-  auto compute_row = [&](int idx, auto slot_tag) {
+  auto compute_row = [&](int idx, auto slot_tag, int kbase, int pass) {
     constexpr int R = decltype(slot_tag)::value;
     if (idx >= nt) return;
+    const int kend = kbase + XK < K ? kbase + XK : K;
     // this lane's dequantised pieces of the row (zeros past K)
     bf16x8_t wv[NP];
 #pragma unroll
@@ -267,9 +317,9 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
       float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const int k = 8 * (lane + kWave * i);
-        const bool kin = k < K;
-        const int kk = kin ? k : 0;
+        const int k = kbase + 8 * (lane + kWave * i);
+        const bool kin = k < kend;
+        const int kk = kin ? k - kbase : 0;
         bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(&xs[xa + kk]);
         bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(&xs[xb + kk]);
         const bf16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -285,8 +335,23 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
           a1 = __builtin_amdgcn_fdot2_f32_bf16(x2b, w2, a1, false);
         }
       }
-      a0 = dl_wave_sum(a0) + bv;
-      a1 = dl_wave_sum(a1) + bv;
+      a0 = dl_wave_sum(a0);
+      a1 = dl_wave_sum(a1);
+      if constexpr (SPLIT) {
+        if (pass > 0) {
+          a0 = s_acc[sa][wave] + a0;
+          a1 = s_acc[sb][wave] + a1;
+        }
+        if (pass + 1 < npass) {
+          if (lane == 0) {
+            s_acc[sa][wave] = a0;
+            if (two) s_acc[sb][wave] = a1;
+          }
+          continue;
+        }
+      }
+      a0 += bv;
+      a1 += bv;
       const uint16_t ca = (uint16_t)f32_to_bf16_bits(p.relu2 ? relu2_f32(a0) : a0);
       const uint16_t cb = (uint16_t)f32_to_bf16_bits(p.relu2 ? relu2_f32(a1) : a1);
       if (lane == 0) {
@@ -295,22 +360,25 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
       }
     }
   };
-  dl_for_slots<0, PF>([&](auto r) { load_row(decltype(r)::value, r); });
-  // the activations into LDS (their loads were issued before the rows')
-#pragma unroll
-  for (int i = 0; i < kDlXLoads; ++i) {
-    const int q = tid + kDlThreads * i;
-    if (q < nx) *reinterpret_cast<u32x4_t*>(&xs[(q / k8) * K + (q % k8) * 8]) = xr[i];
-  }
-  __syncthreads();
-  // row idx lives in ring slot idx % PF; its slot is refilled with row
-  // idx + PF as soon as it has been used
-  for (int idx = 0; idx < nt; idx += PF) {
-    dl_for_slots<0, PF>([&](auto r) {
-      constexpr int R = decltype(r)::value;
-      compute_row(idx + R, r);
-      load_row(idx + R + PF, r);
-    });
+  for (int pass = 0; pass < npass; ++pass) {
+    const int kbase = pass * XK;
+    if (pass > 0) {
+      __syncthreads();  // every wave is done with the previous pass's activations
+      x_load(kbase);
+    }
+    dl_for_slots<0, PF>([&](auto r) { load_row(decltype(r)::value, r, kbase); });
+    // the activations into LDS (their loads were issued before the rows')
+    x_store();
+    __syncthreads();
+    // row idx lives in ring slot idx % PF; its slot is refilled with row
+    // idx + PF as soon as it has been used
+    for (int idx = 0; idx < nt; idx += PF) {
+      dl_for_slots<0, PF>([&](auto r) {
+        constexpr int R = decltype(r)::value;
+        compute_row(idx + R, r, kbase, pass);
+        load_row(idx + R + PF, r, kbase);
+      });
+    }
   }
   __syncthreads();
 
@@ -338,24 +406,29 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
 
 int decode_layer_max_slots() { return kDlMaxS; }
 int decode_layer_max_experts() { return kDlMaxE; }
-int64_t decode_layer_max_act_elems() { return kDlMaxXElems; }
 int decode_layer_max_k() { return kDlMaxPieces / kDlPassPieces * kDlPass; }
 
-template <int WDT, int NP>
+template <int WDT, int NP, bool SPLIT>
 static void launch_dl(const DecodeLayerParams& p, bool bias, dim3 grid, hipStream_t stream) {
   // Two rows in flight per wave (8 KB per wave at K = 2048, 64 KB per CU):
   // on a cold cache, depths 1, 2, 3, 4, 6 and 8 gave about 134, 121, 124, 123, 123
   // and 124 us at M = 28 (K = 2048) and 172, 152, 154, 160 us at M = 24,
   // K = 2688 (depths 1-4); deeper rings only lengthen the memory queues.
-  constexpr int PF = 2;
-  if (bias) hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, true, NP, PF>), grid, dim3(kDlThreads), 0, stream, p);
-  else hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, false, NP, PF>), grid, dim3(kDlThreads), 0, stream, p);
+  // With two passes each row is half as long, so twice as many rows are
+  // kept in flight.
+  constexpr int PF = SPLIT ? 4 : 2;
+  if (bias)
+    hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, true, NP, PF, SPLIT>), grid, dim3(kDlThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, false, NP, PF, SPLIT>), grid, dim3(kDlThreads), 0, stream, p);
 }
 
 template <int WDT>
 static void launch_dl_wdt(const DecodeLayerParams& p, bool bias, dim3 grid, hipStream_t stream) {
-  if (p.K <= kDlPass) launch_dl<WDT, kDlPassPieces>(p, bias, grid, stream);
-  else launch_dl<WDT, kDlMaxPieces>(p, bias, grid, stream);
+  const int64_t act = (int64_t)(p.S / p.top_k) * p.K;  // activation elements of all tokens
+  if (p.K <= kDlPass) launch_dl<WDT, kDlPassPieces, false>(p, bias, grid, stream);
+  else if (act <= kDlMaxXElems) launch_dl<WDT, kDlMaxPieces, false>(p, bias, grid, stream);
+  else launch_dl<WDT, kDlPassPieces, true>(p, bias, grid, stream);
 }
 
 hipError_t launch_decode_layer(const DecodeLayerParams& p, int wdt, bool bias, hipStream_t stream) {

@@ -5,7 +5,10 @@ on the same inputs, and both match the float64 oracle: every weight encoding,
 with and without bias and the relu2 epilogue, K short of a pass and across
 two passes, N not a multiple of 8, skewed and repeated routing, ids outside
 [0, E), NaN scale bytes, and the launch's limits (256 slots, 1024 experts,
-K = 4096, M x K = 65536)."""
+K = 4096). Where the activations of all tokens exceed 76288 elements they
+are staged in two passes over the halves of K and each output is summed per
+pass; those cases are checked against the oracle, and against the three
+launches within the parity bar."""
 
 import numpy as np
 import pytest
@@ -64,7 +67,8 @@ def _same_bits(a, b, what):
 CASES = [
     # T, k, E, N, K, w_dtype, bias, epilogue
     (5, 6, 16, 200, 352, "bf16", True, "relu2"),      # K short of one 2048 pass
-    (24, 6, 32, 264, 2688, "bf16", True, "relu2"),    # the Nemotron hidden size: two passes, M x K = 64512
+    (24, 6, 32, 264, 2688, "bf16", True, "relu2"),    # the Nemotron hidden size: two 2048-element passes
+    (28, 6, 32, 264, 2688, "e4m3", True, "none"),     # M x K = 75264, near the on-chip maximum (76288)
     (32, 8, 64, 256, 2048, "bf16", False, "none"),    # 256 slots
     (16, 4, 32, 256, 4096, "e4m3", True, "none"),     # K = 4096 and M x K = 65536
     (28, 4, 16, 256, 2080, "e4m3", False, "relu2"),
@@ -189,8 +193,8 @@ def test_repeated_calls_identical_and_empty():
 
 def test_outside_the_limits_is_refused():
     moe = _moe()
-    assert not moe.moe_decode_layer_fits(25, 6, 128, 2688)
-    d = to_dev(synth.gemm_case(25, 6, 8, 64, 2688, "bf16", seed=71))
+    assert not moe.moe_decode_layer_fits(4, 6, 8, 4128)
+    d = to_dev(synth.gemm_case(4, 6, 8, 64, 4128, "bf16", seed=71))
     with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
         moe.moe_decode_layer(d["x"], d["ids"], d["topk_w"], d["w"], "bf16")
     with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
@@ -217,3 +221,56 @@ def test_nan_scale_bytes_propagate_like_the_oracle(wd):
     assert np.isnan(got_c[:, 5]).any() and np.isnan(got_y[0, 40])
     assert_parity(got_c, rC, what="C")
     assert_parity(got_y, ry, what="y")
+
+
+SPLIT_CASES = [
+    # T, k, E, N, K, w_dtype, bias, epilogue: M x K > 76288, two passes over the halves of K
+    (29, 6, 32, 264, 2688, "bf16", True, "relu2"),     # the Nemotron hidden size past 28 tokens
+    (32, 8, 64, 256, 4096, "e4m3", True, "none"),      # the largest: 256 slots, K = 4096
+    (32, 6, 16, 200, 2688, "e2m1x2", False, "none"),   # halves of 1344
+    (32, 2, 8, 72, 2400, "bf16", False, "relu2"),      # unequal halves: 1216 + 1184
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "T{}k{}E{}N{}K{}{}{}{}".format(
+    *c[:6], "b" if c[6] else "", c[7]))
+def test_two_pass_layer_against_oracle_and_three_launches(case):
+    T, k, E, N, K, wd, bias, ep = case
+    moe = _moe()
+    assert moe.moe_decode_layer_fits(T, k, E, K) and T * K > 76288
+    d = synth.gemm_case(T, k, E, N, K, wd, seed=T * 11 + N + K, bias=bias, w_std=0.5)
+    dd = to_dev(d)
+    C3, y3 = _unfused(dd, T, k, E, N, wd, ep)
+    C1, y1 = _fused(dd, T, k, N, wd, ep)
+    torch.cuda.synchronize()
+    rC, routed, ry = _oracle(d, T, k, E, wd, ep)
+    assert routed.all()
+    assert_parity(bf16_to_f64(C1), rC, what=f"C {case}")
+    assert_parity(bf16_to_f64(y1), ry, what=f"y {case}")
+    # the three launches sum each output over all of K at once: equal within
+    # the bar (the per-pass grouping may move a last bit)
+    assert_parity(bf16_to_f64(C1), bf16_to_f64(C3), what=f"C vs three launches {case}")
+    assert_parity(bf16_to_f64(y1), bf16_to_f64(y3), what=f"y vs three launches {case}")
+
+
+@pytest.mark.parametrize("M", [28, 32])
+def test_nemotron_up_projection_at_28_and_32_tokens(M):
+    # the page's recipe shape (hidden 2688, N 1856, E 128, top-6): 28 tokens
+    # are the most whose activations fit on chip at once (the bits of the
+    # three launches), 32 take two passes (within the bar); the oracle
+    # checks 64 sampled columns
+    d = synth.nemotron_layer(M, device="cuda", bias=True)
+    dd = {"x": d["x"], "ids": d["ids"], "topk_w": d["topk_w"], "w": d["w1"], "w_scale": None, "bias": d["b1"]}
+    C3, y3 = _unfused(dd, M, 6, 128, 1856, "bf16", "relu2")
+    C1, y1 = _fused(dd, M, 6, 1856, "bf16", "relu2")
+    torch.cuda.synchronize()
+    if M == 28:
+        _same_bits(C1, C3, "C")
+        _same_bits(y1, y3, "y")
+    else:
+        assert_parity(bf16_to_f64(y1), bf16_to_f64(y3), what="y vs three launches")
+    cols = np.sort(np.random.default_rng(28).choice(1856, 64, replace=False))
+    sub = dict(dd, w=d["w1"][:, torch.from_numpy(cols).cuda(), :].contiguous(),
+               bias=d["b1"][:, torch.from_numpy(cols).cuda()].contiguous())
+    rC, _, ry = _oracle(sub, M, 6, 128, "bf16", "relu2")
+    assert_parity(bf16_to_f64(C1)[:, cols], rC, what="C")

@@ -140,7 +140,7 @@ def _layer_case(seed):
     rng = np.random.default_rng(3000 + seed)
     wd = ("e2m1x2", "e4m3", "bf16")[seed % 3]
     K = 32 * int(rng.integers(1, 129))                 # up to 4096
-    T = int(rng.integers(0, min(32, 65536 // K) + 1))  # activations fit on chip
+    T = int(rng.integers(0, 33))                       # two passes over K when T x K > 76288
     E = int(rng.integers(1, 300))
     k = int(rng.integers(1, min(E, 8) + 1))
     N = int(rng.integers(1, 700))
@@ -148,7 +148,7 @@ def _layer_case(seed):
                 bias=bool(rng.integers(0, 2)), packed=bool(rng.integers(0, 2)))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(17))
 def test_decode_layer_random_shapes(seed):
     # the fused decode layer (routing, GEMM, combine in one launch) on random
     # shapes within its limits: y and C against the oracle

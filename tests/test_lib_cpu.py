@@ -201,8 +201,8 @@ def test_grouped_gemm_rejects(no_device):
 def test_decode_layer_fits():
     f = moe.moe_decode_layer_fits
     assert f(28, 6, 128, 2048) and f(32, 8, 1024, 2048) and f(0, 6, 128, 2048)
-    assert f(24, 6, 128, 2688) and not f(25, 6, 128, 2688)   # M x K <= 65536
-    assert f(16, 6, 128, 4096) and not f(1, 6, 128, 4128)    # K <= 4096
+    assert f(24, 6, 128, 2688) and f(28, 6, 128, 2688)       # one pass, two passes of K
+    assert f(32, 8, 128, 4096) and not f(1, 6, 128, 4128)    # K <= 4096
     assert not f(33, 1, 128, 256)                            # beyond the decode bucket
     assert not f(32, 9, 128, 256)                            # 288 slots
     assert not f(1, 6, 1025, 256)
@@ -219,7 +219,6 @@ def _dl(ids=FAKE, tw=FAKE, y=FAKE, y_ld=None, **kw):
 def test_decode_layer_rejects(no_device):
     assert L.moe_decode_layer(None, FAKE, FAKE, FAKE, 256, None) == INVALID
     assert _dl(T=33) == UNSUPPORTED                  # beyond the decode bucket
-    assert _dl(T=32, K=4096) == UNSUPPORTED          # M x K > 65536
     assert _dl(K=4128) == UNSUPPORTED                # K > 4096
     assert _dl(E=1025) == UNSUPPORTED
     assert _dl(T=32, k=9, E=16) == UNSUPPORTED       # 288 slots
