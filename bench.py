@@ -22,7 +22,8 @@ weights, activations, ids and routing weights in, y out) over their summed
 event time (GB/s); `roofline` = the same for the layer kernel, the step's
 only launch. `cold.per_m` gives median / p10 / p90 per M for both paths;
 `cold.three_launch` the three-launch figures and the decode GEMM's own
-roofline. `warm` holds both paths warm (graph-replayed steps on a cycled set
+roofline; `cold_k2688` the fused layer on the same protocol at the page
+recipe's hidden size, K = 2688. `warm` holds both paths warm (graph-replayed steps on a cycled set
 of routings, and back-to-back launches of the layer kernel and of the
 decode GEMM).
 `large_m` holds the large-M half of the metric: the W4A16 gate+up GEMM (and
@@ -1124,6 +1125,75 @@ def decode_cold(torch, moe, dev, stream, args, clock):
             "per_m": out, "calls": n}
 
 
+def decode_cold_k2688(torch, moe, dev, stream, args, clock):
+    """The extra decode row at the page recipe's hidden size (K = 2688, the
+    Nemotron shape; E=128, N=1856, top-6, bf16), through the fused layer
+    alone, with the cold-cache protocol of decode_cold: per M, median / p10 /
+    p90 of the call and its fraction of 8 TB/s. 28 tokens of 2688 are the
+    most whose activations the layer holds on chip at once."""
+    import numpy as np
+    import synth
+    E, N, K, k = 128, 1856, 2688, 6
+    w = synth.bf16_normal((E, N, K), 0.02, 1006, "w1", dev)
+    n_steps = args.warmup + args.steps
+    calls = {}
+    for M in DECODE_MS:
+        lst = []
+        for r in range(n_steps):
+            x_src = synth.bf16_normal((M, K), 1.0, 1006, f"cold-x{M}c{r}", dev)
+            ids_src, tw_src = synth.softmax_topk_routing(M, E, k, 1006, f"cold-route{M}c{r}", dev)
+            x, ids, tw = torch.empty_like(x_src), torch.empty_like(ids_src), torch.empty_like(tw_src)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            touched = len(np.unique(ids_src.cpu().numpy()))
+            layer, _ = moe.moe_decode_layer_prepare(x, ids, tw, w, "bf16", out=y, stream=stream)
+            lst.append(dict(srcs=((x, x_src), (ids, ids_src), (tw, tw_src)), layer=layer, touched=touched,
+                            step_bytes=touched * N * K * 2 + M * K * 2 + M * k * 8 + M * N * 2))
+        calls[M] = lst
+    flush_src = torch.ones(1 << 29, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    spin = spin_cycles(torch, stream, SPIN_MS)
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in DECODE_MS] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    timed = []
+    clock.region = "decode_cold_k2688"
+    gc.collect()
+    gc.disable()
+    with torch.cuda.stream(stream):
+        for step in range(n_steps):
+            torch.cuda._sleep(spin)
+            for i, M in enumerate(DECODE_MS):
+                c = calls[M][step]
+                flush_dst.copy_(flush_src)
+                for dst, src in c["srcs"]:
+                    dst.copy_(src)
+                ev = events[step][i]
+                ev[0].record(stream)
+                c["layer"]()
+                ev[1].record(stream)
+                if step >= args.warmup:
+                    timed.append((M, ev, c))
+            stream.synchronize()
+    gc.enable()
+    torch.cuda.synchronize()
+    clock.region = None
+    per_m = {M: ([], []) for M in DECODE_MS}
+    tot_b = tot_us = 0.0
+    for M, ev, c in timed:
+        us = ev[0].elapsed_time(ev[1]) * 1e3
+        per_m[M][0].append(us)
+        per_m[M][1].append(c["step_bytes"] / us / 1e3 / PEAK_HBM_GBS)
+        tot_b += c["step_bytes"]
+        tot_us += us
+    del calls, flush_src, flush_dst, w
+    torch.cuda.empty_cache()
+    return {"workload": "decode bf16 MoE at the recipe's hidden size, E=128 N=1856 K=2688 top-6, fused layer",
+            "GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 3),
+            "hbm_frac": round(tot_b / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "per_m": {str(M): {"layer_us": stats(per_m[M][0]),
+                               "layer_hbm_frac_median": round(float(np.median(per_m[M][1])), 4)}
+                      for M in DECODE_MS}}
+
+
 def measure(wl, torch, stream, args, nv, clock, region):
     """Warm measurement of a workload: K graph-replayed steps (W warmup), then
     the dominant kernel's launch durations from HIP events on its stream, one
@@ -1343,6 +1413,8 @@ def decode_main(torch, moe, dev, stream, args, clock):
         three["gemm_roofline"] = {"bound": "hbm", "achieved": three["gemm_GBps"], "peak": PEAK_HBM_GBS,
                                   "unit": "GB/s", "frac": round(three["gemm_GBps"] / PEAK_HBM_GBS, 4),
                                   "traffic": load_traffic("decode", None), "kernel": "moe_decode_kernel"}
+        if args.phase == "both":  # (the profiled --phase cold runs time the headline's launches only)
+            line["cold_k2688"] = decode_cold_k2688(torch, moe, dev, stream, args, clock)
         line["cold"] = {"per_m": cold["per_m"], "calls_per_path": cold["calls"],
                         "three_launch": three, "clock": clock.summary("decode_cold"),
                         "ms_per_step_note": "device time of the step's launches (events); the copies that "
