@@ -16,15 +16,24 @@
 //    cross-workgroup step and no scratch memory. Each wave streams its row of
 //    every touched expert in ascending expert order with non-temporal loads,
 //    two experts ahead; every expert's weights are read once.
-//  * Every global load before the combine is a buffer load whose
-//    out-of-range pieces read as zero, so none sits under a branch: the
-//    compiler can then wait for exactly the oldest row of the prefetch ring
-//    (memory counters retire in order) instead of for all loads in flight.
-//  * The routing is done by every workgroup in LDS from the at most 256 ids:
-//    per-expert counts (LDS atomics), one scan giving each touched expert its
-//    slot range and its place in the touched list, a scatter of the slots.
-//    The order of slots inside an expert does not matter: each output is
-//    computed on its own. The activation rows of all tokens are loaded while
+//  * Every weight, scale and bias load is a buffer load whose out-of-range
+//    pieces read as zero, so none sits under a branch: the compiler can then
+//    wait for exactly the oldest row of the prefetch ring (memory counters
+//    retire in order) instead of for all loads in flight. The activation
+//    loads stop at the last piece the token rows hold (a workgroup-uniform
+//    bound); the first wait on the ids then covers them too, which costs
+//    nothing, as the first weight rows wait for the routing anyway.
+//  * The routing is done by every workgroup from the at most 256 ids. Up to
+//    8 slots (one token's top-k), every wave does it on its own in registers
+//    (lane s holds slot s: its rank among the routed slots by (expert,
+//    slot), its expert's slot count and its place in the touched list, each
+//    counted over the other lanes; the tables are then read with ballots),
+//    so no barrier stands between the ids and the first weight rows; the
+//    count loops take a few hundred cycles per slot, so beyond that it is
+//    done in LDS: per-expert counts (LDS atomics), one scan giving each
+//    touched expert its slot range and its place in the touched list, a
+//    scatter of the slots. The order of slots inside an expert does not
+//    matter: each output is computed on its own. The activation rows of all tokens are loaded while
 //    the routing runs and written to LDS (M x K bf16, at most 149 KB) once
 //    the first weight rows are on their way; when they do not fit (M x K >
 //    76288, e.g. 32 tokens of 2688) they are staged in two passes over the
@@ -51,6 +60,7 @@ constexpr int kDlWaves = 8;                      // weight rows (output columns)
 constexpr int kDlThreads = kDlWaves * kWave;
 constexpr int kDlMaxE = 1024;
 constexpr int kDlMaxS = 256;                     // slots (tokens x top_k)
+constexpr int kDlRegSlots = 8;                   // routed in registers up to this many slots
 // M x K activation elements in LDS (149 KB: 28 tokens of 2688 fit); with
 // the other arrays the workgroup uses all but ~1 KB of the CU's 160 KB
 constexpr int kDlMaxXElems = 76288;
@@ -108,7 +118,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dl_rsrc(const void* base, uint
 // half at a time, and each output's sum is formed per half (wave sum of
 // each half, the halves added in order), so the bits may differ from the
 // three launches' in the last place.
-template <int WDT, bool BIAS, int NP, int PF, bool SPLIT>
+// RR: at most kDlRegSlots slots, routed in registers by every wave (no LDS
+// tables).
+template <int WDT, bool BIAS, int NP, int PF, bool SPLIT, bool RR>
 __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeLayerParams p) {
   // token rows, K elements each. Its last 4 KB hold the per-expert counts
   // (then the scatter cursors) during the routing, before any row is
@@ -139,12 +151,15 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
   // ---- 1. the routing ids, then every token's activations (of the first
   //      pass) into registers. xs holds row t at t * XK: K elements, or a
   //      pass of kDlPass when SPLIT (zeros past K).
+  // (RR: every wave reads all ids, lane s slot s; else thread s slot s)
   const uint32_t id_raw = __builtin_amdgcn_raw_buffer_load_b32(dl_rsrc(p.topk_ids, (uint32_t)S * 4u),
-                                                               (uint32_t)tid * 4u, 0, 0);
+                                                               (uint32_t)(RR ? lane : tid) * 4u, 0, 0);
   const int XK = SPLIT ? ((K / 2 + 31) / 32) * 32 : K;  // K elements per pass (and xs row stride)
   const int k8 = XK / 8;
   const int npass = SPLIT ? 2 : 1;
   const __amdgpu_buffer_rsrc_t x_rsrc = dl_rsrc(p.x, p.x_bytes);
+  // pieces per thread that hold activations (the rest would read zeros)
+  const int xl = (M * k8 + kDlThreads - 1) / kDlThreads;
   u32x4_t xr[kDlXLoads];
   // f(i, t, c) for this thread's pieces i: 16 bytes at row t, element 8 c
   // (piece tid + kDlThreads * i; t and c stepped, not divided, per piece)
@@ -164,6 +179,7 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
   };
   auto x_load = [&](int kbase) {
     x_pieces([&](int i, int t, int c) {
+      if (i >= xl) return;
       const uint32_t off = (t < M && kbase + c * 8 < K) ? (uint32_t)(((int64_t)t * p.x_ld + kbase + c * 8) * 2)
                                                         : kDlOOB;
       xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, off, 0, 0));
@@ -171,73 +187,128 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
   };
   auto x_store = [&]() {
     x_pieces([&](int i, int t, int c) {
-      if (t < M) *reinterpret_cast<u32x4_t*>(&xs[t * XK + c * 8]) = xr[i];
+      if (i < xl && t < M) *reinterpret_cast<u32x4_t*>(&xs[t * XK + c * 8]) = xr[i];
     });
   };
   x_load(0);
 
-  // ---- 2. routing: counts, scan, scatter
-  for (int e = tid; e < E; e += kDlThreads) s_cnt[e] = 0;
-  __syncthreads();
-  if (tid < S) {
-    const int id = (int)id_raw;
-    const int r = (id >= 0 && id < E) ? id : -1;  // ids outside [0, E) are not routed
-    s_id[tid] = r;
-    if (r >= 0) atomicAdd(&s_cnt[r], 1);
-  }
-  __syncthreads();
-  // experts 2 tid, 2 tid + 1: exclusive scans of the slot counts and of the
-  // touched flags over all experts (E <= 1024 = 2 x 512)
-  int c0 = 0, c1 = 0;
-  if (2 * tid < E) c0 = s_cnt[2 * tid];
-  if (2 * tid + 1 < E) c1 = s_cnt[2 * tid + 1];
-  const int csum = c0 + c1, tsum = (c0 > 0) + (c1 > 0);
-  int ci = csum, ti = tsum;
+  // ---- 2. routing
+  // RR: lane s (s < S) holds slot s: its expert (-1: not routed), its
+  // position among the routed slots ordered by (expert, slot), its expert's
+  // slot count, whether it is that expert's first slot, and then the
+  // expert's place among the touched experts (ascending)
+  int rr_e = -1, rr_pos = 0, rr_cnt = 0, rr_ti = 0, rr_xoff = 0;
+  bool rr_first = false;
+  int nt;
+  if constexpr (RR) {
+    if (lane < S) {
+      const int id = (int)id_raw;
+      rr_e = (id >= 0 && id < E) ? id : -1;
+    }
+    int before = 0;
+    for (int j = 0; j < S; ++j) {
+      const int ej = __builtin_amdgcn_readlane(rr_e, j);
+      const bool same = ej == rr_e;
+      rr_pos += (ej >= 0 && (ej < rr_e || (same && j < lane))) ? 1 : 0;
+      rr_cnt += same ? 1 : 0;
+      before += (same && j < lane) ? 1 : 0;
+    }
+    rr_first = rr_e >= 0 && before == 0;
+    const uint64_t firsts = __builtin_amdgcn_ballot_w64(rr_first);
+    for (uint64_t m = firsts; m != 0; m &= m - 1)
+      rr_ti += (__builtin_amdgcn_readlane(rr_e, (int)__builtin_ctzll(m)) < rr_e) ? 1 : 0;
+    nt = __builtin_popcountll(firsts);
+    rr_xoff = (lane / top_k) * XK;
+    if (wave == 0 && lane < S) s_id[lane] = rr_e;  // for the combine (barriers follow)
+  } else {
+    // counts, scan, scatter
+    for (int e = tid; e < E; e += kDlThreads) s_cnt[e] = 0;
+    __syncthreads();
+    if (tid < S) {
+      const int id = (int)id_raw;
+      const int r = (id >= 0 && id < E) ? id : -1;  // ids outside [0, E) are not routed
+      s_id[tid] = r;
+      if (r >= 0) atomicAdd(&s_cnt[r], 1);
+    }
+    __syncthreads();
+    // experts 2 tid, 2 tid + 1: exclusive scans of the slot counts and of the
+    // touched flags over all experts (E <= 1024 = 2 x 512)
+    int c0 = 0, c1 = 0;
+    if (2 * tid < E) c0 = s_cnt[2 * tid];
+    if (2 * tid + 1 < E) c1 = s_cnt[2 * tid + 1];
+    const int csum = c0 + c1, tsum = (c0 > 0) + (c1 > 0);
+    int ci = csum, ti = tsum;
 #pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int a = __shfl_up(ci, d, kWave), b = __shfl_up(ti, d, kWave);
-    if (lane >= d) {
-      ci += a;
-      ti += b;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int a = __shfl_up(ci, d, kWave), b = __shfl_up(ti, d, kWave);
+      if (lane >= d) {
+        ci += a;
+        ti += b;
+      }
     }
-  }
-  if (lane == kWave - 1) {
-    s_part[0][wave] = ci;
-    s_part[1][wave] = ti;
-  }
-  __syncthreads();
-  int cbase = 0, tbase = 0, ttot = 0;
-  for (int w = 0; w < kDlWaves; ++w) {
-    if (w < wave) {
-      cbase += s_part[0][w];
-      tbase += s_part[1][w];
+    if (lane == kWave - 1) {
+      s_part[0][wave] = ci;
+      s_part[1][wave] = ti;
     }
-    ttot += s_part[1][w];
+    __syncthreads();
+    int cbase = 0, tbase = 0, ttot = 0;
+    for (int w = 0; w < kDlWaves; ++w) {
+      if (w < wave) {
+        cbase += s_part[0][w];
+        tbase += s_part[1][w];
+      }
+      ttot += s_part[1][w];
+    }
+    int co = cbase + ci - csum, to = tbase + ti - tsum;
+    if (c0 > 0) {
+      s_tl[to] = 2 * tid;
+      s_toff[to] = co;
+      s_tcnt[to] = c0;
+      ++to;
+    }
+    if (2 * tid < E) s_cnt[2 * tid] = co;  // the cursor of the scatter
+    co += c0;
+    if (c1 > 0) {
+      s_tl[to] = 2 * tid + 1;
+      s_toff[to] = co;
+      s_tcnt[to] = c1;
+    }
+    if (2 * tid + 1 < E) s_cnt[2 * tid + 1] = co;
+    if (tid == 0) s_ntouched = ttot;
+    __syncthreads();
+    if (tid < S && s_id[tid] >= 0) {
+      const int pos = atomicAdd(&s_cnt[s_id[tid]], 1);
+      s_slot[pos] = tid;
+      s_xoff[pos] = (tid / top_k) * XK;
+    }
+    __syncthreads();
+    nt = __builtin_amdgcn_readfirstlane(s_ntouched);
   }
-  int co = cbase + ci - csum, to = tbase + ti - tsum;
-  if (c0 > 0) {
-    s_tl[to] = 2 * tid;
-    s_toff[to] = co;
-    s_tcnt[to] = c0;
-    ++to;
-  }
-  if (2 * tid < E) s_cnt[2 * tid] = co;  // the cursor of the scatter
-  co += c0;
-  if (c1 > 0) {
-    s_tl[to] = 2 * tid + 1;
-    s_toff[to] = co;
-    s_tcnt[to] = c1;
-  }
-  if (2 * tid + 1 < E) s_cnt[2 * tid + 1] = co;
-  if (tid == 0) s_ntouched = ttot;
-  __syncthreads();
-  if (tid < S && s_id[tid] >= 0) {
-    const int pos = atomicAdd(&s_cnt[s_id[tid]], 1);
-    s_slot[pos] = tid;
-    s_xoff[pos] = (tid / top_k) * XK;
-  }
-  __syncthreads();
-  const int nt = __builtin_amdgcn_readfirstlane(s_ntouched);
+  // touched expert idx < nt: its id, its slots' first position, their count
+  auto touched = [&](int idx, int& e, int& o, int& c) {
+    if constexpr (RR) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(rr_first && rr_ti == idx);
+      const int l = m != 0 ? (int)__builtin_ctzll(m) : 0;
+      e = __builtin_amdgcn_readlane(rr_e, l);
+      o = __builtin_amdgcn_readlane(rr_pos, l);
+      c = __builtin_amdgcn_readlane(rr_cnt, l);
+    } else {
+      e = __builtin_amdgcn_readfirstlane(s_tl[idx]);
+      o = __builtin_amdgcn_readfirstlane(s_toff[idx]);
+      c = __builtin_amdgcn_readfirstlane(s_tcnt[idx]);
+    }
+  };
+  // the slot at grouped position q and the xs offset of its token's row
+  auto slot_at = [&](int q, int& sl, int& xo) {
+    if constexpr (RR) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(rr_e >= 0 && rr_pos == q);
+      sl = m != 0 ? (int)__builtin_ctzll(m) : 0;
+      xo = __builtin_amdgcn_readlane(rr_xoff, sl);
+    } else {
+      sl = __builtin_amdgcn_readfirstlane(s_slot[q]);
+      xo = __builtin_amdgcn_readfirstlane(s_xoff[q]);
+    }
+  };
 
   // ---- 3. this wave's weight row of every touched expert, through a ring
   const int n = blockIdx.x * kDlWaves + wave;
@@ -251,7 +322,8 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
     constexpr int R = decltype(slot_tag)::value;
     const int kend = kbase + XK < K ? kbase + XK : K;
     const bool live = row_live && idx < nt;
-    const int e = live ? __builtin_amdgcn_readfirstlane(s_tl[idx]) : 0;
+    int e = 0, o_unused, c_unused;
+    if (live) touched(idx, e, o_unused, c_unused);
     const int nn = live ? n : 0;
     const __amdgpu_buffer_rsrc_t w_rsrc =
         dl_rsrc(p.w + (int64_t)e * p.w_stride_e + (int64_t)nn * p.w_row, live ? p.w_rspan : 0u);
@@ -304,16 +376,15 @@ __global__ __launch_bounds__(kDlThreads, 1) void moe_decode_layer_kernel(DecodeL
       }
     }
     const float bv = BIAS ? bf16_bits_to_f32(braw[R] & 0xffffu) : 0.0f;
-    const int o = __builtin_amdgcn_readfirstlane(s_toff[idx]);
-    const int cnt = __builtin_amdgcn_readfirstlane(s_tcnt[idx]);
+    int e_unused, o, cnt;
+    touched(idx, e_unused, o, cnt);
     // two slots at a time: two independent accumulation chains
     for (int j = 0; j < cnt; j += 2) {
       const bool two = j + 1 < cnt;
       const int jb = two ? j + 1 : j;
-      const int sa = __builtin_amdgcn_readfirstlane(s_slot[o + j]);
-      const int sb = __builtin_amdgcn_readfirstlane(s_slot[o + jb]);
-      const int xa = __builtin_amdgcn_readfirstlane(s_xoff[o + j]);
-      const int xb = __builtin_amdgcn_readfirstlane(s_xoff[o + jb]);
+      int sa, sb, xa, xb;
+      slot_at(o + j, sa, xa);
+      slot_at(o + jb, sb, xb);
       float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
@@ -408,7 +479,7 @@ int decode_layer_max_slots() { return kDlMaxS; }
 int decode_layer_max_experts() { return kDlMaxE; }
 int decode_layer_max_k() { return kDlMaxPieces / kDlPassPieces * kDlPass; }
 
-template <int WDT, int NP, bool SPLIT>
+template <int WDT, int NP, bool SPLIT, bool RR>
 static void launch_dl(const DecodeLayerParams& p, bool bias, dim3 grid, hipStream_t stream) {
   // Two rows in flight per wave (8 KB per wave at K = 2048, 64 KB per CU):
   // on a cold cache, depths 1, 2, 3, 4, 6 and 8 gave about 134, 121, 124, 123, 123
@@ -418,17 +489,24 @@ static void launch_dl(const DecodeLayerParams& p, bool bias, dim3 grid, hipStrea
   // kept in flight.
   constexpr int PF = SPLIT ? 4 : 2;
   if (bias)
-    hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, true, NP, PF, SPLIT>), grid, dim3(kDlThreads), 0, stream, p);
+    hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, true, NP, PF, SPLIT, RR>), grid, dim3(kDlThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, false, NP, PF, SPLIT>), grid, dim3(kDlThreads), 0, stream, p);
+    hipLaunchKernelGGL((moe_decode_layer_kernel<WDT, false, NP, PF, SPLIT, RR>), grid, dim3(kDlThreads), 0, stream, p);
 }
 
 template <int WDT>
 static void launch_dl_wdt(const DecodeLayerParams& p, bool bias, dim3 grid, hipStream_t stream) {
   const int64_t act = (int64_t)(p.S / p.top_k) * p.K;  // activation elements of all tokens
-  if (p.K <= kDlPass) launch_dl<WDT, kDlPassPieces, false>(p, bias, grid, stream);
-  else if (act <= kDlMaxXElems) launch_dl<WDT, kDlMaxPieces, false>(p, bias, grid, stream);
-  else launch_dl<WDT, kDlPassPieces, true>(p, bias, grid, stream);
+  const bool rr = p.S <= kDlRegSlots;  // routed in registers
+  if (p.K <= kDlPass) {
+    if (rr) launch_dl<WDT, kDlPassPieces, false, true>(p, bias, grid, stream);
+    else launch_dl<WDT, kDlPassPieces, false, false>(p, bias, grid, stream);
+  } else if (act <= kDlMaxXElems) {
+    if (rr) launch_dl<WDT, kDlMaxPieces, false, true>(p, bias, grid, stream);
+    else launch_dl<WDT, kDlMaxPieces, false, false>(p, bias, grid, stream);
+  } else {
+    launch_dl<WDT, kDlPassPieces, true, false>(p, bias, grid, stream);
+  }
 }
 
 hipError_t launch_decode_layer(const DecodeLayerParams& p, int wdt, bool bias, hipStream_t stream) {

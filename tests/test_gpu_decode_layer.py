@@ -4,7 +4,8 @@ C equal, bit for bit, those of moe_align -> moe_grouped_gemm -> moe_combine
 on the same inputs, and both match the float64 oracle: every weight encoding,
 with and without bias and the relu2 epilogue, K short of a pass and across
 two passes, N not a multiple of 8, skewed and repeated routing, ids outside
-[0, E), NaN scale bytes, and the launch's limits (256 slots, 1024 experts,
+[0, E), single-token calls (up to 8 slots, routed in registers), NaN scale
+bytes, and the launch's limits (256 slots, 1024 experts,
 K = 4096). Where the activations of all tokens exceed 76288 elements they
 are staged in two passes over the halves of K and each output is summed per
 pass; those cases are checked against the oracle, and against the three
@@ -174,6 +175,43 @@ def test_ids_outside_the_experts_contribute_zero():
     assert np.isnan(got[~routed]).all()          # rows of unrouted slots are not written
     assert_parity(got[routed], rC[routed], what="C")
     assert_parity(bf16_to_f64(y1), ry, what="y")
+
+
+SMALL_ROUTES = [
+    # T, k, K, ids (one row per token), w_dtype, bias, epilogue; E = 8. Up
+    # to 8 slots every wave routes in registers; 9 and more go through LDS.
+    (1, 8, 2688, [[5, 1, 7, 0, 3, 2, 6, 4]], "bf16", True, "relu2"),    # 8 slots, all experts
+    (1, 6, 1024, [[3, 3, 3, 3, 3, 3]], "e4m3", False, "none"),           # one expert named six times
+    (2, 4, 2688, [[2, 0, 2, 1], [1, 2, 0, 0]], "e2m1x2", True, "none"),  # shared and repeated across tokens
+    (1, 6, 2048, [[4, -1, 9, 1 << 30, 0, 9]], "bf16", True, "none"),     # ids outside [0, E) among repeats
+    (1, 4, 4096, [[-1, 8, 8, -5]], "bf16", False, "none"),               # no slot routed
+    (1, 1, 96, [[7]], "e4m3", True, "relu2"),                            # top-1, K short of a lane's piece
+    (2, 4, 512, [[6, 6, 1, 0], [6, 1, 0, 1]], "e2m1x2", False, "none"),
+    (3, 3, 2688, [[1, 0, 1], [7, 7, 7], [0, 2, 4]], "bf16", False, "relu2"),  # 9 slots: routed in LDS
+]
+
+
+@pytest.mark.parametrize("case", SMALL_ROUTES, ids=lambda c: "T{}k{}K{}{}".format(c[0], c[1], c[2], c[4]))
+def test_few_slots_routed_in_registers(case):
+    T, k, K, ids, wd, bias, ep = case
+    E, N = 8, 256
+    d = synth.gemm_case(T, k, E, N, K, wd, seed=T * 13 + k, bias=bias, w_std=0.5)
+    d["ids"] = torch.tensor(ids, dtype=torch.int32)
+    dd = to_dev(d)
+    C1, y1 = _fused(dd, T, k, N, wd, ep)
+    torch.cuda.synchronize()
+    rC, routed, ry = _oracle(d, T, k, E, wd, ep)
+    got = bf16_to_f64(C1)
+    assert np.isnan(got[~routed]).all()          # rows of unrouted slots are not written
+    assert_parity(got[routed], rC[routed], what=f"C {case}")
+    assert_parity(bf16_to_f64(y1), ry, what=f"y {case}")
+    if routed.all():
+        C3, y3 = _unfused(dd, T, k, E, N, wd, ep)
+        torch.cuda.synchronize()
+        _same_bits(C1, C3, f"C {case}")
+        _same_bits(y1, y3, f"y {case}")
+    if not routed.any():
+        assert (bf16_to_f64(y1) == 0).all()
 
 
 def test_repeated_calls_identical_and_empty():
