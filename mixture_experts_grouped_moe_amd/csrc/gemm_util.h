@@ -97,6 +97,77 @@ __device__ __forceinline__ int swz(int row, int u) {
   return u ^ ((row / (16 / U)) % U);
 }
 
+// Bytes of LDS a wave needs to stage 32 rows of OC output columns
+// (row stride OC * 2 + 16 bytes: the 16 spread the rows over the banks).
+template <int OC>
+constexpr int stage_rows_bytes() { return 32 * (OC * 2 + 16); }
+
+// Stores a wave's output tile (two 32-row MFMA row tiles of OC columns) to
+// the bf16 rows of C in 16-byte pieces. In the 32x32 MFMA layout a lane
+// holds one column and 16 rows of a tile, so storing straight from the
+// accumulators writes 2 bytes per lane and instruction; instead, per 32-row
+// tile, adjacent lanes pair their columns (one DPP swap: the even lane keeps
+// row i, the odd lane row i + 1), the 4-byte pairs go to this wave's LDS
+// area `stg` (stage_rows_bytes<OC>() bytes, 16-byte aligned), and each lane
+// reads back 8 consecutive columns of one row and stores them whole.
+//   val(mt, j, i): the output value (fp32, before its one bf16 rounding) of
+//     row mt * 32 + (i / 4) * 8 + h * 4 + i % 4 and column j * 32 + l32 of
+//     the wave's tile (lane = 32 h + l32);
+//   slots: LDS list of the tile's slot ids, row r of the wave at slots[r0 + r];
+//     C row = slot id, none when it is >= S;
+//   columns col0 .. col0 + OC - 1 of C, those >= out_w not stored.
+// c must be 16-byte aligned and c_ld a multiple of 8 (16-byte row pieces).
+template <int OC, class F>
+__device__ __forceinline__ void store_tile_rows(F&& val, lds_u8_t* stg, const lds_u8_t* slots, int r0, uint16_t* c,
+                                                int64_t c_ld, int S, int col0, int out_w, int lane) {
+  constexpr int XS = OC * 2 + 16;  // staging row stride, bytes
+  constexpr int PR = OC / 8;       // 16-byte pieces per row
+  static_assert(OC % 32 == 0 && 64 % PR == 0, "columns per wave");
+  const int l32 = lane % 32, h = lane / 32, odd = lane & 1;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int j = 0; j < OC / 32; ++j) {
+#pragma unroll
+      for (int ip = 0; ip < 8; ++ip) {
+        const int i0 = 2 * ip;
+        const uint32_t v0 = f32_to_bf16_bits(val(mt, j, i0));
+        const uint32_t v1 = f32_to_bf16_bits(val(mt, j, i0 + 1));
+        // the even lane receives its odd neighbour's row i0, the odd lane its
+        // even neighbour's row i0 + 1
+        const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(odd ? v0 : v1), 0xB1, 0xF, 0xF, false);
+        const uint32_t word = odd ? (nb | (v1 << 16)) : (v0 | (nb << 16));
+        const int row = (i0 / 4) * 8 + h * 4 + i0 % 4 + odd;
+        const int col = j * 32 + (l32 & ~1);
+        *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(stg + row * XS + col * 2) = word;
+      }
+    }
+    // (a wave's LDS operations complete in order: the pieces read below see
+    // the pairs written above, and the next tile's pairs are written after
+    // these reads; the empty asm keeps the compiler from reordering them)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < 32 * PR / 64; ++it) {
+      const int q = it * 64 + lane;
+      const int row = q / PR, pc = q % PR;
+      const u32x4_t v = lds_read<u32x4_t>(stg + row * XS + pc * 16);
+      const int s = lds_read<int32_t>(slots + (r0 + mt * 32 + row) * 4);
+      const int col = col0 + pc * 8;
+      if (s < S && col < out_w) {
+        uint16_t* dst = c + (int64_t)s * c_ld + col;
+        if (col + 8 <= out_w) {
+          *reinterpret_cast<u32x4_t*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < out_w) dst[e] = (uint16_t)(v[e / 2] >> (16 * (e % 2)));
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+}
+
 // f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
