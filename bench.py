@@ -510,6 +510,11 @@ class W4A16(Workload):
     def extra(self, per_call_us):
         return {"tokens": [c["T"] for c in self.calls], "buckets": [c["Tb"] for c in self.calls]}
 
+    def dense_shapes(self, v):
+        """(M, N, K) of the gate+up and the down products of variant v."""
+        S = self.calls[v]["T"] * self.k
+        return {"up": (S, 2 * self.I, self.H), "down": (S, self.H, self.I)}
+
     cpu_sample_desc = "gate+up GEMM with SwiGLU and down GEMM over all slots of experts 0-3"
 
     def cpu_sample(self):
@@ -584,6 +589,9 @@ class MXFP8(Workload):
 
     def extra(self, per_call_us):
         return {"touched_experts": self.touched, "empty_experts": self.empty}
+
+    def dense_shapes(self, v):
+        return {"gemm": (self.T * self.k, self.N, self.K)}
 
     def cpu_sample(self):
         import numpy as np
@@ -1297,6 +1305,39 @@ def time_second_kernel(wl, torch, stream, args, nv):
                   "hbm_GBps": round(nbytes / secs / 1e9, 1)}}
 
 
+def library_dense(torch, dev, stream, shapes, reps=10):
+    """A reference, not part of the path: the library's dense bf16 GEMM
+    (torch.matmul, i.e. hipBLASLt) on dense operands of the same product
+    sizes (C[M, N] = A[M, K] B[N, K]^T), timed with one event pair per launch
+    after warmup: the MFMA rate this machine sustains on a plain GEMM of that
+    size. Returns its TFLOP/s over all shapes and the median launch time of
+    each distinct shape."""
+    flops, secs, per_shape = 0, 0.0, {}
+    with torch.cuda.stream(stream):
+        for (M, N, K) in shapes:
+            key = f"{M}x{N}x{K}"
+            if key not in per_shape:
+                a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+                b = torch.randn(N, K, device=dev, dtype=torch.bfloat16)
+                for _ in range(3):
+                    torch.matmul(a, b.t())
+                ev = []
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    torch.matmul(a, b.t())
+                    e1.record(stream)
+                    ev.append((e0, e1))
+                torch.cuda.synchronize()
+                ts = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+                per_shape[key] = ts[len(ts) // 2]
+                del a, b
+            flops += 2 * M * N * K
+            secs += per_shape[key] * 1e-3
+    torch.cuda.empty_cache()
+    return {"tflops": round(flops / secs / 1e12, 1), "median_ms": {k: round(v, 4) for k, v in per_shape.items()}}
+
+
 def large_m_block(torch, dev, stream, args, clock):
     """The large-M half of the metric: per workload, the dominant kernel's
     TFLOP/s and fractions of the bf16 MFMA peak and of HBM bandwidth (sums
@@ -1325,6 +1366,17 @@ def large_m_block(torch, dev, stream, args, clock):
         out[name].update(wl.extra(None))
         if hasattr(wl, "second_launches"):
             out[name].update(time_second_kernel(wl, torch, stream, args, nv))
+        if hasattr(wl, "dense_shapes"):
+            # the same products as one dense bf16 library GEMM each (variants
+            # weighted as the timed launches cycle through them)
+            ref = {}
+            for part in wl.dense_shapes(0):
+                lib = library_dense(torch, dev, stream, [wl.dense_shapes(v)[part] for v in range(nv)])
+                ours = out[name]["tflops"] if part in ("up", "gemm") else out[name][part]["tflops"]
+                ref[part] = dict(lib, kernel_frac=round(ours / lib["tflops"], 3))
+            out[name]["library_dense_bf16"] = dict(ref, note=(
+                "reference only: torch.matmul (hipBLASLt) on dense bf16 operands of the same product "
+                "sizes; kernel_frac = this kernel's TFLOP/s over the library's"))
         del wl, m
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
