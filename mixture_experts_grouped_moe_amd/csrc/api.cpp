@@ -284,6 +284,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* g, moe_stream_t stream) {
   p.c_ld = a.c_ld;
   p.sorted = a.sorted_token_ids;
   p.expert_ids = a.expert_ids;
+  p.post_pad = a.num_tokens_post_pad;
   p.S = (int32_t)S;
   p.N = (int32_t)a.n;
   p.K = (int32_t)a.k;

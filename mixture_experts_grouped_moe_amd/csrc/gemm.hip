@@ -88,9 +88,20 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void moe_gemm_kernel(GemmPara
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][STAGE_BYTES];
   static_assert(kMinBlocks * STAGES * STAGE_BYTES <= 160 * 1024, "two workgroups per CU");
 
-  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = L % p.max_blocks;
-  const int tile_n = L / p.max_blocks;
+  // The grid covers every block moe_align could fill; the R blocks in use
+  // (its padded row count / 64) times the N tiles are the real work. The
+  // hardware deals workgroup ids round robin to the 8 XCDs: the real work is
+  // split into 8 contiguous ranges of equal size, one per XCD, each walked in
+  // order (all blocks of one N tile, then the next, so an expert's weight
+  // tile is reused from the XCD's L2); the other workgroups return at once.
+  // (Dealing out the whole grid instead gave the XCDs whose ranges held no
+  // unused blocks up to 14% more real workgroups than the others.)
+  const int R = min(p.max_blocks, max(*p.post_pad, 0) / kBM);
+  const uint32_t work = (uint32_t)(gridDim.x / p.max_blocks) * (uint32_t)R;
+  if (blockIdx.x / 8 >= work / 8 + (blockIdx.x % 8 < work % 8 ? 1u : 0u)) return;
+  const uint32_t L = xcd_remap(blockIdx.x, work);
+  const int b = L % R;
+  const int tile_n = L / R;
   const int e = p.expert_ids[b];
   if (e < 0 || e >= p.E) return;  // sentinel block (or an id outside this layer's experts)
 

@@ -32,6 +32,7 @@ struct GemmParams {
   int64_t c_ld;
   const int32_t* sorted;
   const int32_t* expert_ids;
+  const int32_t* post_pad;  // moe_align's padded row count: blocks past post_pad / block_m are unused
   int32_t S;           // PAD value (= number of slots)
   int32_t N, K;
   int32_t max_blocks;
