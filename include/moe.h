@@ -218,7 +218,10 @@ typedef struct {
 
   const int32_t* sorted_token_ids; /* (device) from moe_align */
   const int32_t* expert_ids;       /* (device) */
-  const int32_t* num_tokens_post_pad; /* (device) */
+  const int32_t* num_tokens_post_pad; /* (device) moe_align's padded row count; the
+                             large-M bf16-activation kernel takes the number of
+                             blocks in use from it (blocks at or past
+                             num_tokens_post_pad / block_m must hold -1) */
   int32_t block_m;        /* must equal moe_gemm_block_m(a_dtype, w_dtype, T) */
   int64_t max_blocks;     /* length of expert_ids; only the first
                              moe_align_max_blocks(S, E, block_m) blocks
