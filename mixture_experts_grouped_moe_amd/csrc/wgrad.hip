@@ -14,9 +14,12 @@
 //    zeros, nothing is atomic and repeated calls give identical bits.
 //  * Slot rows of grad (256 columns) and x (256 columns), 512 bytes each, go
 //    straight from global memory into LDS with buffer_load ... lds,
-//    slot-major as they lie in memory, 32 slots per pipeline unit in three
-//    32 KB stages (two units ahead, across tile boundaries, one barrier per
-//    unit). Each wave computes 64 x 128 of the tile: 16 MFMAs per unit. The
+//    slot-major as they lie in memory, 32 slots per pipeline unit in four
+//    32 KB stages. Units go in pairs (one 64-slot routing block): one
+//    barrier per pair, after which the next pair's loads are issued (across
+//    tile boundaries) and the pair is computed (one barrier per unit with
+//    three stages measured 2% slower). Each wave computes 64 x 128 of the
+//    tile: 16 MFMAs per unit. The
 //    tile size is what the operand traffic asks for: loading both operands
 //    costs (rows + columns) bytes per slot for rows x columns products, and
 //    256 x 256 measured faster than 128 x 256 at two workgroups per CU
@@ -66,7 +69,7 @@ constexpr int kWgXRowB = kWgTK * 2;          // 512 B: a slot's x piece
 constexpr int kWgGUnitB = kWgUM * kWgGRowB;  // 16 KB
 constexpr int kWgXUnitB = kWgUM * kWgXRowB;  // 16 KB
 constexpr int kWgStageB = kWgGUnitB + kWgXUnitB;
-constexpr int kWgStages = 3;
+constexpr int kWgStages = 4;                 // two pairs of units
 constexpr int kWgWaves = 8;
 constexpr int kWgThreads = kWgWaves * 64;
 constexpr int kWgGLoads = kWgGUnitB / 1024 / kWgWaves;  // DMA instructions per wave per unit: 2 grad
@@ -109,11 +112,11 @@ __device__ __forceinline__ wg_i32x4_t wg_scalar_ids4(__amdgpu_buffer_rsrc_t rsrc
 
 // Wait until at most N of this wave's vector-memory operations are in
 // flight and every LDS and scalar-memory operation is done, then barrier;
-// `ids` (a prefetched scalar load) is final from here on.
+// `a` and `b` (prefetched scalar loads) are final from here on.
 template <int N>
-__device__ __forceinline__ void wg_wait_barrier(wg_i32x4_t& ids) {
+__device__ __forceinline__ void wg_wait_barrier(wg_i32x4_t& a, wg_i32x4_t& b) {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%1) lgkmcnt(0)\n\ts_barrier" : "+s"(ids) : "n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%2) lgkmcnt(0)\n\ts_barrier" : "+s"(a), "+s"(b) : "n"(N) : "memory");
 }
 
 // Operand of 8 consecutive slots [m0, m0 + 8) of tile column c0 + lane % 32,
@@ -144,7 +147,7 @@ struct WgTile {
 };
 
 __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams p) {
-  // three stages of [grad unit | x unit], slot-major
+  // four stages of [grad unit | x unit], slot-major
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kWgStages][kWgStageB];
   __shared__ int32_t s_start[kWgMaxExperts + 1];  // first block of expert e (s_start[E] = end)
 
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
   const uint32_t lds_base = (uint32_t)(uintptr_t)(wg_lds_u8_t*)&lds[0][0];
   const uint32_t g_row = (uint32_t)(p.grad_ld * 2), x_row = (uint32_t)(p.x_ld * 2);
 
-  // ---- loader: walks the same tiles' units kWgStages - 1 units ahead of the
+  // ---- loader: walks the same tiles' units one pair ahead of the
   //      computation. Unit u of a tile is slots [32u, 32u + 32) of its block
   //      list; wave w loads slot rows 4w .. 4w + 3 of both parts (two
   //      instructions of 2 rows x 32 lanes each).
@@ -235,16 +238,23 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
       if (ld_live) ld = tile_at(T);
     }
   };
-  auto ld_ids = [&]() {
-    wg_i32x4_t v = {0, 0, 0, 0};
-    if (ld_live) v = wg_scalar_ids4(sorted_rsrc, (uint32_t)((ld.b0 * kWgBM + ld_u * kWgUM + wave * 4) * 4));
-    return v;
+  // the ids of the pair of units the loader points at (a pair is one
+  // 64-slot routing block, never split across tiles)
+  auto ld_ids_pair = [&](wg_i32x4_t& a, wg_i32x4_t& b) {
+    a = wg_i32x4_t{0, 0, 0, 0};
+    b = a;
+    if (ld_live) {
+      const uint32_t off = (uint32_t)((ld.b0 * kWgBM + ld_u * kWgUM + wave * 4) * 4);
+      a = wg_scalar_ids4(sorted_rsrc, off);
+      b = wg_scalar_ids4(sorted_rsrc, off + kWgUM * 4);
+    }
   };
   ld_skip_empty();
-  wg_i32x4_t ids = ld_ids();
-  wg_wait_barrier<0>(ids);
+  wg_i32x4_t ids, ids_b;
+  ld_ids_pair(ids, ids_b);
+  wg_wait_barrier<0>(ids, ids_b);
 
-  auto issue_next = [&](int stage) {
+  auto issue_unit = [&](int stage, const wg_i32x4_t& uid) {
     // scalar row offsets of the wave's 8 slots within the tile's column
     // range (a PAD slot s = S lands at or past the end of both buffers)
     // (past the last tile the ids are 0 and the bases put every lane past
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
     uint32_t go[4], xo[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t s = (uint32_t)ids[r];
+      const uint32_t s = (uint32_t)uid[r];
       const uint64_t prod = ((uint64_t)__umulhi(s, p.topk_magic) << 32) | (s * p.topk_magic);
       const uint32_t xrow = (uint32_t)(prod >> p.topk_shift);
       go[r] = s * g_row + g_base;
@@ -269,10 +279,14 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
     for (int i = 0; i < kWgXLoads; ++i)
       wg_dma16(x_rsrc, pick(xm1, xo[2 * i + 1], xo[2 * i]) + (i % 2 ? x_col1 : x_col0),
                dst + (uint32_t)(kWgGUnitB + (wave * kWgXLoads + i) * 1024));
+  };
+  auto issue_pair = [&](int stage) {  // stages stage, stage + 1
+    issue_unit(stage, ids);
+    issue_unit(stage + 1, ids_b);
     if (ld_live) {
-      ++ld_u;
+      ld_u += 2;
       ld_skip_empty();
-      ids = ld_ids();  // completes by the next wait
+      ld_ids_pair(ids, ids_b);  // complete by the next wait
     }
   };
 
@@ -302,17 +316,14 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
   };
 
-  // ---- computation. Before a unit the wave waits until only the loads of
-  //      the next unit (and the stores of a tile finished just before) are in
-  //      flight; the barrier then makes every wave's DMA visible and
-  //      guarantees all waves finished the previous unit, whose stage the
-  //      loads issued next overwrite.
-#pragma unroll
-  for (int q = 0; q < kWgStages - 1; ++q) {
-    issue_next(q);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(ids));
-  }
-  int st = 0;  // stage of the next unit computed
+  // ---- computation, a pair of units (one routing block) per barrier:
+  //      before a pair the wave waits until only the stores of a tile
+  //      finished just before are in flight (the pair's loads were issued
+  //      before them); the barrier makes every wave's DMA visible and
+  //      guarantees all waves finished the previous pair, whose two stages
+  //      the loads issued next overwrite.
+  issue_pair(0);
+  int st = 0;  // first stage of the next pair computed
   bool stored = false;
   for (int it = 0; tile_index(it) < total; ++it) {
     const WgTile t = tile_at(tile_index(it));
@@ -323,19 +334,17 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int nu = 2 * (t.b1 - t.b0);
-    for (int u = 0; u < nu; ++u) {
+    for (int u = 0; u < nu; u += 2) {
       if (stored) {
-        // (more stores than the counter can express: waiting for 63 younger
-        // operations may also wait for some stores, never too few)
-        constexpr int kAfterStores = kWgLoads * (kWgStages - 2) + kWgStores;
-        wg_wait_barrier<(kAfterStores > 63 ? 63 : kAfterStores)>(ids);
+        wg_wait_barrier<kWgStores>(ids, ids_b);
         stored = false;
       } else {
-        wg_wait_barrier<kWgLoads * (kWgStages - 2)>(ids);
+        wg_wait_barrier<0>(ids, ids_b);
       }
-      issue_next(st == 0 ? kWgStages - 1 : st - 1);  // the stage computed last, now free
+      issue_pair(st ^ 2);  // the pair computed last, now free
       contract(st);
-      st = st == kWgStages - 1 ? 0 : st + 1;
+      contract(st + 1);
+      st ^= 2;
     }
     // store the tile through LDS: the stage the next unit's loads will go
     // to is free once every wave is past its last contraction. Each wave
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
       // the buffer drops), so the waits above, which count them, stay exact
       const __amdgpu_buffer_rsrc_t dw_rsrc = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.dw + (int64_t)t.e * p.N * p.K), 0, (int)(uint32_t)((int64_t)p.N * p.K * 4), 0x00020000);
-      const int free_stage = st == 0 ? kWgStages - 1 : st - 1;
+      const int free_stage = st ^ 2;  // the last pair's first stage
       __attribute__((address_space(3))) float* scr =
           (__attribute__((address_space(3))) float*)&lds[free_stage][wave * 8 * 512];
 #pragma unroll
