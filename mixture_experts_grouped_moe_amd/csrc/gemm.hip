@@ -39,12 +39,15 @@
 //    their use; the E8M0 byte rides in the exponent field of the conversion's
 //    scale operand, which gives exactly 2^(b-127) including 0x00 and 0xFF.
 //  * v_mfma_f32_32x32x16_bf16, fp32 accumulators, one bf16 rounding at the
-//    store. Each wave: 64 rows x (32 * NT) columns.
+//    store. Each wave: 64 rows x (32 * NT) columns. C is written in 16-byte
+//    row pieces staged through LDS (store_tile_rows), or element by element
+//    when C is not 16-byte aligned.
 //  * LDS rows are made of 16-byte units XOR-swizzled by row so that each
 //    16-lane group of a read instruction spreads over all 64 banks.
 //  * Workgroup ids are remapped so each XCD walks all routing blocks of one
 //    N tile in order: consecutive blocks of one expert reuse the weight tile
-//    from that XCD's L2.
+//    from that XCD's L2. Only the blocks in use (moe_align's padded row
+//    count) are dealt out, in equal ranges per XCD.
 //  * SwiGLU: a tile's weight rows are the gate rows of its h columns followed
 //    by the matching up rows, arranged so that a lane holds gate and up of the
 //    same output element in the same accumulator register.

@@ -25,7 +25,9 @@
 //    scale operand of lane l is that of K block h: its 32 elements are bytes
 //    0-15 of both lane halves (h = 0) or bytes 16-31 (h = 1). So a lane reads
 //    16-byte units h and 2 + h of its row's 64-byte step piece.
-//  * fp32 accumulators, bias and SwiGLU in the epilogue, one bf16 rounding.
+//  * fp32 accumulators, bias and SwiGLU in the epilogue, one bf16 rounding;
+//    C is written in 16-byte row pieces staged through LDS (store_tile_rows),
+//    or element by element when C is not 16-byte aligned.
 //
 // The same kernel in per-token mode is moe_gemm_per_token of that PR
 // (Summary: E4M3 operands with one fp32 scale per activation row and one per

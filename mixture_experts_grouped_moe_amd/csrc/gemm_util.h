@@ -1,7 +1,8 @@
 // Building blocks of the large-M grouped GEMM kernels (bf16 activations in
 // gemm.hip, MXFP8 activations in gemm_f8.hip): the workgroup shape, the
 // LDS-DMA and byte loads issued with inline assembly, the wait-and-barrier of
-// the K loop, the LDS swizzle and the weight rows of an N tile.
+// the K loop, the LDS swizzle, the staged store of an output tile and the
+// weight rows of an N tile.
 #pragma once
 
 #include <type_traits>
