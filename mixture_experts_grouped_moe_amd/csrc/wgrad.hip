@@ -74,7 +74,6 @@ constexpr int kWgWaves = 8;
 constexpr int kWgThreads = kWgWaves * 64;
 constexpr int kWgGLoads = kWgGUnitB / 1024 / kWgWaves;  // DMA instructions per wave per unit: 2 grad
 constexpr int kWgXLoads = kWgXUnitB / 1024 / kWgWaves;  //   + 2 x (2 rows each)
-constexpr int kWgLoads = kWgGLoads + kWgXLoads;
 constexpr int kWgStores = 8 * 4;             // 16-byte stores per lane per tile
 constexpr int kWgPerCU = 1;                  // resident workgroups per CU
 constexpr int kWgMaxExperts = 1024;
@@ -346,8 +345,9 @@ __global__ __launch_bounds__(kWgThreads, kWgPerCU) void wgrad_kernel(WgradParams
       contract(st + 1);
       st ^= 2;
     }
-    // store the tile through LDS: the stage the next unit's loads will go
-    // to is free once every wave is past its last contraction. Each wave
+    // store the tile through LDS: the first stage of the pair computed last
+    // is free once every wave is past its last contraction (the next
+    // pair's loads go to the other two). Each wave
     // passes 8 rows at a time through its own 4 KB of it and writes whole
     // 512-byte row pieces with 16-byte stores.
     __syncthreads();
