@@ -336,7 +336,8 @@ class Nemotron(Workload):
     """The Nemotron-shaped non-gated squared-ReLU decode layer (E=128, top-6,
     hidden 2688, N=1856, bf16) at M = 1, 7, 14, 21, 28: per M one step runs
     moe_align -> up GEMM with relu2 -> down GEMM -> moe_combine, both GEMMs on
-    the decode kernel."""
+    the decode kernel. The line also times the mid-M bucket (M = 64, 120) on
+    the large-M kernel (`mid_m`)."""
     name = "nemotron"
     dominant = "moe_decode_kernel"
     bound = "hbm"
@@ -416,7 +417,51 @@ class Nemotron(Workload):
         if per_call_us is not None:
             for i, M in enumerate(self.MS):
                 us[str(M)] = {"up": round(per_call_us[2 * i], 2), "down": round(per_call_us[2 * i + 1], 2)}
-        return {"us_per_gemm": us, "touched_experts": {str(M): self.calls[0][i]["touched"] for i, M in enumerate(self.MS)}}
+        out = {"us_per_gemm": us, "touched_experts": {str(M): self.calls[0][i]["touched"] for i, M in enumerate(self.MS)}}
+        if per_call_us is not None:
+            out["mid_m"] = self._mid_m()
+        return out
+
+    MID_MS = (64, 120)
+
+    def _mid_m(self, reps=10):
+        """The steady-state mid-M decode bucket (M ~ 115-120 tokens, and 64):
+        the same layer's up and down GEMMs run on the large-M kernel (64-row
+        routing blocks); each GEMM launched back to back on resident inputs,
+        one event pair per launch. GB/s counts the touched experts' weights,
+        the activations read and the outputs written."""
+        import numpy as np
+        import synth
+        torch, moe = self.torch, self.moe
+        res = {}
+        for M in self.MID_MS:
+            dm = synth.nemotron_layer(M, device=self.w1.device, weights=False)
+            bm = moe.moe_gemm_block_m("bf16", M)
+            routing = moe.moe_align(dm["ids"], self.E, bm)
+            S = M * self.k
+            touched = len(np.unique(dm["ids"].cpu().numpy()))
+            h = torch.empty((S, self.N), dtype=torch.bfloat16, device=self.w1.device)
+            c2 = torch.empty((S, self.H), dtype=torch.bfloat16, device=self.w1.device)
+            up, _ = moe.moe_grouped_gemm_prepare(dm["x"], self.w1, "bf16", routing, M, self.k, self.E, self.k,
+                                                 epilogue="relu2", out=h)
+            down, _ = moe.moe_grouped_gemm_prepare(h, self.w2, "bf16", routing, M, self.k, self.E, 1, out=c2)
+            wb = touched * self.N * self.H * 2
+            entry = {"touched_experts": touched}
+            for name, fn, nbytes in (("up", up, wb + M * self.H * 2 + S * self.N * 2),
+                                     ("down", down, wb + S * self.N * 2 + S * self.H * 2)):
+                for _ in range(3):
+                    fn()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+                for a, b in ev:
+                    a.record()
+                    fn()
+                    b.record()
+                torch.cuda.synchronize()
+                t = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+                entry[name] = {"us": round(t, 1), "GBps": round(nbytes / t / 1e3, 1),
+                               "hbm_frac": round(nbytes / t / 1e3 / PEAK_HBM_GBS, 4)}
+            res[str(M)] = entry
+        return res
 
     def cpu_sample(self):
         import synth
