@@ -769,6 +769,9 @@ class PerToken(Workload):
     def dominant_launches(self, v):
         return [(self._gemm, self.gemm_bytes())]
 
+    def dominant_flops_bytes(self, v):
+        return self.step_flops(v), self.gemm_bytes()
+
     def extra(self, per_call_us):
         return {"touched_experts": self.touched, "empty_experts": self.empty}
 
@@ -1347,7 +1350,8 @@ def time_second_kernel(wl, torch, stream, args, nv):
     nbytes = sum(n for _, _, _, n in durs)
     return {key: {"launch_us": stats(us), "tflops": round(flops / secs / 1e12, 1),
                   "bf16_peak_frac": round(flops / secs / 1e12 / PEAK_BF16_TFLOPS, 4),
-                  "hbm_GBps": round(nbytes / secs / 1e9, 1)}}
+                  "hbm_GBps": round(nbytes / secs / 1e9, 1),
+                  **attainable(flops, nbytes, flops / secs / 1e12)}}
 
 
 def library_dense(torch, dev, stream, shapes, reps=10):
@@ -1383,6 +1387,16 @@ def library_dense(torch, dev, stream, shapes, reps=10):
     return {"tflops": round(flops / secs / 1e12, 1), "median_ms": {k: round(v, 4) for k, v in per_shape.items()}}
 
 
+def attainable(flops, nbytes, tflops, peak_tflops=PEAK_BF16_TFLOPS):
+    """Arithmetic intensity (flop/B of the algorithmic work) and the fraction
+    of the attainable roofline min(MFMA peak of the dtype, AI x HBM peak)
+    reached."""
+    ai = flops / nbytes
+    roof = min(peak_tflops, ai * PEAK_HBM_GBS / 1e3)
+    return {"arith_intensity": round(ai, 1), "attainable_tflops": round(roof, 1),
+            "attainable_frac": round(tflops / roof, 4)}
+
+
 def large_m_block(torch, dev, stream, args, clock):
     """The large-M half of the metric: per workload, the dominant kernel's
     TFLOP/s and fractions of the bf16 MFMA peak and of HBM bandwidth (sums
@@ -1403,6 +1417,7 @@ def large_m_block(torch, dev, stream, args, clock):
             "bf16_peak_frac": round(flops / secs / 1e12 / PEAK_BF16_TFLOPS, 4),
             "hbm_GBps": round(nbytes / secs / 1e9, 1),
             "hbm_frac": round(nbytes / secs / 1e9 / PEAK_HBM_GBS, 4),
+            **attainable(flops, nbytes, flops / secs / 1e12),
             "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
             "step_tflops": round(m["step_flops"] / m["dt"] / 1e12, 1),
             "ms_per_step": round(m["dt"] / args.steps * 1e3, 4),
@@ -1550,6 +1565,12 @@ def workload_main(torch, dev, stream, args, clock):
         if args.workload in ("mxfp8a", "pertoken"):
             extra["mfma_frac_step_fp8"] = round(value / (2 * PEAK_BF16_TFLOPS), 4)
         extra["hbm_GBps_step"] = round(m["step_bytes"] / dt / 1e9, 1)
+        if hasattr(wl, "dominant_flops_bytes"):
+            # the dominant kernel against min(its dtype's MFMA peak, AI x HBM peak)
+            fl = sum(wl.dominant_flops_bytes(v)[0] for v in m["launch_variant"])
+            nb = sum(wl.dominant_flops_bytes(v)[1] for v in m["launch_variant"])
+            peak = 2 * PEAK_BF16_TFLOPS if args.workload in ("mxfp8a", "pertoken") else PEAK_BF16_TFLOPS
+            extra["kernel_roofline"] = attainable(fl, nb, fl / (m["dom_ms"] * 1e-3) / 1e12, peak)
         dtype = {"w4a16": "bf16 x e2m1 (bf16 MFMA)", "mxfp8": "bf16 x e4m3 (bf16 MFMA)",
                  "mxfp8a": "e4m3 x e4m3, E8M0 per 32 (scaled fp8 MFMA)",
                  "pertoken": "e4m3 x e4m3, fp32 per-row and per-expert scales (fp8 MFMA)",
