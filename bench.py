@@ -938,14 +938,19 @@ def cpu_baseline(wl, target_s):
             break
     dt = time.perf_counter() - t0
     scale = 1e9 if unit == "GB/s" else 1e12
+    blas = "unknown"
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
         threads = max((i.get("num_threads", 1) for i in info), default=1)
+        libs = [i for i in info if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api', '?')} {libs[0].get('version', '')}".strip()
     except Exception:
         threads = cores
     _ = np
     return {"value": done_units / dt / scale, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "blas": blas, "affinity_cpus": cores,
             "sample": f"{n} runs over a {len(items)}-item sample of the {wl.name} workload "
                       f"({wl.cpu_sample_desc}), {dt:.1f} s"}
 
