@@ -1454,8 +1454,8 @@ def main():
         record_counters(args.counters_key or args.workload, args.counters_from)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of this "
-                                   "build (--gpus must be 1)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the library has no multi-GPU path "
+                                   "(--gpus must be 1)"}))
         sys.exit(2)
     import torch
     import mixture_experts_grouped_moe_amd as moe  # noqa: F401  (fails loudly if libmoe.so is missing)
