@@ -7,17 +7,24 @@
 // second review: sentinel blocks hold -1) and torchada PR #115 ("Follow-up on
 // this table": moe_align_block_size runs ahead of the fused MoE GEMM).
 //
-// One workgroup of 1024 threads does the whole job: the sizes on this path
-// (at most a few hundred thousand slots, at most 1024 experts) keep it in the
-// microsecond range, and one workgroup needs no cross-workgroup
-// synchronisation and no workspace. Each of up to 16 waves owns a contiguous
-// run of slots: it counts its run's slots per expert, a scan in expert-major,
-// wave-minor order gives every wave its first position per expert, and each
-// wave then scatters its own run 64 slots at a time, ranking equal expert
-// ids with ballots and advancing its own per-expert counters. The order
-// within an expert is therefore ascending slot order (runs in slot order,
-// batches in order, lanes in order), the result unique and deterministic,
-// and the scatter needs no workgroup barrier.
+// G workgroups of 1024 threads (G = 1 up to 8K slots, then one per 8K
+// slots, at most 16); no workspace and no cross-workgroup synchronisation.
+// The slots are cut into 16 G contiguous runs, run r = 16 g + w owned by
+// wave w of workgroup g. Every workgroup reads all ids: its waves count
+// every run, into the per-expert totals, the counts of the runs before the
+// workgroup's own, and each wave's count of its own run. A scan over
+// experts of the padded totals then gives every wave its first position per
+// expert (the expert's offset, the runs before this workgroup, the earlier
+// waves of this workgroup), and each wave scatters its own run 64 slots at
+// a time, ranking equal expert ids with ballots and advancing its own
+// per-expert counters. The order within an expert is therefore ascending
+// slot order (runs in slot order, batches in order, lanes in order): the
+// result is unique and the same for any G. The scattered 4-byte stores of a
+// run were what one workgroup spent most of its time on (one CU's memory
+// pipeline), so they are spread over G CUs; the histogram is repeated in
+// each workgroup instead of exchanged, which needs no scratch memory.
+#include <algorithm>
+
 #include "common.h"
 #include "params.h"
 
@@ -27,52 +34,69 @@ constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 constexpr int kAlignMaxExperts = 1024;
 constexpr int kAlignBatch = 8;  // 64-slot batches whose ids a wave loads together
+constexpr int kAlignSlotsPerWg = 8192;  // slots per additional workgroup
+constexpr int kAlignMaxWgs = 16;
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int32_t S, int32_t E, int32_t B,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
     int32_t* __restrict__ post_pad, int32_t max_blocks) {
-  __shared__ int32_t cnt[kAlignMaxExperts];
+  __shared__ int32_t tot[kAlignMaxExperts];   // per-expert slot counts (all runs)
+  __shared__ int32_t bef[kAlignMaxExperts];   // ... of the runs before this workgroup's
   __shared__ int32_t off[kAlignMaxExperts];   // exclusive scan of padded counts
-  // per wave and expert: the count of the wave's run, then its next position
+  // per wave and expert: the count of the wave's own run, then its next position
   __shared__ int32_t wave_pos[kAlignWaves][kAlignMaxExperts];
   __shared__ int32_t wave_sum[kAlignWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  // this wave's run of slots: one run per 64 slots, at most one per wave, so
-  // small inputs leave most waves (and their counters) idle
-  const int runs = min(kAlignWaves, S / kWave + 1);
+  const int G = gridDim.x, g = blockIdx.x;
+  // runs: one per 64 slots, at most 16 per workgroup, so small inputs leave
+  // most waves (and their counters) idle
+  const int runs = min(kAlignWaves * G, S / kWave + 1);
   const int run_len = S / runs + (S % runs != 0);
-  const int r0 = min(wave * run_len, S), r1 = min(r0 + run_len, S);
+  const int own = g * kAlignWaves + wave;  // this wave's run
 
-  for (int i = tid; i < runs * kAlignMaxExperts; i += kAlignThreads)
+  for (int i = tid; i < kAlignWaves * kAlignMaxExperts; i += kAlignThreads)
     (&wave_pos[0][0])[i] = 0;
+  for (int e = tid; e < kAlignMaxExperts; e += kAlignThreads) {
+    tot[e] = 0;
+    bef[e] = 0;
+  }
   __syncthreads();
 
-  // 1. per-wave histogram of its run
-  for (int base = r0; base < r1; base += kWave * kAlignBatch) {
-    int ev[kAlignBatch];
+  // 1. histograms: wave w counts runs w, w + 16, ... (all of them, across
+  //    the workgroups' ranges)
+  for (int r = wave; r < runs; r += kAlignWaves) {
+    const int r0 = min(r * run_len, S), r1 = min(r0 + run_len, S);
+    const bool mine = r == own, before = r < g * kAlignWaves;
+    for (int base = r0; base < r1; base += kWave * kAlignBatch) {
+      int ev[kAlignBatch];
 #pragma unroll
-    for (int i = 0; i < kAlignBatch; ++i) {
-      const int s = base + i * kWave + lane;
-      ev[i] = s < r1 ? ids[s] : -1;
-    }
+      for (int i = 0; i < kAlignBatch; ++i) {
+        const int s = base + i * kWave + lane;
+        ev[i] = s < r1 ? ids[s] : -1;
+      }
 #pragma unroll
-    for (int i = 0; i < kAlignBatch; ++i) {
-      if (base + i * kWave >= r1) break;  // uniform across the wave
-      if (ev[i] >= 0 && ev[i] < E) atomicAdd(&wave_pos[wave][ev[i]], 1);
+      for (int i = 0; i < kAlignBatch; ++i) {
+        if (base + i * kWave >= r1) break;  // uniform across the wave
+        const int e = ev[i];
+        if (e >= 0 && e < E) {
+          atomicAdd(&tot[e], 1);
+          if (before) atomicAdd(&bef[e], 1);
+          if (mine) atomicAdd(&wave_pos[wave][e], 1);
+        }
+      }
     }
   }
   __syncthreads();
 
-  // 2. per-expert totals, exclusive scan of p_e = ceil(c_e / B) * B over
-  //    experts (E <= 1024: one value per thread; wave-level inclusive scan,
-  //    then across waves), and each wave's first position per expert
+  // 2. exclusive scan of p_e = ceil(c_e / B) * B over experts (E <= 1024:
+  //    one value per thread; wave-level inclusive scan, then across waves),
+  //    and each wave's first position per expert
   int c = 0;
-  if (tid < E)
-    for (int w = 0; w < runs; ++w) c += wave_pos[w][tid];
+  if (tid < E) c = tot[tid];
   const int p = ((c + B - 1) / B) * B;
   int incl = p;
   for (int d = 1; d < kWave; d <<= 1) {
@@ -81,27 +105,27 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   }
   if (lane == kWave - 1) wave_sum[wave] = incl;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_sum[w];
+  int before_sum = 0;
+  for (int w = 0; w < wave; ++w) before_sum += wave_sum[w];
   int total = 0;
   for (int w = 0; w < kAlignWaves; ++w) total += wave_sum[w];
-  const int o_e = before + incl - p;
+  const int o_e = before_sum + incl - p;
   if (tid < E) {
     off[tid] = o_e;
-    cnt[tid] = c;
-    int next = o_e;
-    for (int w = 0; w < runs; ++w) {
+    int next = o_e + bef[tid];
+    for (int w = 0; w < kAlignWaves; ++w) {
       const int t = wave_pos[w][tid];
       wave_pos[w][tid] = next;
       next += t;
     }
   }
-  if (tid == 0) *post_pad = total;
+  if (g == 0 && tid == 0) *post_pad = total;
   __syncthreads();
 
   // 3. expert id per block: the largest e with off[e] <= b * B (that expert
-  //    is never empty when b * B < total); -1 past the used blocks.
-  for (int b = tid; b < max_blocks; b += kAlignThreads) {
+  //    is never empty when b * B < total); -1 past the used blocks. Blocks
+  //    are dealt to the workgroups in turn.
+  for (int b = g * kAlignThreads + tid; b < max_blocks; b += G * kAlignThreads) {
     int pos = b * B;
     int e = -1;
     if (pos < total) {
@@ -114,24 +138,27 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     }
     expert_ids[b] = e;
   }
-  // 4. PAD: the tail of each expert's segment (under 32 positions: one thread
-  //    per expert; otherwise one wave per expert, lanes on consecutive
-  //    positions) and everything past `total`.
+  // 4. PAD: the tail of each expert's segment (under 32 positions: one
+  //    thread per expert; otherwise one wave per expert, lanes on
+  //    consecutive positions) and everything past `total`; experts and
+  //    positions are dealt to the workgroups in turn.
   const int32_t pad = S;
   if (B <= 32) {
-    if (tid < E)
+    if (tid < E && tid % G == g)
       for (int q = o_e + c; q < o_e + p; ++q) sorted_ids[q] = pad;
   } else {
-    for (int e = wave; e < E; e += kAlignWaves) {
-      const int o = off[e], c_e = cnt[e];
+    for (int e = g * kAlignWaves + wave; e < E; e += G * kAlignWaves) {
+      const int o = off[e], c_e = tot[e];
       const int end = o + ((c_e + B - 1) / B) * B;
       for (int q = o + c_e + lane; q < end; q += kWave) sorted_ids[q] = pad;
     }
   }
   const int64_t len = (int64_t)max_blocks * B;
-  for (int64_t q = total + tid; q < len; q += kAlignThreads) sorted_ids[q] = pad;
+  for (int64_t q = total + (int64_t)g * kAlignThreads + tid; q < len; q += (int64_t)G * kAlignThreads)
+    sorted_ids[q] = pad;
 
-  // 5. each wave scatters its run in order, 64 slots at a time
+  // 5. each wave scatters its own run in order, 64 slots at a time
+  const int r0 = min(own * run_len, S), r1 = own < runs ? min(r0 + run_len, S) : r0;
   for (int base = r0; base < r1; base += kWave * kAlignBatch) {
     int ev[kAlignBatch];
 #pragma unroll
@@ -261,7 +288,8 @@ hipError_t launch_block_map(const int32_t* group_sizes, int32_t E, int32_t B, in
 hipError_t launch_align(const int32_t* ids, int32_t S, int32_t E, int32_t B,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* post_pad,
                         int32_t max_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, stream,
+  const int G = std::max(1, std::min(kAlignMaxWgs, S / kAlignSlotsPerWg));
+  hipLaunchKernelGGL(align_kernel, dim3((uint32_t)G), dim3(kAlignThreads), 0, stream,
                      ids, S, E, B, sorted_ids, expert_ids, post_pad, max_blocks);
   return hipGetLastError();
 }

@@ -118,3 +118,17 @@ def test_run_boundaries(S):
         ids = rng.integers(0, E, size=(S, 1)).astype(np.int32)
         ids[S // 3: S // 3 + S // 4, 0] = E - 1
         _check(ids, E, B, extra_blocks=1)
+
+
+@pytest.mark.parametrize("S", [16383, 16384, 16385, 24577, 65535, 131071, 200003])
+def test_workgroup_boundaries(S):
+    # above 8192 slots the routing runs on one workgroup per 8192 slots (at
+    # most 16), each counting every run and scattering its own 16: slot
+    # counts on either side of a workgroup count's edge, the cap, padding
+    # below and above 32 rows, ids outside [0, E), and one heavy expert whose
+    # slots span several workgroups' runs
+    rng = np.random.default_rng(S)
+    for E, B in ((5, 8), (256, 64), (1024, 32)):
+        ids = rng.integers(-2, E + 2, size=(S, 1)).astype(np.int32)
+        ids[S // 5: S // 5 + S // 3, 0] = E - 1
+        _check(ids, E, B, extra_blocks=2)
