@@ -57,10 +57,12 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   const int runs = min(kAlignWaves * G, S / kWave + 1);
   const int run_len = S / runs + (S % runs != 0);
   const int own = g * kAlignWaves + wave;  // this wave's run
+  // waves of this workgroup that own a run (only their counter rows are used)
+  const int nw = max(0, min(kAlignWaves, runs - g * kAlignWaves));
 
-  for (int i = tid; i < kAlignWaves * kAlignMaxExperts; i += kAlignThreads)
+  for (int i = tid; i < nw * kAlignMaxExperts; i += kAlignThreads)
     (&wave_pos[0][0])[i] = 0;
-  for (int e = tid; e < kAlignMaxExperts; e += kAlignThreads) {
+  for (int e = tid; e < E; e += kAlignThreads) {
     tot[e] = 0;
     bef[e] = 0;
   }
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   if (tid < E) {
     off[tid] = o_e;
     int next = o_e + bef[tid];
-    for (int w = 0; w < kAlignWaves; ++w) {
+    for (int w = 0; w < nw; ++w) {
       const int t = wave_pos[w][tid];
       wave_pos[w][tid] = next;
       next += t;
