@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import synth
-from helpers import assert_parity, bf16_to_f64, host, need_gpu, to_dev
+from helpers import assert_parity, bf16_to_f64, combine_scale, host, need_gpu, to_dev
 from oracle import gemm as ogemm
 
 pytestmark = pytest.mark.gpu
@@ -58,7 +58,7 @@ def _oracle(d, T, k, E, wd, epilogue):
     h = host(d)
     C, routed = ogemm.grouped_gemm(h["x"], k, h["w"], wd, h["w_scale"], h["ids"], E, bias=h["bias"],
                                    epilogue=epilogue)
-    return C, routed, ogemm.combine(C, h["topk_w"], k)
+    return C, routed, ogemm.combine(C, h["topk_w"], k), combine_scale(C, h["topk_w"], k)
 
 
 def _same_bits(a, b, what):
@@ -90,10 +90,10 @@ def test_decode_layer_equals_three_launches_and_oracle(case):
     torch.cuda.synchronize()
     _same_bits(C1, C3, f"C {case}")
     _same_bits(y1, y3, f"y {case}")
-    rC, routed, ry = _oracle(d, T, k, E, wd, ep)
+    rC, routed, ry, ys = _oracle(d, T, k, E, wd, ep)
     assert routed.all()
     assert_parity(bf16_to_f64(C1), rC, what=f"C {case}")
-    assert_parity(bf16_to_f64(y1), ry, what=f"y {case}")
+    assert_parity(bf16_to_f64(y1), ry, scale=ys, what=f"y {case}")
 
 
 @pytest.mark.parametrize("M", [1, 7, 14, 21, 28, 32])
@@ -109,9 +109,9 @@ def test_decode_shape_equals_three_launches(M):
     _same_bits(y1, y3, f"y M={M}")
     cols = np.sort(np.random.default_rng(M).choice(N, 64, replace=False))
     sub = dict(d, w=d["w"][:, torch.from_numpy(cols).cuda(), :].contiguous())
-    rC, _, ry = _oracle(sub, T, k, E, "bf16", "none")
+    rC, _, ry, ys = _oracle(sub, T, k, E, "bf16", "none")
     assert_parity(bf16_to_f64(C1)[:, cols], rC, what=f"C M={M}")
-    assert_parity(bf16_to_f64(y1)[:, cols], ry, what=f"y M={M}")
+    assert_parity(bf16_to_f64(y1)[:, cols], ry, scale=ys, what=f"y M={M}")
 
 
 def test_nemotron_up_projection_equals_three_launches():
@@ -134,9 +134,9 @@ def test_ragged_n_against_oracle():
     dd = to_dev(d)
     C1, y1 = _fused(dd, T, k, N, "e4m3", "relu2")
     torch.cuda.synchronize()
-    rC, _, ry = _oracle(d, T, k, E, "e4m3", "relu2")
+    rC, _, ry, ys = _oracle(d, T, k, E, "e4m3", "relu2")
     assert_parity(bf16_to_f64(C1), rC, what="C")
-    assert_parity(bf16_to_f64(y1), ry, what="y")
+    assert_parity(bf16_to_f64(y1), ry, scale=ys, what="y")
 
 
 @pytest.mark.parametrize("kind", ["zipf", "repeated"])
@@ -156,8 +156,8 @@ def test_skewed_and_repeated_routing(kind):
     torch.cuda.synchronize()
     _same_bits(C1, C3, "C")
     _same_bits(y1, y3, "y")
-    rC, _, ry = _oracle(d, T, k, E, "bf16", "none")
-    assert_parity(bf16_to_f64(y1), ry, what="y")
+    rC, _, ry, ys = _oracle(d, T, k, E, "bf16", "none")
+    assert_parity(bf16_to_f64(y1), ry, scale=ys, what="y")
 
 
 def test_ids_outside_the_experts_contribute_zero():
@@ -169,12 +169,12 @@ def test_ids_outside_the_experts_contribute_zero():
     dd = to_dev(d)
     C1, y1 = _fused(dd, T, k, N, "bf16", "none")
     torch.cuda.synchronize()
-    rC, routed, ry = _oracle(d, T, k, E, "bf16", "none")
+    rC, routed, ry, ys = _oracle(d, T, k, E, "bf16", "none")
     assert routed.sum() == T * k - 3
     got = bf16_to_f64(C1)
     assert np.isnan(got[~routed]).all()          # rows of unrouted slots are not written
     assert_parity(got[routed], rC[routed], what="C")
-    assert_parity(bf16_to_f64(y1), ry, what="y")
+    assert_parity(bf16_to_f64(y1), ry, scale=ys, what="y")
 
 
 SMALL_ROUTES = [
@@ -200,11 +200,11 @@ def test_few_slots_routed_in_registers(case):
     dd = to_dev(d)
     C1, y1 = _fused(dd, T, k, N, wd, ep)
     torch.cuda.synchronize()
-    rC, routed, ry = _oracle(d, T, k, E, wd, ep)
+    rC, routed, ry, ys = _oracle(d, T, k, E, wd, ep)
     got = bf16_to_f64(C1)
     assert np.isnan(got[~routed]).all()          # rows of unrouted slots are not written
     assert_parity(got[routed], rC[routed], what=f"C {case}")
-    assert_parity(bf16_to_f64(y1), ry, what=f"y {case}")
+    assert_parity(bf16_to_f64(y1), ry, scale=ys, what=f"y {case}")
     if routed.all():
         C3, y3 = _unfused(dd, T, k, E, N, wd, ep)
         torch.cuda.synchronize()
@@ -254,11 +254,11 @@ def test_nan_scale_bytes_propagate_like_the_oracle(wd):
     dd = to_dev(d)
     C1, y1 = _fused(dd, T, k, N, wd, "none")
     torch.cuda.synchronize()
-    rC, _, ry = _oracle(d, T, k, E, wd, "none")
+    rC, _, ry, ys = _oracle(d, T, k, E, wd, "none")
     got_c, got_y = bf16_to_f64(C1), bf16_to_f64(y1)
     assert np.isnan(got_c[:, 5]).any() and np.isnan(got_y[0, 40])
     assert_parity(got_c, rC, what="C")
-    assert_parity(got_y, ry, what="y")
+    assert_parity(got_y, ry, scale=ys, what="y")
 
 
 SPLIT_CASES = [
@@ -281,10 +281,10 @@ def test_two_pass_layer_against_oracle_and_three_launches(case):
     C3, y3 = _unfused(dd, T, k, E, N, wd, ep)
     C1, y1 = _fused(dd, T, k, N, wd, ep)
     torch.cuda.synchronize()
-    rC, routed, ry = _oracle(d, T, k, E, wd, ep)
+    rC, routed, ry, ys = _oracle(d, T, k, E, wd, ep)
     assert routed.all()
     assert_parity(bf16_to_f64(C1), rC, what=f"C {case}")
-    assert_parity(bf16_to_f64(y1), ry, what=f"y {case}")
+    assert_parity(bf16_to_f64(y1), ry, scale=ys, what=f"y {case}")
     # the three launches sum each output over all of K at once: equal within
     # the bar (the per-pass grouping may move a last bit)
     assert_parity(bf16_to_f64(C1), bf16_to_f64(C3), what=f"C vs three launches {case}")
@@ -310,5 +310,5 @@ def test_nemotron_up_projection_at_28_and_32_tokens(M):
     cols = np.sort(np.random.default_rng(28).choice(1856, 64, replace=False))
     sub = dict(dd, w=d["w1"][:, torch.from_numpy(cols).cuda(), :].contiguous(),
                bias=d["b1"][:, torch.from_numpy(cols).cuda()].contiguous())
-    rC, _, ry = _oracle(sub, M, 6, 128, "bf16", "relu2")
+    rC, _, ry, ys = _oracle(sub, M, 6, 128, "bf16", "relu2")
     assert_parity(bf16_to_f64(C1)[:, cols], rC, what="C")

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from helpers import assert_parity, bf16_to_f64, host, need_gpu, to_dev
+from helpers import assert_parity, bf16_to_f64, combine_scale, host, need_gpu, to_dev
 from oracle import gemm as ogemm
 
 pytestmark = pytest.mark.gpu
@@ -97,7 +97,8 @@ def test_config1_and_combine():
     assert_parity(bf16_to_f64(C), ref, what="config1 C")
     y = moe.moe_combine(C, dd["topk_w"], 2)
     torch.cuda.synchronize()
-    assert_parity(bf16_to_f64(y), ogemm.combine(ref, h["topk_w"], 2), what="config1 y")
+    assert_parity(bf16_to_f64(y), ogemm.combine(ref, h["topk_w"], 2), scale=combine_scale(ref, h["topk_w"], 2),
+                  what="config1 y")
 
 
 @pytest.mark.parametrize("M", [1, 7, 14, 21, 28])

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import synth
-from helpers import assert_parity, bf16_to_f64, host, need_gpu
+from helpers import assert_parity, bf16_to_f64, combine_scale, host, need_gpu
 from oracle import gemm as ogemm
 from oracle import layer as olayer
 
@@ -50,7 +50,7 @@ def test_small_layer_full_parity(bias):
                                      hh["w2"], hh["s2"], hh["b2"])
     assert_parity(bf16_to_f64(h), rh, what="h")
     assert_parity(bf16_to_f64(c2), rc2, what="c2")
-    assert_parity(bf16_to_f64(y), ry, what="y")
+    assert_parity(bf16_to_f64(y), ry, scale=combine_scale(rc2, hh["topk_w"], 4), what="y")
 
 
 def test_layer_binding_matches_steps():
@@ -107,7 +107,8 @@ def test_gpt_oss_layer_sampled_parity(big_layer, bias):
     assert_parity(bf16_to_f64(h[slots]), rh[slots], what="h sampled")
     assert_parity(bf16_to_f64(c2[slots]), rc2[slots], what="c2 sampled")
     ry = ogemm.combine(rc2[slots], hh["topk_w"][tokens], 4)
-    assert_parity(bf16_to_f64(y[tokens]), ry, what="y sampled")
+    assert_parity(bf16_to_f64(y[tokens]), ry, scale=combine_scale(rc2[slots], hh["topk_w"][tokens], 4),
+                  what="y sampled")
 
 
 PAD_T = [6554, 6656, 6657, 7680, 8191, 8192] + synth.draw_token_counts(2, 6554, 8192, seed=1003)

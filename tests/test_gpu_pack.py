@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import synth
-from helpers import assert_parity, bf16_to_f64, host, need_gpu, to_dev
+from helpers import assert_parity, bf16_to_f64, combine_scale, host, need_gpu, to_dev
 from oracle import gemm as ogemm
 from oracle import layer as olayer
 from oracle import layout as olayout
@@ -107,9 +107,9 @@ def test_packed_layer_matches_oracle_and_padding_is_exact():
     assert torch.equal(y.view(torch.int16), y_pad.view(torch.int16))
     assert torch.equal(y.view(torch.int16), y_rows.view(torch.int16))
     hh = host(d)
-    _, _, ry = olayer.w4a16_layer(hh["x"][:T], hh["ids"][:T], hh["topk_w"][:T], 4, 8, hh["w1"], hh["s1"],
-                                  hh["b1"], hh["w2"], hh["s2"], hh["b2"])
-    assert_parity(bf16_to_f64(y), ry, what="packed layer y")
+    _, rc2, ry = olayer.w4a16_layer(hh["x"][:T], hh["ids"][:T], hh["topk_w"][:T], 4, 8, hh["w1"], hh["s1"],
+                                    hh["b1"], hh["w2"], hh["s2"], hh["b2"])
+    assert_parity(bf16_to_f64(y), ry, scale=combine_scale(rc2, hh["topk_w"][:T], 4), what="packed layer y")
 
 
 def test_packed_gpt_oss_layer_matches_rows_bitwise():

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import synth
-from helpers import assert_parity, bf16_to_f64, host, need_gpu, to_dev
+from helpers import assert_parity, bf16_to_f64, combine_scale, host, need_gpu, to_dev
 from oracle import gemm as ogemm
 from oracle import layer as olayer
 
@@ -92,4 +92,4 @@ def test_nemotron_relu2_layer(M):
                                      hh["b2"])
     assert_parity(bf16_to_f64(h), rh, what=f"nemotron h M={M}")
     assert_parity(bf16_to_f64(c2), rc2, what=f"nemotron c2 M={M}")
-    assert_parity(bf16_to_f64(y), ry, what=f"nemotron layer M={M}")
+    assert_parity(bf16_to_f64(y), ry, scale=combine_scale(rc2, hh["topk_w"], k), what=f"nemotron layer M={M}")
