@@ -1533,7 +1533,12 @@ def decode_main(torch, moe, dev, stream, args, clock):
         if args.phase == "both":  # (the profiled --phase cold runs time the headline's launches only)
             line["cold_k2688"] = decode_cold_k2688(torch, moe, dev, stream, args, clock)
         line["cold"] = {"per_m": cold["per_m"], "calls_per_path": cold["calls"],
-                        "three_launch": three, "clock": clock.summary("decode_cold"),
+                        "three_launch": three,
+                        "clock": dict(clock.summary("decode_cold"), note=(
+                            "sampled every 10 ms over the whole cold region, most of whose time is the "
+                            "20 ms one-wave spin heading each step, so it shows the spin's clock; the "
+                            "calls run right after 1 GiB copies, and 8 more copies ahead of each step's "
+                            "first call moved no per-M median by more than 1.5%")),
                         "ms_per_step_note": "device time of the step's launches (events); the copies that "
                                             "evict the cache between calls are outside it",
                         "bytes_note": "value counts the bytes the step must move (touched experts' weights, "
