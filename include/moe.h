@@ -42,7 +42,6 @@ typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARGUMENT = 1, /* a null pointer, a bad size, stride or combination */
   MOE_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. not a gfx950 device) */
-  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
   MOE_ERR_HIP = 4               /* a HIP runtime call failed; see moe_last_error() */
 } moe_status;
 
@@ -165,8 +164,9 @@ moe_status moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t top_k,
  * once, bias read through explicit strides; [TRT] Description: W4A16 MXFP4,
  * rows independent; [TA] What it does: bf16 decode at M <= 32).
  *
- * For every block b with e = expert_ids[b] >= 0 and every position r of it
- * with slot s = sorted_token_ids[b * block_m + r] < PAD:
+ * For every block b with 0 <= e = expert_ids[b] < num_experts (a block naming
+ * another id is skipped) and every position r of it with slot
+ * s = sorted_token_ids[b * block_m + r] < PAD:
  *   pre[n] = sum_k A_hat[s / a_row_div][k] * W_hat[e][n][k] + bias[e][n]
  *   W_hat[e][n][k] = dec(W[e][n][k]) * 2^(w_scale[e][n][k / 32] - 127)
  *   A_hat = A (bf16), or dec(A[r][k]) * 2^(a_scale[r][k / 32] - 127) for

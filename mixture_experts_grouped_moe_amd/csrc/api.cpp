@@ -163,7 +163,6 @@ const char* moe_status_string(int32_t status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
-    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
     default: return "MOE_ERR_UNKNOWN";
   }
