@@ -37,7 +37,7 @@ def _case(seed):
                 packed=bool(rng.integers(0, 2)), over_slots=bool(rng.integers(0, 2)))
 
 
-@pytest.mark.parametrize("seed", range(18))
+@pytest.mark.parametrize("seed", range(36))
 def test_grouped_gemm_random_shapes(seed):
     import mixture_experts_grouped_moe_amd as moe
     c = _case(seed)
@@ -60,7 +60,7 @@ def test_grouped_gemm_random_shapes(seed):
     assert_parity(bf16_to_f64(out), ref, what=f"case {seed}")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_mxfp8_activation_gemm_random_shapes(seed):
     # E4M3 activation codes with E8M0 scales (the scaled fp8 MFMA kernel):
     # the same random shapes, activations drawn directly as codes and scales
@@ -88,7 +88,7 @@ def test_mxfp8_activation_gemm_random_shapes(seed):
     assert_parity(bf16_to_f64(out), ref, what=f"mxfp8 activations, case {seed}")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_per_token_gemm_random_groups(seed):
     # the group_sizes interface: random expert counts (about a third of the
     # groups empty), random N, K a multiple of 16, bias and packed weights
@@ -112,7 +112,7 @@ def test_per_token_gemm_random_groups(seed):
     assert_parity(bf16_to_f64(out), ref, what=f"per-token case {seed}")
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(20))
 def test_wgrad_random_shapes(seed):
     # dW[e] = sum over e's slots of grad[s]^T x[s // k] on random shapes
     # (N and K multiples of 32, empty experts likely at large E), every
@@ -149,7 +149,7 @@ def _layer_case(seed):
                 bias=bool(rng.integers(0, 2)), packed=bool(rng.integers(0, 2)))
 
 
-@pytest.mark.parametrize("seed", range(17))
+@pytest.mark.parametrize("seed", range(34))
 def test_decode_layer_random_shapes(seed):
     # the fused decode layer (routing, GEMM, combine in one launch) on random
     # shapes within its limits: y and C against the oracle
