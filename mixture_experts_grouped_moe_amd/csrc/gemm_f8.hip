@@ -16,7 +16,9 @@
 //  * Each 64-wide K step moves 8 KB of activation codes and 32 KB of weight
 //    codes straight into LDS with buffer_load ... lds, three stages deep (two
 //    steps in flight), and the step's E8M0 bytes by byte (or 2-byte) DMA
-//    into a ring of scale sets in LDS, one step ahead of the tiles.
+//    into a ring of scale sets in LDS, one step ahead of the tiles; with
+//    packed weights one wave fetches the N tile's weight scale bytes of a
+//    step in a single 16-byte-per-lane DMA (1 KB).
 //  * The contraction is v_mfma_scale_f32_32x32x64_f8f6f4: one instruction
 //    per 32 x 32 output tile and K step, with the E8M0 bytes fed to it as they
 //    are (no dequantisation). Its operand layout (measured on gfx950): lane l
@@ -62,10 +64,23 @@ __device__ __forceinline__ void dma_ushort(__amdgpu_buffer_rsrc_t rsrc, uint32_t
 
 constexpr int kE8M0One = 127;                   // E8M0 code of 2^0
 
-// WS2: a weight row's two scale bytes of a step are adjacent and 2-byte
-// aligned (even scale strides), so one 2-byte DMA per lane fetches both and
-// one DMA covers 64 rows; otherwise one byte per lane and 32 rows per DMA.
-template <bool SWIGLU, bool BIAS, bool PT, bool WS2>
+// How the weight scale bytes of a step reach LDS (WSM):
+//  kWsByte  one byte per lane, 32 rows per DMA, every wave;
+//  kWsPair  a row's two bytes of a step adjacent and 2-byte aligned (even
+//           scale strides): one 2-byte DMA per lane, 64 rows per DMA, every
+//           wave;
+//  kWsPiece the K-block layout with 16-byte aligned strides: the tile's 512
+//           rows' byte pairs of a step are 64 aligned 16-byte pieces of 8
+//           consecutive rows each (a SwiGLU tile's gate and up runs are 64
+//           rows long and start at multiples of 8 when N/2 is), so one wave
+//           fetches them all with a single 16-byte DMA. The activation
+//           scale DMAs are then issued once per 32-row group too, by waves
+//           0 .. 3, where the other modes have two waves load each group.
+// The load path pays per DMA instruction more than per byte, so fewer
+// scale DMAs leave more of it to the tiles.
+constexpr int kWsByte = 0, kWsPair = 1, kWsPiece = 2;
+
+template <bool SWIGLU, bool BIAS, bool PT, int WSM>
 __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(GemmParams p) {
   constexpr int NT = kF8NT, STAGES = kF8Stages, RB = kF8RowBytes, BM = kF8BM;
   constexpr int WN = NT * 32, BN = kWavesN * WN;
@@ -75,15 +90,22 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   constexpr int W_BYTES = BN * RB;                  // 32 KB
   constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // 1
   constexpr int W_LOADS = W_BYTES / 1024 / NWAVES;  // 4
+  constexpr bool WS2 = WSM == kWsPair, WSP = WSM == kWsPiece;
   constexpr int AS_BYTES = PT ? 0 : BM * 2 * 4;     // the step's activation scale bytes, one dword each
-  constexpr int WS_BYTES = PT ? 0 : BN * (WS2 ? 1 : 2) * 4;  // the step's weight scale bytes, one dword per row (WS2) or byte
+  // the step's weight scale bytes: one dword per row (kWsPair) or per byte
+  // (kWsByte), or the rows' byte pairs as they lie in memory (kWsPiece)
+  constexpr int WS_BYTES = PT ? 0 : (WSP ? BN * 2 : BN * (WS2 ? 1 : 2) * 4);
   constexpr int AS_GROUPS = BM / 32;                // 32-row groups, one scale DMA each
-  constexpr int WS_ROWS = WS2 ? 64 : 32;            // weight rows per scale DMA
-  constexpr int WS_DMAS = BN / WS_ROWS / NWAVES;    // weight-scale DMAs per wave
+  constexpr int WS_ROWS = WS2 ? 64 : 32;            // weight rows per scale DMA (per-wave modes)
+  constexpr int WS_DMAS = WSP ? 0 : BN / WS_ROWS / NWAVES;  // weight-scale DMAs per wave (per-wave modes)
   static_assert(NWAVES % AS_GROUPS == 0, "every wave issues one activation-scale DMA");
-  static_assert(WS_DMAS * NWAVES * WS_ROWS == BN, "weight-scale split");
+  static_assert(WSP || WS_DMAS * NWAVES * WS_ROWS == BN, "weight-scale split");
+  static_assert(!WSP || (BN * 2 == 64 * 16 && AS_GROUPS < NWAVES), "one 16-byte piece per lane of one wave");
   constexpr int T_LOADS = A_LOADS + W_LOADS;        // tile DMAs per step per wave
-  constexpr int S_DMAS = PT ? 0 : WS_DMAS + 1;      // scale DMAs per step per wave
+  // scale DMAs per step of a wave: every wave the same in the per-wave
+  // modes; with kWsPiece one for waves 0 .. AS_GROUPS (activation groups,
+  // then the weight pieces) and none for the others
+  constexpr int S_DMAS = PT ? 0 : (WSP ? 1 : WS_DMAS + 1);
   // A step's scale bytes are loaded one step before its tiles, into their
   // own ring of SR sets; before computing a step a wave may leave in flight
   // the tiles of the next STAGES - 2 steps and the scales of the next
@@ -91,6 +113,7 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   constexpr int SR = STAGES + 1;
   constexpr int SC_BYTES = AS_BYTES + WS_BYTES;
   constexpr int WAIT_N = T_LOADS * (STAGES - 2) + S_DMAS * (STAGES - 1);
+  constexpr int WAIT_N0 = T_LOADS * (STAGES - 2);   // a wave that loads no scale bytes
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && W_LOADS * NWAVES * 1024 == W_BYTES, "tile split");
   static_assert(WAIT_N < 64, "vmcnt range");
   constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
@@ -172,19 +195,34 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
   // row's place in the group), where each wave reads those of its own rows
   // and columns: the waves of a row group or of a column group would
   // otherwise each load the same bytes. Activation rows: group
-  // wave % AS_GROUPS (two waves write each group alike); weight rows: groups
-  // WS_DMAS * wave + i (WS2: 64-row groups, one dword per row holding
-  // both bytes).
+  // wave % AS_GROUPS (in the per-wave modes two waves write each group
+  // alike); weight rows: groups WS_DMAS * wave + i (kWsPair: 64-row groups,
+  // one dword per row holding both bytes), or (kWsPiece) the byte pairs of
+  // the tile's rows in row order, 2 bytes per row.
   int32_t my_wrow[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) my_wrow[nt] = tile_w_row<NT, SWIGLU>(wn * WN + nt * 32 + l32, tile_n, p.N);
-  uint32_t ws_off[WS_DMAS];
+  uint32_t ws_off[WS_DMAS > 0 ? WS_DMAS : 1];
 #pragma unroll
   for (int i = 0; i < WS_DMAS; ++i) {
     const int r = WS2 ? (WS_DMAS * wave + i) * 64 + lane : (WS_DMAS * wave + i) * 32 + l32;
     const int32_t wr = tile_w_row<NT, SWIGLU>(r, tile_n, p.N);
     ws_off[i] = !PT && wr >= 0 ? (uint32_t)((int64_t)wr * p.ws_row + (WS2 ? 0 : h)) : kOOB;
   }
+  // kWsPiece: lane l fetches tile rows 8l .. 8l + 7 (their first row's byte
+  // pair; the other seven follow it in memory). A piece whose first row lies
+  // past N (or past N/2 gate columns) holds no row in use and reads zeros;
+  // the pairs of rows past N inside a used piece feed only columns that are
+  // never stored.
+  uint32_t wsp_off = kOOB;
+  if constexpr (WSP) {
+    const int32_t wr = tile_w_row<NT, SWIGLU>(8 * lane, tile_n, p.N);
+    wsp_off = wr >= 0 ? (uint32_t)((int64_t)wr * p.ws_row) : kOOB;
+  }
+  // waves 0 .. AS_GROUPS - 1 load the activation scales, wave AS_GROUPS the
+  // weight pieces (kWsPiece); in the per-wave modes every wave loads both
+  const bool as_wave = !WSP || wave < AS_GROUPS;
+  const bool wsp_wave = WSP && wave == AS_GROUPS;
   const int as_group = wave % AS_GROUPS;
   uint32_t as_off;
   {
@@ -232,7 +270,10 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
         if constexpr (WS2) dma_ushort(s_rsrc, live ? ws_off[i] : kOOB, ss, base + AS_BYTES + (WS_DMAS * wave + i) * 256);
         else dma_byte(s_rsrc, h_live ? ws_off[i] : kOOB, ss, base + AS_BYTES + (WS_DMAS * wave + i) * 256);
       }
-      dma_byte(as_rsrc, h_live ? as_off : kOOB, sas, base + as_group * 256);
+      if constexpr (WSP) {
+        if (wsp_wave) dma16(s_rsrc, live ? wsp_off : kOOB, ss, base + AS_BYTES);
+      }
+      if (as_wave) dma_byte(as_rsrc, h_live ? as_off : kOOB, sas, base + as_group * 256);
     }
   };
 
@@ -271,7 +312,12 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
     for (int nt = 0; nt < NT; ++nt) {
       const f8_v8i bf = operand(Ws, wn * WN + nt * 32 + l32);
       int sw = kE8M0One;
-      if constexpr (!PT && WS2) {
+      if constexpr (!PT && WSP) {
+        // the row's byte of K block 2 * step + h; the second block of a half
+        // K step lies past K
+        const int sb = lds_read<uint8_t>(Ss + (wn * WN + nt * 32 + l32) * 2 + h);
+        sw = (h && step * kBK + 32 >= p.K) ? 0 : sb;
+      } else if constexpr (!PT && WS2) {
         // both bytes of the row; the second block of a half K step lies past K
         const uint32_t d = lds_read<uint32_t>(Ss + (wn * WN + nt * 32 + l32) * 4);
         sw = (h && step * kBK + 32 >= p.K) ? 0 : (int)((d >> (8 * h)) & 0xffu);
@@ -298,10 +344,13 @@ __global__ __launch_bounds__(kF8Threads, kF8MinBlocks) void moe_gemm_f8_kernel(G
     issue(ST, st);
     issue_scales(ST + 1);
   });
+  // (kWsPiece: the waves that load no scale bytes have fewer loads in flight)
+  const bool scale_wave = !WSP || as_wave || wsp_wave;
   for (int step = 0; step < nsteps_pad; step += STAGES) {
     static_for<0, STAGES>([&](auto st) {
       constexpr int ST = decltype(st)::value;
-      wait_loads_barrier<WAIT_N>(no_regs);
+      if (scale_wave) wait_loads_barrier<WAIT_N>(no_regs);
+      else wait_loads_barrier<WAIT_N0>(no_regs);
       issue(step + ST + STAGES - 1, std::integral_constant<int, (ST + STAGES - 1) % STAGES>{});
       if (wave_live) compute(st, step + ST);
       issue_scales(step + ST + STAGES);
@@ -388,16 +437,25 @@ hipError_t launch_gemm_f8(const GemmParams& p, bool swiglu, bool bias, hipStream
   const int bn = kWavesN * 32 * kF8NT;
   const int64_t tiles = swiglu ? (p.N / 2 + bn / 2 - 1) / (bn / 2) : (p.N + bn - 1) / bn;
   const dim3 grid((uint32_t)(tiles * p.max_blocks));
-  // both scale bytes of a row's step in one aligned 2-byte load?
+  // the K-block layout with 16-byte aligned pieces of 8 rows' byte pairs
+  // (a SwiGLU tile's up rows start at N/2 + a multiple of 8)?
+  const bool wsp = p.ws_row == 2 && p.ws_blk % 16 == 0 && p.ws_stride_e % 16 == 0 &&
+                   ((uintptr_t)p.ws & 15) == 0 && (!swiglu || (p.N / 2) % 8 == 0);
+  // else both scale bytes of a row's step in one aligned 2-byte load?
   const bool ws2 = p.ws_row % 2 == 0 && p.ws_blk % 2 == 0 && p.ws_stride_e % 2 == 0 && (uintptr_t)p.ws % 2 == 0;
-#define MOE_LAUNCH_F8(SW, BI, W2) \
-  hipLaunchKernelGGL((moe_gemm_f8_kernel<SW, BI, false, W2>), grid, dim3(kF8Threads), 0, stream, p)
+  const int wsm = wsp ? kWsPiece : (ws2 ? kWsPair : kWsByte);
+#define MOE_LAUNCH_F8(SW, BI) \
+  do { \
+    if (wsm == kWsPiece) hipLaunchKernelGGL((moe_gemm_f8_kernel<SW, BI, false, kWsPiece>), grid, dim3(kF8Threads), 0, stream, p); \
+    else if (wsm == kWsPair) hipLaunchKernelGGL((moe_gemm_f8_kernel<SW, BI, false, kWsPair>), grid, dim3(kF8Threads), 0, stream, p); \
+    else hipLaunchKernelGGL((moe_gemm_f8_kernel<SW, BI, false, kWsByte>), grid, dim3(kF8Threads), 0, stream, p); \
+  } while (0)
   if (swiglu) {
-    if (bias) { if (ws2) MOE_LAUNCH_F8(true, true, true); else MOE_LAUNCH_F8(true, true, false); }
-    else { if (ws2) MOE_LAUNCH_F8(true, false, true); else MOE_LAUNCH_F8(true, false, false); }
+    if (bias) MOE_LAUNCH_F8(true, true);
+    else MOE_LAUNCH_F8(true, false);
   } else {
-    if (bias) { if (ws2) MOE_LAUNCH_F8(false, true, true); else MOE_LAUNCH_F8(false, true, false); }
-    else { if (ws2) MOE_LAUNCH_F8(false, false, true); else MOE_LAUNCH_F8(false, false, false); }
+    if (bias) MOE_LAUNCH_F8(false, true);
+    else MOE_LAUNCH_F8(false, false);
   }
 #undef MOE_LAUNCH_F8
   return hipGetLastError();
@@ -407,8 +465,8 @@ hipError_t launch_gemm_per_token(const GemmParams& p, bool bias, hipStream_t str
   if (p.max_blocks <= 0) return hipSuccess;
   const int bn = kWavesN * 32 * kF8NT;
   const dim3 grid((uint32_t)((p.N + bn - 1) / bn * (int64_t)p.max_blocks));
-  if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, true, false>), grid, dim3(kF8Threads), 0, stream, p);
-  else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, true, false>), grid, dim3(kF8Threads), 0, stream, p);
+  if (bias) hipLaunchKernelGGL((moe_gemm_f8_kernel<false, true, true, kWsByte>), grid, dim3(kF8Threads), 0, stream, p);
+  else hipLaunchKernelGGL((moe_gemm_f8_kernel<false, false, true, kWsByte>), grid, dim3(kF8Threads), 0, stream, p);
   return hipGetLastError();
 }
 

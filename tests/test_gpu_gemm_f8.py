@@ -37,6 +37,11 @@ CASES = [
     (1, 2, 8, 640, 320, "swiglu", False, True, "k"),
     (7, 6, 16, 200, 352, "none", True, False, "k"),
     (100, 4, 8, 256, 192, "none", False, False, "1"),
+    # packed weights: the N tile's scale bytes of a step in one 16-byte DMA
+    # per lane (SwiGLU with N/2 a multiple of 8, edge tile of 8 h columns),
+    # and the per-wave 2-byte scale DMAs where N/2 is not (N/2 = 100)
+    (60, 4, 6, 1040, 352, "swiglu", False, True, "k"),
+    (150, 3, 5, 200, 288, "swiglu", True, True, "k"),
 ]
 
 
