@@ -47,6 +47,26 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "T{}k{}E{}N{}K{}-{}-b{}-p{}-div{}".format(*c))
 def test_f8_gemm_matches_oracle(case):
+    _check(case)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_packed_scale_pieces_random_shapes(seed):
+    # packed weights with N a multiple of 16 (so N/2 is one of 8): the shapes
+    # whose weight scale bytes of a step arrive as 16-byte pieces of 8 rows,
+    # fetched by one wave; ragged N tiles, K tails, SwiGLU, bias, token and
+    # slot rows
+    rng = np.random.default_rng(7000 + seed)
+    E = int(rng.integers(1, 41))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    case = (int(rng.integers(1, 261)), k, E, 16 * int(rng.integers(1, 81)), 32 * int(rng.integers(1, 41)),
+            ("none", "swiglu")[int(rng.integers(0, 2))], bool(rng.integers(0, 2)), True,
+            ("k", "1")[int(rng.integers(0, 2))])
+    print("case", seed, case, flush=True)
+    _check(case)
+
+
+def _check(case):
     moe = _moe()
     T, k, E, N, K, epi, bias, packed, div = case
     a_row_div = k if div == "k" else 1
