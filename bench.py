@@ -1536,9 +1536,10 @@ def decode_main(torch, moe, dev, stream, args, clock):
                         "three_launch": three,
                         "clock": dict(clock.summary("decode_cold"), note=(
                             "sampled every 10 ms over the whole cold region, most of whose time is the "
-                            "20 ms one-wave spin heading each step, so it shows the spin's clock; the "
-                            "calls run right after 1 GiB copies, and 8 more copies ahead of each step's "
-                            "first call moved no per-M median by more than 1.5%")),
+                            "20 ms one-wave spin heading each step, so it describes the region, not the "
+                            "calls (it has read 190 to 2020 MHz on different runs); the calls run right "
+                            "after 1 GiB copies, and 8 more copies ahead of each step's first call moved "
+                            "no per-M median by more than 1.5%")),
                         "ms_per_step_note": "device time of the step's launches (events); the copies that "
                                             "evict the cache between calls are outside it",
                         "bytes_note": "value counts the bytes the step must move (touched experts' weights, "
