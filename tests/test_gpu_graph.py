@@ -112,10 +112,13 @@ def test_graph_w4a16_layer_step():
     _replays_match(step, [*r, h, c2, y])
 
 
-def test_graph_mxfp8_activation_step():
+@pytest.mark.parametrize("packed", [False, True])
+def test_graph_mxfp8_activation_step(packed):
+    # packed weights take the kernel's one-DMA weight-scale path
     moe = _moe()
     T, k, E, N, K = 100, 4, 8, 512, 192
     d = synth.gemm_case(T, k, E, N, K, "e4m3", seed=23, bias=True, w_std=0.5, device="cuda")
+    w, ws = (moe.moe_pack_weights(d["w"], "e4m3", w_scale=d["w_scale"]), None) if packed else (d["w"], d["w_scale"])
     bm = moe.moe_gemm_block_m("e4m3", T, moe.MOE_E4M3)
     r = _routing(moe, T, k, E, bm)
     q = torch.empty((T, K), dtype=torch.uint8, device="cuda")
@@ -125,8 +128,7 @@ def test_graph_mxfp8_activation_step():
     def step():
         moe.moe_quantize_mxfp8(d["x"], out=q, out_scales=qs)
         moe.moe_align(d["ids"], E, bm, out=r)
-        moe.moe_grouped_gemm(q, d["w"], "e4m3", r, T, k, E, k, w_scale=d["w_scale"], bias=d["bias"], out=C,
-                             a_scale=qs)
+        moe.moe_grouped_gemm(q, w, "e4m3", r, T, k, E, k, w_scale=ws, bias=d["bias"], out=C, a_scale=qs)
     _replays_match(step, [q, qs, *r, C])
 
 
