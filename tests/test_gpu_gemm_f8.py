@@ -92,6 +92,37 @@ def _check(case):
     assert_parity(bf16_to_f64(out), ref, what=f"f8 {case}")
 
 
+@pytest.mark.parametrize("epi", ["none", "swiglu"])
+def test_scale_load_paths_same_bits(epi):
+    # the same packed weights with their scale bytes 16-byte aligned (one
+    # 16-byte DMA per step for the tile), at a 2-byte offset (a 2-byte DMA
+    # per lane from every wave) and at a 1-byte offset (byte DMAs): only the
+    # way the bytes reach LDS differs, so C must be the same bits
+    moe = _moe()
+    T, k, E, N, K = 150, 4, 8, 1040, 352
+    d = synth.gemm_case(T, k, E, N, K, "e4m3", seed=91, bias=True, w_std=0.5)
+    a_codes = synth.e4m3_normal((T, K), 1.0, 91, "xq").cuda()
+    a_scales = synth.e8m0_uniform((T, K // 32), 120, 130, 91, "xs").cuda()
+    dd = to_dev(d)
+    pw = moe.moe_pack_weights(dd["w"], "e4m3", w_scale=dd["w_scale"])
+    routing = moe.moe_align(dd["ids"], E, moe.moe_gemm_block_m("e4m3", T, moe.MOE_E4M3))
+    n_out = N // 2 if epi == "swiglu" else N
+    outs = []
+    for off in (0, 2, 1):
+        buf = torch.zeros(pw.scales.numel() + 64, dtype=torch.uint8, device="cuda")
+        sc = buf[off:off + pw.scales.numel()].view(pw.scales.shape)
+        sc.copy_(pw.scales)
+        w = moe.PackedWeights(pw.codes, sc, "e4m3", N, K)
+        out = torch.full((T * k, n_out), float("nan"), dtype=torch.bfloat16, device="cuda")
+        moe.moe_grouped_gemm(a_codes, w, "e4m3", routing, T, k, E, k, bias=dd["bias"], epilogue=epi, out=out,
+                             a_scale=a_scales)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(outs[0]).all()
+    for off, o in zip((2, 1), outs[1:]):
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16)), f"scale bytes at offset {off}"
+
+
 def test_bf16_to_mxfp8_to_gemm_chain():
     # the GPU path quantizes bf16 activations and runs the MXFP8 x MXFP8 GEMM;
     # the oracle converts the same bf16 values itself and multiplies in float64
