@@ -15,9 +15,14 @@
 //
 // HBM-bound: one thread per (row, 32-element block) reads 64 bytes, writes
 // 32 code bytes and one scale byte; a wave covers 4 KB of contiguous input.
-// Every step is exact in fp32 (bf16 times a power of two inside the normal
-// range, then an integer rounding on the bits), so the codes are the same
-// as a float64 evaluation of the definition.
+// The codes come from gfx950's scaled conversion v_cvt_scalef32_pk_fp8_bf16
+// (two elements per instruction), which divides by the power of two given
+// as an E8M0 exponent and rounds to the nearest E4M3 value, ties to even,
+// but turns results past 448 into NaN and keeps the sign of -0 (measured).
+// So each element's magnitude is first clamped to 448 * 2^X (bf16 bits are
+// ordered like magnitudes: one packed 16-bit min for two elements) and the
+// sign of a zero is cleared; the conversion of v / 2^X is then exact up to
+// its single rounding, which is the definition's.
 #include "common.h"
 #include "params.h"
 
@@ -25,16 +30,19 @@ namespace moe {
 
 constexpr int kQuantThreads = 256;
 
-// |a| (a finite, non-negative fp32) -> E4M3 magnitude code, round to nearest
-// even, saturating at 448 (code 0x7E).
-__device__ __forceinline__ uint32_t e4m3_magnitude(float a) {
-  if (a >= 448.0f) return 0x7Eu;
-  if (a < 0.015625f) return (uint32_t)__builtin_rintf(a * 512.0f);  // subnormals: m * 2^-9
-  const uint32_t bits = __float_as_uint(a);
-  // keep 3 mantissa bits: round at bit 20 (ties to even), carries move into
-  // the exponent; rebias the exponent from 127 to 7
-  const uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);
-  return (r >> 20) - ((127u - 7u) << 3);
+typedef short q_v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 q_v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned short q_v2u16 __attribute__((ext_vector_type(2)));
+
+// Two bf16 elements (bits of one dword) -> the dword with their magnitudes
+// clamped to `lim2` (448 * 2^X in both halves) and the sign of a zero
+// element cleared. Each half's magnitude plus 0x7FFF has bit 15 set exactly
+// when the magnitude is non-zero, and never carries into the other half.
+__device__ __forceinline__ uint32_t clamp_pair(uint32_t d, uint32_t lim2) {
+  const uint32_t mag = d & 0x7FFF7FFFu;
+  const uint32_t sgn = d & 0x80008000u & (mag + 0x7FFF7FFFu);
+  const q_v2u16 m = __builtin_elementwise_min(__builtin_bit_cast(q_v2u16, mag), __builtin_bit_cast(q_v2u16, lim2));
+  return __builtin_bit_cast(uint32_t, m) | sgn;
 }
 
 __global__ __launch_bounds__(kQuantThreads) void quant_mxfp8_kernel(
@@ -70,22 +78,23 @@ __global__ __launch_bounds__(kQuantThreads) void quant_mxfp8_kernel(
     // (below 2^-126) gives X below -127, so the clamp decides
     const int e = (int)(amax >> 7);
     const int X = e == 0 ? -127 : min(max(e - 127 - 8, -127), 127);
-    const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, X in [-127, 120]
+    // the conversion's scale operand: E8M0 byte X + 127 in the exponent
+    // field (byte 0 is 2^-127); X <= 119 for finite inputs, so 448 * 2^X
+    // (bf16 exponent 135 + X, mantissa 0x60) is a finite bf16
+    const float scale = __uint_as_float((uint32_t)(X + 127) << 23);
+    const uint32_t lim = ((uint32_t)(135 + X) << 7) | 0x60u;
+    const uint32_t lim2 = lim | (lim << 16);
     uint32_t out[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t pair = 0;
-#pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-          const uint32_t h = (v[j][w] >> (16 * hlf)) & 0xFFFFu;
-          const float a = bf16_bits_to_f32(h & 0x7FFFu) * inv;
-          const uint32_t sign = (h & 0x8000u) && (h & 0x7FFFu) ? 0x80u : 0u;  // v < 0 (not -0)
-          pair |= (e4m3_magnitude(a) | sign) << (8 * hlf);
-        }
-        // elements 8j + 2w, 8j + 2w + 1 -> bytes 2w, 2w + 1 of dword j / 2 half j % 2
-        out[2 * j + w / 2] = (w % 2 == 0) ? pair : (out[2 * j + w / 2] | (pair << 16));
+      for (int w = 0; w < 4; w += 2) {
+        // elements 8j + 2w .. 8j + 2w + 3 -> the four bytes of dword 2j + w/2
+        const uint32_t lo = clamp_pair(v[j][w], lim2), hi = clamp_pair(v[j][w + 1], lim2);
+        q_v2s r = {0, 0};
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(q_v2bf, lo), scale, false);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(q_v2bf, hi), scale, true);
+        out[2 * j + w / 2] = __builtin_bit_cast(uint32_t, r);
       }
     dst[0] = u32x4_t{out[0], out[1], out[2], out[3]};
     dst[1] = u32x4_t{out[4], out[5], out[6], out[7]};
